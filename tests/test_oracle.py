@@ -1,0 +1,112 @@
+"""CPU tests: the oracle against its pins, and the pins against planted mistakes."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "li_oracle.c")
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# Plausible mistakes planted in a copy of the oracle's C source: each must make
+# at least one pin fail.  (old text, new text) pairs; the old text must occur.
+C_MUTANTS = {
+    "absorb_transposed_W": ("acc += qi[e] * W[e * r + t];", "acc += qi[e] * W[t * d + e];"),
+    "absorb_wrong_query_index": ("acc += qi[e] * W[e * r + t];", "acc += qi[t % d] * W[e * r + t];"),
+    "score_no_relu": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;",
+                      "total += w[h] * dot;\n        }\n        s[i] = total;"),
+    "score_no_head_weight": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;",
+                             "total += (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;"),
+    "score_relu_after_sum": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;",
+                             "total += w[h] * dot;\n        }\n        s[i] = total > 0.0 ? total : 0.0;"),
+    "score_wrong_head_index": ("dot += qt[h * r + t] * c[t];", "dot += qt[t] * c[t];"),
+    "score_ignores_row_list": ("const int64_t row = rows ? (int64_t)rows[i] : i;", "const int64_t row = i;"),
+    "score_dropped_last_term": ("for (int64_t t = 0; t < r; ++t)\n                dot += qt",
+                                "for (int64_t t = 0; t < r - 1; ++t)\n                dot += qt"),
+    "explicit_transposed_W": ("acc += W[e * r + t] * c[t];", "acc += W[t * d + e] * c[t];"),
+    "topk_ascending": ("if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
+                       "if (x->s > y->s) return 1;\n    if (x->s < y->s) return -1;"),
+    "topk_tiebreak_reversed": ("return (x->p > y->p) - (x->p < y->p);", "return (x->p < y->p) - (x->p > y->p);"),
+    "topk_drops_position_map": ("e[i].p = pos ? pos[i] : (int32_t)i;", "e[i].p = (int32_t)i;"),
+}
+
+
+def _run_pins():
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+@pytest.mark.parametrize("name", sorted(C_MUTANTS))
+def test_pins_catch_c_mutant(name, mutant_dir):
+    old, new = C_MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    msrc = mutant_dir / f"{name}.c"
+    msrc.write_text(src.replace(old, new, 1))
+    so = mutant_dir / f"{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(msrc), "-o", str(so), "-lm"])
+    oracle.use_library(str(so))
+    try:
+        failed = _run_pins()
+    finally:
+        oracle.use_library(None)
+    assert failed, f"no pin catches the planted mistake {name}"
+
+
+def _mut_valid_rows_exclusive(pos, length):
+    return int(max(0, min(int(pos), int(length))))
+
+
+def _mut_hs_follower_full_prefix(q, W, w, latents, qseq, qpos, lens, k, M):
+    res = _orig_hs(q, W, w, latents, qseq, qpos, lens, k, M)
+    for l in range(1, len(q)):
+        full = oracle.full_layer(q[l], W[l], w[l], latents, qseq, qpos, lens, k)
+        for i, r in enumerate(res[l]):
+            r.sel = full[i].sel
+    return res
+
+
+def _mut_hs_follower_uncapped(q, W, w, latents, qseq, qpos, lens, k, M):
+    res = _orig_hs(q, W, w, latents, qseq, qpos, lens, k, M)
+    for l in range(1, len(q)):
+        for r in res[l]:
+            r.sel = oracle.topk(r.cand_scores, len(r.cand), pos=r.cand)
+    return res
+
+
+_orig_hs = oracle.hs_group
+
+PY_MUTANTS = {
+    "valid_rows_exclusive": ("valid_rows", _mut_valid_rows_exclusive),
+    "hs_follower_scores_full_prefix": ("hs_group", _mut_hs_follower_full_prefix),
+    "hs_follower_budget_uncapped": ("hs_group", _mut_hs_follower_uncapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_python_mutant(name, monkeypatch):
+    attr, fn = PY_MUTANTS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    assert _run_pins(), f"no pin catches the planted mistake {name}"
+
+
+def test_oracle_threads_reported():
+    assert oracle.num_threads() >= 1
