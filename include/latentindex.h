@@ -1,0 +1,184 @@
+/*
+ * latentindex.h — C ABI of the LatentIndex sparse-attention indexer hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: LatentIndex, "Cross-Layer Sharing with Layer-Specific Selection for
+ * Sparse Attention" (arXiv:2610.04635), as summarised section by section on
+ * paperlayer.ai.  Sections cited below are the paper's.
+ *
+ *   - A layer group shares one latent cache c_s written by its first (anchor)
+ *     layer (§3.1, §B.2).
+ *   - Each layer l folds its key decoder into its query,
+ *     qt_{l,h} = q_{l,h} W_dec_l (§3.1, §A.2, §B.2), and scores every valid
+ *     cached row s as I_l(s) = sum_h w_{l,h} * max(0, qt_{l,h} . c_s).
+ *   - Each layer then selects its own top-k rows (§3.1, §4.1: k = 2048).
+ *   - Hierarchical selection (HS, §3.2, §C.4): the anchor proposes its top-M
+ *     rows (M = 8192 in the paper) and each follower rescores only those and
+ *     selects its own top-k within them.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  Descriptor structs
+ *     are host memory read during the call only.
+ *   - The caller owns all memory (cache pool, block table, queries, outputs,
+ *     workspace).  The library never allocates, frees or synchronizes; every
+ *     call only enqueues kernels on `stream` and returns.
+ *   - Row-major layouts; int32 indices; `bf16` means IEEE bfloat16 bits.
+ *   - Host-side validation happens before anything is enqueued: a failing
+ *     call returns a status, enqueues nothing and never aborts.  Values that
+ *     live in device memory (seq_lens, block-table entries, positions,
+ *     candidates) cannot be checked on the host; out-of-range values there
+ *     are undefined behaviour.  NaN/Inf inputs are undefined.
+ *   - LI_ERR_HIP reports a failed launch (detail in li_last_error()).
+ *   - Calls on different streams are independent; calls that share output
+ *     or workspace buffers must be ordered by the caller.
+ */
+#ifndef LATENTINDEX_H
+#define LATENTINDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LI_ABI_VERSION 1
+#define LI_API __attribute__((visibility("default")))
+#define LI_PAGE_SIZE 64      /* rows per cache page                        */
+#define LI_MAX_HEADS 64      /* indexer heads per query                    */
+#define LI_MAX_TOPK 65536    /* largest k / M accepted by the selectors    */
+
+typedef enum {
+    LI_OK = 0,
+    LI_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    LI_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent        */
+    LI_ERR_UNSUPPORTED = 3, /* valid but not supported (r, H, d, dtype, ...) */
+    LI_ERR_WORKSPACE = 4,   /* workspace smaller than li_workspace_bytes()   */
+    LI_ERR_HIP = 5          /* a HIP launch failed                           */
+} li_status;
+
+typedef enum { LI_BF16 = 0, LI_FP32 = 1 } li_dtype;
+
+/*
+ * Shared latent cache of one layer group (§3.1: one cache per group, rows
+ * written once by the anchor; §B.2: cached once per group).
+ *   pool        [num_pages][page_size][r] of `dtype`; logical row j of
+ *               sequence b lives at page block_table[b*max_pages + j/64],
+ *               slot j%64.
+ *   block_table [batch][max_pages] int32 physical page ids.
+ *   seq_lens    [batch] int32 rows present per sequence (after appends).
+ * page_size must be LI_PAGE_SIZE.  r in {64, 128, 256} for LI_BF16,
+ * 1..256 for LI_FP32.  A contiguous cache is the identity block table.
+ */
+typedef struct {
+    void *pool;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t max_pages;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t r;
+    li_dtype dtype;
+} li_cache;
+
+/*
+ * Queries of one call.  Query i belongs to sequence seq[i] and sits at
+ * position pos[i]; it scores rows j < n_i = min(pos[i] + 1, seq_lens[seq[i]])
+ * (causal prefix including its own row; §C.4 caps every budget at the valid
+ * prefix).  max_valid (host) is an upper bound on every n_i; it sizes the
+ * launch grids and the score stride.
+ */
+typedef struct {
+    const int32_t *seq;
+    const int32_t *pos;
+    int32_t Q;
+    int32_t max_valid;
+} li_queries;
+
+/*
+ * append_latent — the anchor writes T new latent rows into the group cache
+ * (§3.1: the shared representation is cached once per group; followers only
+ * read it).  rows [T][r] of the cache dtype; row t goes to sequence seq[t],
+ * logical position pos[t].  Rows are copied bit-exactly.  Updating
+ * seq_lens is the caller's job.  Rows that target the same slot race.
+ */
+LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const int32_t *seq,
+                           const int32_t *pos, int32_t T, hipStream_t stream);
+
+/*
+ * absorb_query — qt = q W_dec for every query and head (§3.1, §A.2, §B.2).
+ *   q       [Q][H][d]   (dtype)
+ *   w_dec   [d][r]      (dtype) the layer's key decoder, latent -> key
+ *   q_tilde [Q][H][r]   (dtype) output
+ * LI_BF16: bf16 inputs, fp32 accumulation, one round-to-nearest-even to bf16.
+ * LI_FP32: fp32 throughout.  H <= 64; r in {64,128,256} and d in
+ * {32,64,128,256} for LI_BF16; r in 1..256 and d in 1..1024 for LI_FP32.
+ */
+LI_API li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32_t Q, int32_t H,
+                          int32_t d, int32_t r, li_dtype dtype, hipStream_t stream);
+
+/*
+ * score_topk — full-prefix scoring and per-query top-k (§3.1, §4.1).
+ *   q_tilde [Q][H][r] absorbed queries (cache dtype); w [Q][H] fp32 head
+ *   weights (any sign).  scores[i][j] = sum_h w[i][h] max(0, q_tilde[i][h] . c_j)
+ *   for j < n_i, accumulated in fp32.
+ *   idx     [Q][k] out: the set of the min(k, n_i) highest-scoring positions
+ *           (unordered; slots past count[i] are -1).  Among exactly equal
+ *           scores any choice may be returned.
+ *   count   [Q]    out: min(k, n_i).
+ *   k_inner, idx_inner [Q][k_inner], count_inner [Q]: optional nested
+ *           selection (HS anchor, §3.2/§C.4: top-M candidates with the
+ *           anchor's own top-k inside them).  k_inner = 0 and NULL pointers
+ *           disable it; otherwise 0 < k_inner <= k and idx_inner is a subset
+ *           of idx.
+ *   scores  [Q][ld] fp32 out (optional, NULL keeps them in the workspace);
+ *           ld >= max_valid.  Entries j >= n_i are left untouched.
+ *   ws      workspace of at least li_workspace_bytes(op, ...) with op =
+ *           LI_OP_SCORE_TOPK (scores == NULL) or LI_OP_SCORE_TOPK_EXT_SCORES.
+ * The per-layer baseline indexer (a layer's own key cache of width d, no
+ * decoder) is this call on a cache of r = d with q_tilde = q.
+ */
+LI_API li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde,
+                        const float *w, int32_t H, int32_t k, int32_t *idx, int32_t *count,
+                        int32_t k_inner, int32_t *idx_inner, int32_t *count_inner, float *scores,
+                        int64_t ld, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hs_select — HS follower step (§3.2, §3.4, §C.4): rescore only the anchor's
+ * candidates with this layer's query and select this layer's top-k of them.
+ *   cand       [Q][M] candidate positions (the anchor's idx output with
+ *              k = M); cand_count [Q] valid entries per query (<= M).  The
+ *              entries must be distinct valid rows of the query's sequence.
+ *   idx        [Q][k] out: absolute positions of the min(k, cand_count[i])
+ *              best candidates (unordered, -1 padded); count [Q] out.
+ *   cand_scores [Q][M] fp32 out (optional): the follower's candidate scores.
+ *   ws         at least li_workspace_bytes(LI_OP_HS_SELECT, ...).
+ */
+LI_API li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
+                       const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w,
+                       int32_t H, int32_t k, int32_t *idx, int32_t *count, float *cand_scores,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace operations:
+ *   LI_OP_SCORE_TOPK             li_score_topk with scores == NULL (the score
+ *                                rows live in the workspace)
+ *   LI_OP_HS_SELECT              li_hs_select
+ *   LI_OP_SCORE_TOPK_EXT_SCORES  li_score_topk with a caller score buffer */
+enum { LI_OP_SCORE_TOPK = 0, LI_OP_HS_SELECT = 1, LI_OP_SCORE_TOPK_EXT_SCORES = 2 };
+
+/* Workspace bytes for `op` at these sizes (M ignored for the score_topk ops,
+ * max_valid ignored for LI_OP_HS_SELECT).  0 means invalid sizes. */
+LI_API size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32_t r, int32_t k,
+                          int32_t M);
+
+LI_API const char *li_status_str(li_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+LI_API const char *li_last_error(void);
+LI_API int32_t li_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LATENTINDEX_H */

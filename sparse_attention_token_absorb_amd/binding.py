@@ -1,0 +1,284 @@
+"""Thin Python binding of liblatentindex (ctypes over the C ABI).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+outputs and workspaces are allocated with torch, and every call goes straight
+to the C entry point of the same name on the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or fails to load, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblatentindex.so")
+
+LI_OK, LI_ERR_NULL, LI_ERR_SHAPE, LI_ERR_UNSUPPORTED, LI_ERR_WORKSPACE, LI_ERR_HIP = range(6)
+LI_BF16, LI_FP32 = 0, 1
+LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
+PAGE_SIZE = 64
+EXPORTED = ["li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select", "li_workspace_bytes",
+            "li_status_str", "li_last_error", "li_abi_version"]
+
+
+class LIError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({_status_name(status)}): {detail}")
+        self.status = status
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("r", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class _Queries(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("Q", ctypes.c_int32),
+                ("max_valid", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load liblatentindex.so (built in-tree).  Raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m sparse_attention_token_absorb_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cp, qp = ctypes.POINTER(_Cache), ctypes.POINTER(_Queries)
+        L.li_append_latent.argtypes = [cp, vp, vp, vp, i32, vp]
+        L.li_absorb_query.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+        L.li_score_topk.argtypes = [cp, qp, vp, vp, i32, i32, vp, vp, i32, vp, vp, vp, i64, vp, sz, vp]
+        L.li_hs_select.argtypes = [cp, qp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.li_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32]
+        L.li_workspace_bytes.restype = sz
+        L.li_status_str.argtypes = [ctypes.c_int]
+        L.li_status_str.restype = ctypes.c_char_p
+        L.li_last_error.argtypes = []
+        L.li_last_error.restype = ctypes.c_char_p
+        L.li_abi_version.restype = i32
+        for f in ("li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().li_status_str(s).decode()
+    except Exception:  # library not loadable: still give a readable message
+        return str(s)
+
+
+def _check(status: int, where: str) -> None:
+    if status != LI_OK:
+        raise LIError(status, where, lib().li_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _li_dtype(dt) -> int:
+    if dt == torch.bfloat16:
+        return LI_BF16
+    if dt == torch.float32:
+        return LI_FP32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+@dataclass
+class LatentCache:
+    """Paged shared latent cache of one layer group (caller-owned tensors).
+
+    pool [num_pages][64][r] (bf16 or fp32), block_table [batch][max_pages]
+    int32, seq_lens [batch] int32.
+    """
+    pool: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
+
+    def __post_init__(self):
+        if self.pool.dim() != 3 or self.pool.shape[1] != PAGE_SIZE:
+            raise ValueError("pool must be [num_pages][64][r]")
+        _need(self.pool, "pool", self.pool.dtype)
+        _li_dtype(self.pool.dtype)
+        dev = self.pool.device
+        _need(self.block_table, "block_table", torch.int32, dev)
+        _need(self.seq_lens, "seq_lens", torch.int32, dev)
+        if self.block_table.dim() != 2 or self.seq_lens.shape != (self.block_table.shape[0],):
+            raise ValueError("block_table must be [batch][max_pages] and seq_lens [batch]")
+
+    @property
+    def device(self):
+        return self.pool.device
+
+    @property
+    def r(self) -> int:
+        return int(self.pool.shape[2])
+
+    @property
+    def dtype(self):
+        return self.pool.dtype
+
+    def desc(self) -> _Cache:
+        return _Cache(self.pool.data_ptr(), self.block_table.data_ptr(), self.seq_lens.data_ptr(),
+                      int(self.block_table.shape[0]), int(self.block_table.shape[1]), PAGE_SIZE,
+                      int(self.pool.shape[0]), self.r, _li_dtype(self.pool.dtype))
+
+
+def _queries(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int) -> _Queries:
+    _need(seq, "seq", torch.int32, cache.device)
+    _need(pos, "pos", torch.int32, cache.device)
+    if seq.dim() != 1 or pos.shape != seq.shape:
+        raise ValueError("seq and pos must be [Q]")
+    return _Queries(seq.data_ptr(), pos.data_ptr(), int(seq.shape[0]), int(max_valid))
+
+
+def workspace_bytes(op: int, Q: int, max_valid: int, H: int, r: int, k: int, M: int = 0) -> int:
+    return int(lib().li_workspace_bytes(op, Q, max_valid, H, r, k, M))
+
+
+def _workspace(device, nbytes: int, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _need(ws, "ws", torch.uint8, device)
+    return ws
+
+
+def append_latent(cache: LatentCache, rows: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor) -> None:
+    """li_append_latent: copy rows [T][r] into the pool at (seq[t], pos[t])."""
+    _need(rows, "rows", cache.dtype, cache.device)
+    _need(seq, "seq", torch.int32, cache.device)
+    _need(pos, "pos", torch.int32, cache.device)
+    T = int(rows.shape[0])
+    if rows.dim() != 2 or rows.shape[1] != cache.r or seq.shape != (T,) or pos.shape != (T,):
+        raise ValueError("rows must be [T][r], seq and pos [T]")
+    c = cache.desc()
+    _check(lib().li_append_latent(ctypes.byref(c), _ptr(rows), _ptr(seq), _ptr(pos), T, _stream(cache.device)),
+           "li_append_latent")
+
+
+def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """li_absorb_query: q [Q][H][d] x W_dec [d][r] -> q_tilde [Q][H][r]."""
+    dev = q.device
+    _need(q, "q", q.dtype, dev)
+    dt = _li_dtype(q.dtype)
+    _need(w_dec, "w_dec", q.dtype, dev)
+    if q.dim() != 3 or w_dec.dim() != 2 or w_dec.shape[0] != q.shape[2]:
+        raise ValueError("q must be [Q][H][d] and w_dec [d][r]")
+    Q, H, d = (int(x) for x in q.shape)
+    r = int(w_dec.shape[1])
+    if out is None:
+        out = torch.empty((Q, H, r), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, dev, (Q, H, r))
+    _check(lib().li_absorb_query(_ptr(q), _ptr(w_dec), _ptr(out), Q, H, d, r, dt, _stream(dev)), "li_absorb_query")
+    return out
+
+
+class TopK:
+    """Outputs of score_topk / hs_select (device tensors)."""
+
+    def __init__(self, idx, count, idx_inner=None, count_inner=None, scores=None):
+        self.idx = idx
+        self.count = count
+        self.idx_inner = idx_inner
+        self.count_inner = count_inner
+        self.scores = scores
+
+
+def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int, q_tilde: torch.Tensor,
+               w: torch.Tensor, k: int, k_inner: int = 0, keep_scores: bool = False,
+               ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None) -> TopK:
+    """li_score_topk: score every valid row and take the top-k (+ nested top-k_inner)."""
+    dev = cache.device
+    qs = _queries(cache, seq, pos, max_valid)
+    Q = qs.Q
+    _need(q_tilde, "q_tilde", cache.dtype, dev)
+    if q_tilde.dim() != 3 or q_tilde.shape[0] != Q or q_tilde.shape[2] != cache.r:
+        raise ValueError("q_tilde must be [Q][H][r]")
+    H = int(q_tilde.shape[1])
+    _need(w, "w", torch.float32, dev, (Q, H))
+    if out is None:
+        out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
+        if k_inner:
+            out.idx_inner = torch.empty((Q, k_inner), dtype=torch.int32, device=dev)
+            out.count_inner = torch.empty(Q, dtype=torch.int32, device=dev)
+        if keep_scores:
+            out.scores = torch.empty((Q, max(max_valid, 1)), dtype=torch.float32, device=dev)
+    _need(out.idx, "idx", torch.int32, dev, (Q, k))
+    _need(out.count, "count", torch.int32, dev, (Q,))
+    ld = 0
+    if out.scores is not None:
+        _need(out.scores, "scores", torch.float32, dev)
+        ld = int(out.scores.shape[1])
+    op = LI_OP_SCORE_TOPK_EXT_SCORES if out.scores is not None else LI_OP_SCORE_TOPK
+    nb = workspace_bytes(op, Q, max_valid, H, cache.r, k, 0)
+    ws = _workspace(dev, nb, ws)
+    c = cache.desc()
+    _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(q_tilde), _ptr(w), H, k, _ptr(out.idx),
+                               _ptr(out.count), k_inner, _ptr(out.idx_inner), _ptr(out.count_inner),
+                               _ptr(out.scores), ld, _ptr(ws), ws.numel(), _stream(dev)), "li_score_topk")
+    return out
+
+
+def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int, cand: torch.Tensor,
+              cand_count: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor, k: int, keep_scores: bool = False,
+              ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None) -> TopK:
+    """li_hs_select: rescore the anchor's candidates and take this layer's top-k of them."""
+    dev = cache.device
+    qs = _queries(cache, seq, pos, max_valid)
+    Q = qs.Q
+    _need(cand, "cand", torch.int32, dev)
+    if cand.dim() != 2 or cand.shape[0] != Q:
+        raise ValueError("cand must be [Q][M]")
+    M = int(cand.shape[1])
+    _need(cand_count, "cand_count", torch.int32, dev, (Q,))
+    _need(q_tilde, "q_tilde", cache.dtype, dev)
+    if q_tilde.dim() != 3 or q_tilde.shape[0] != Q or q_tilde.shape[2] != cache.r:
+        raise ValueError("q_tilde must be [Q][H][r]")
+    H = int(q_tilde.shape[1])
+    _need(w, "w", torch.float32, dev, (Q, H))
+    if out is None:
+        out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
+        if keep_scores:
+            out.scores = torch.empty((Q, M), dtype=torch.float32, device=dev)
+    _need(out.idx, "idx", torch.int32, dev, (Q, k))
+    _need(out.count, "count", torch.int32, dev, (Q,))
+    if out.scores is not None:
+        _need(out.scores, "cand_scores", torch.float32, dev, (Q, M))
+    nb = workspace_bytes(LI_OP_HS_SELECT, Q, 0, H, cache.r, k, M)
+    ws = _workspace(dev, nb, ws)
+    c = cache.desc()
+    _check(lib().li_hs_select(ctypes.byref(c), ctypes.byref(qs), _ptr(cand), _ptr(cand_count), M, _ptr(q_tilde),
+                              _ptr(w), H, k, _ptr(out.idx), _ptr(out.count), _ptr(out.scores), _ptr(ws),
+                              ws.numel(), _stream(dev)), "li_hs_select")
+    return out

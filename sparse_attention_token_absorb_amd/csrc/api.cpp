@@ -1,0 +1,295 @@
+// C ABI of liblatentindex: argument validation, workspace carving and
+// kernel dispatch.  Every entry point validates on the host first and only
+// then enqueues work on the caller's stream; nothing here allocates, frees
+// or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/latentindex.h"
+#include "li_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+li_status fail(li_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+li_status fail(li_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+li_status ok()
+{
+    g_last_error.clear();
+    return LI_OK;
+}
+
+li_status hip_fail(hipError_t e, const char *where)
+{
+    return fail(LI_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int64_t score_ld(int32_t max_valid) { return ((int64_t)std::max(max_valid, 1) + 63) / 64 * 64; }
+
+bool r_supported(int32_t r, li_dtype dt)
+{
+    if (dt == LI_BF16) return r == 64 || r == 128 || r == 256;
+    if (dt == LI_FP32) return r >= 1 && r <= 256;
+    return false;
+}
+
+li_status check_cache(const li_cache *c)
+{
+    if (!c) return fail(LI_ERR_NULL, "cache descriptor is NULL");
+    if (!c->pool || !c->block_table || !c->seq_lens) return fail(LI_ERR_NULL, "cache pool/block_table/seq_lens is NULL");
+    if (c->page_size != LI_PAGE_SIZE) return fail(LI_ERR_UNSUPPORTED, "page_size %d (only %d)", c->page_size, LI_PAGE_SIZE);
+    if (c->batch <= 0 || c->max_pages <= 0 || c->num_pages <= 0)
+        return fail(LI_ERR_SHAPE, "batch %d, max_pages %d, num_pages %d must be positive", c->batch, c->max_pages,
+                    c->num_pages);
+    if (c->dtype != LI_BF16 && c->dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)c->dtype);
+    if (!r_supported(c->r, c->dtype)) return fail(LI_ERR_UNSUPPORTED, "latent width r=%d for dtype %d", c->r, (int)c->dtype);
+    return LI_OK;
+}
+
+li_status check_queries(const li_queries *qs, const li_cache *c)
+{
+    if (!qs) return fail(LI_ERR_NULL, "queries descriptor is NULL");
+    if (qs->Q < 0) return fail(LI_ERR_SHAPE, "Q=%d", qs->Q);
+    if (qs->Q > 0 && (!qs->seq || !qs->pos)) return fail(LI_ERR_NULL, "queries seq/pos is NULL");
+    if (qs->max_valid < 0 || (int64_t)qs->max_valid > (int64_t)c->max_pages * LI_PAGE_SIZE)
+        return fail(LI_ERR_SHAPE, "max_valid=%d outside [0, max_pages*%d]", qs->max_valid, LI_PAGE_SIZE);
+    return LI_OK;
+}
+
+li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt, const float *w, int32_t H)
+{
+    li::ScoreArgs a{};
+    a.pool = c->pool;
+    a.bt = c->block_table;
+    a.max_pages = c->max_pages;
+    a.seq_lens = c->seq_lens;
+    a.qseq = qs->seq;
+    a.qpos = qs->pos;
+    a.qt = qt;
+    a.w = w;
+    a.H = H;
+    a.Q = qs->Q;
+    return a;
+}
+
+} // namespace
+
+extern "C" {
+
+int32_t li_abi_version(void) { return LI_ABI_VERSION; }
+
+const char *li_last_error(void) { return g_last_error.c_str(); }
+
+const char *li_status_str(li_status s)
+{
+    switch (s) {
+    case LI_OK: return "LI_OK";
+    case LI_ERR_NULL: return "LI_ERR_NULL";
+    case LI_ERR_SHAPE: return "LI_ERR_SHAPE";
+    case LI_ERR_UNSUPPORTED: return "LI_ERR_UNSUPPORTED";
+    case LI_ERR_WORKSPACE: return "LI_ERR_WORKSPACE";
+    case LI_ERR_HIP: return "LI_ERR_HIP";
+    }
+    return "LI_ERR_UNKNOWN";
+}
+
+size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32_t r, int32_t k, int32_t M)
+{
+    (void)H;
+    (void)r;
+    if (Q < 0 || k <= 0 || k > LI_MAX_TOPK) return 0;
+    switch (op) {
+    case LI_OP_SCORE_TOPK:
+    case LI_OP_SCORE_TOPK_EXT_SCORES: {
+        if (max_valid < 0) return 0;
+        size_t b = op == LI_OP_SCORE_TOPK ? align256((size_t)Q * score_ld(max_valid) * 4) : 0;
+        return b + align256(li::sel_workspace_bytes(Q, std::max(max_valid, 1)));
+    }
+    case LI_OP_HS_SELECT:
+        if (M <= 0 || M > LI_MAX_TOPK) return 0;
+        return align256((size_t)Q * M * 4) + align256(li::sel_workspace_bytes(Q, M));
+    default: return 0;
+    }
+}
+
+li_status li_append_latent(const li_cache *cache, const void *rows, const int32_t *seq, const int32_t *pos, int32_t T,
+                           hipStream_t stream)
+{
+    li_status st = check_cache(cache);
+    if (st != LI_OK) return st;
+    if (T < 0) return fail(LI_ERR_SHAPE, "T=%d", T);
+    if (T == 0) return ok();
+    if (!rows || !seq || !pos) return fail(LI_ERR_NULL, "rows/seq/pos is NULL");
+    const int esize = cache->dtype == LI_BF16 ? 2 : 4;
+    hipError_t e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos,
+                                     T, stream);
+    if (e != hipSuccess) return hip_fail(e, "append_latent launch");
+    return ok();
+}
+
+li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32_t Q, int32_t H, int32_t d, int32_t r,
+                          li_dtype dtype, hipStream_t stream)
+{
+    if (Q < 0) return fail(LI_ERR_SHAPE, "Q=%d", Q);
+    if (H <= 0 || H > LI_MAX_HEADS) return fail(LI_ERR_SHAPE, "H=%d outside [1, %d]", H, LI_MAX_HEADS);
+    if (dtype != LI_BF16 && dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (!r_supported(r, dtype)) return fail(LI_ERR_UNSUPPORTED, "r=%d for dtype %d", r, (int)dtype);
+    if (dtype == LI_BF16 && d != 32 && d != 64 && d != 128 && d != 256)
+        return fail(LI_ERR_UNSUPPORTED, "bf16 absorption needs d in {32,64,128,256}, got %d", d);
+    if (dtype == LI_FP32 && (d <= 0 || d > 1024)) return fail(LI_ERR_SHAPE, "d=%d outside [1, 1024]", d);
+    if (Q == 0) return ok();
+    if (!q || !w_dec || !q_tilde) return fail(LI_ERR_NULL, "q/w_dec/q_tilde is NULL");
+    hipError_t e = li::launch_absorb(q, w_dec, q_tilde, (int64_t)Q * H, d, r, dtype == LI_BF16, stream);
+    if (e != hipSuccess) return hip_fail(e, "absorb_query launch");
+    return ok();
+}
+
+li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
+                        int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner, int32_t *idx_inner,
+                        int32_t *count_inner, float *scores, int64_t ld, void *ws, size_t ws_bytes,
+                        hipStream_t stream)
+{
+    li_status st = check_cache(cache);
+    if (st != LI_OK) return st;
+    st = check_queries(queries, cache);
+    if (st != LI_OK) return st;
+    if (H <= 0 || H > LI_MAX_HEADS) return fail(LI_ERR_SHAPE, "H=%d outside [1, %d]", H, LI_MAX_HEADS);
+    if (k <= 0 || k > LI_MAX_TOPK) return fail(LI_ERR_SHAPE, "k=%d outside [1, %d]", k, LI_MAX_TOPK);
+    if (k_inner < 0 || k_inner > k) return fail(LI_ERR_SHAPE, "k_inner=%d outside [0, k=%d]", k_inner, k);
+    const int32_t Q = queries->Q;
+    if (Q == 0) return ok();
+    if (!q_tilde || !w || !idx || !count) return fail(LI_ERR_NULL, "q_tilde/w/idx/count is NULL");
+    if (k_inner > 0 && (!idx_inner || !count_inner)) return fail(LI_ERR_NULL, "idx_inner/count_inner is NULL");
+    if (scores && ld < queries->max_valid) return fail(LI_ERR_SHAPE, "ld=%lld < max_valid=%d", (long long)ld, queries->max_valid);
+    const int op = scores ? LI_OP_SCORE_TOPK_EXT_SCORES : LI_OP_SCORE_TOPK;
+    const size_t need = li_workspace_bytes(op, Q, queries->max_valid, H, cache->r, k, 0);
+    if (!ws || ws_bytes < need)
+        return fail(LI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+
+    uint8_t *p = (uint8_t *)ws;
+    float *S = scores;
+    int64_t sld = ld;
+    if (!S) {
+        S = (float *)p;
+        sld = score_ld(queries->max_valid);
+        p += align256((size_t)Q * sld * 4);
+    }
+    const int64_t max_n = std::max(queries->max_valid, 1);
+    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, max_n);
+
+    li::SelCall sc{};
+    sc.row = li::SelRow{S, sld, nullptr, 0, nullptr, 0};
+    sc.src_mode = li::kSrcCausal;
+    sc.qseq = queries->seq;
+    sc.qpos = queries->pos;
+    sc.seq_lens = cache->seq_lens;
+    sc.Q = Q;
+    sc.k = k;
+    sc.max_n = max_n;
+    sc.idx = idx;
+    sc.count = count;
+
+    hipError_t e = li::launch_sel_prep(sc, sw, stream);
+    if (e != hipSuccess) return hip_fail(e, "score_topk prep");
+    if (queries->max_valid > 0) {
+        li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
+        a.out = S;
+        a.out_ld = sld;
+        a.max_rows = queries->max_valid;
+        const bool many = Q >= 4 * cache->batch;
+        e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
+        if (e != hipSuccess) return hip_fail(e, "score launch");
+    }
+    e = li::launch_select(sc, sw, stream);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+
+    if (k_inner > 0) {
+        // Nested selection among the outer winners (HS anchor: its own top-k
+        // inside its top-M candidates).
+        li::SelCall ic = sc;
+        ic.row = li::SelRow{S, sld, idx, k, idx, k};
+        ic.src_mode = li::kSrcCount;
+        ic.cnt = count;
+        ic.cnt_cap = k;
+        ic.k = k_inner;
+        ic.max_n = std::min<int64_t>(k, max_n);
+        ic.idx = idx_inner;
+        ic.count = count_inner;
+        e = li::launch_sel_prep(ic, sw, stream);
+        if (e != hipSuccess) return hip_fail(e, "inner prep");
+        e = li::launch_select(ic, sw, stream);
+        if (e != hipSuccess) return hip_fail(e, "inner select");
+    }
+    return ok();
+}
+
+li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
+                       const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w, int32_t H, int32_t k,
+                       int32_t *idx, int32_t *count, float *cand_scores, void *ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    li_status st = check_cache(cache);
+    if (st != LI_OK) return st;
+    st = check_queries(queries, cache);
+    if (st != LI_OK) return st;
+    if (H <= 0 || H > LI_MAX_HEADS) return fail(LI_ERR_SHAPE, "H=%d outside [1, %d]", H, LI_MAX_HEADS);
+    if (k <= 0 || k > LI_MAX_TOPK) return fail(LI_ERR_SHAPE, "k=%d outside [1, %d]", k, LI_MAX_TOPK);
+    if (M <= 0 || M > LI_MAX_TOPK) return fail(LI_ERR_SHAPE, "M=%d outside [1, %d]", M, LI_MAX_TOPK);
+    const int32_t Q = queries->Q;
+    if (Q == 0) return ok();
+    if (!cand || !cand_count || !q_tilde || !w || !idx || !count)
+        return fail(LI_ERR_NULL, "cand/cand_count/q_tilde/w/idx/count is NULL");
+    const size_t need = li_workspace_bytes(LI_OP_HS_SELECT, Q, 0, H, cache->r, k, M);
+    if (!ws || ws_bytes < need)
+        return fail(LI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+
+    uint8_t *p = (uint8_t *)ws;
+    float *S = cand_scores ? cand_scores : (float *)p;
+    p += align256((size_t)Q * M * 4);
+    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, M);
+
+    li::SelCall sc{};
+    sc.row = li::SelRow{S, M, nullptr, 0, cand, M};
+    sc.src_mode = li::kSrcCount;
+    sc.cnt = cand_count;
+    sc.cnt_cap = M;
+    sc.Q = Q;
+    sc.k = k;
+    sc.max_n = M;
+    sc.idx = idx;
+    sc.count = count;
+    hipError_t e = li::launch_sel_prep(sc, sw, stream);
+    if (e != hipSuccess) return hip_fail(e, "hs prep");
+
+    li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
+    a.cand = cand;
+    a.cand_count = cand_count;
+    a.cand_ld = M;
+    a.out = S;
+    a.out_ld = M;
+    a.max_rows = M;
+    e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
+    if (e != hipSuccess) return hip_fail(e, "hs score launch");
+    e = li::launch_select(sc, sw, stream);
+    if (e != hipSuccess) return hip_fail(e, "hs select launch");
+    return ok();
+}
+
+} // extern "C"

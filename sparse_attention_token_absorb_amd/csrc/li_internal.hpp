@@ -1,0 +1,91 @@
+// Host-side launchers shared between the translation units of liblatentindex.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "li_common.hpp"
+
+namespace li {
+
+// Rows to score for one call.
+//   contiguous mode (cand == nullptr): query i scores its causal prefix
+//     rows 0..n_i-1, n_i = min(qpos[i] + 1, seq_lens[qseq[i]]);
+//   gather mode: query i scores rows cand[i*cand_ld + j], j < min(cand_count[i], cand_ld).
+// out[i*out_ld + j] receives the score of the j-th row of query i.
+struct ScoreArgs {
+    const void *pool;
+    const int32_t *bt;
+    int32_t max_pages;
+    const int32_t *seq_lens;
+    const int32_t *qseq;
+    const int32_t *qpos;
+    const int32_t *cand;
+    const int32_t *cand_count;
+    int64_t cand_ld;
+    const void *qt;
+    const float *w;
+    int32_t H;
+    int32_t Q;
+    float *out;
+    int64_t out_ld;
+    int64_t max_rows; // bound on every query's row count (rows past it are not scored)
+};
+
+// Scoring.  `max_rows` bounds every query's row count (grid sizing).
+hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq,
+                        int64_t max_rows, hipStream_t s);
+
+// Absorption qt = q W (see li_absorb_query).
+hipError_t launch_absorb(const void *q, const void *W, void *qt, int64_t QH, int d, int r, bool bf16,
+                         hipStream_t s);
+
+// Append rows into the paged pool.
+hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
+                         const int32_t *seq, const int32_t *pos, int T, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Top-k selection over per-query virtual rows of scores.
+// ---------------------------------------------------------------------------
+struct SelWorkspace {
+    int32_t *nvalid;  // [Q]
+    int32_t *kq;      // [Q]
+    int32_t *ctr;     // [Q][4]
+    uint32_t *hist;   // [Q][kBins0]   (contiguous after ctr)
+    uint2 *cand;      // [Q][cap]
+    int64_t cap;
+};
+
+// How the per-query element count is found:
+//   kSrcCausal: n = min(qpos+1, seq_lens[qseq])
+//   kSrcCount : n = min(cnt[q], cnt_cap)
+enum { kSrcCausal = 0, kSrcCount = 1 };
+
+struct SelCall {
+    SelRow row;
+    int src_mode;
+    const int32_t *qseq, *qpos, *seq_lens;  // kSrcCausal
+    const int32_t *cnt;                      // kSrcCount
+    int32_t cnt_cap;
+    int32_t Q;
+    int32_t k;
+    int64_t max_n;   // host bound on every n
+    int32_t *idx;    // [Q][k]
+    int32_t *count;  // [Q]
+};
+
+// Sizes/layout of the selection workspace for Q queries with n <= max_n.
+size_t sel_workspace_bytes(int64_t Q, int64_t max_n);
+SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n);
+
+// Zero counters/histograms and compute n, K per query (must precede scoring
+// when the score kernel accumulates into the histogram).
+hipError_t launch_sel_prep(const SelCall &c, const SelWorkspace &ws, hipStream_t s);
+// The selection proper (after scores exist).
+hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, hipStream_t s);
+
+constexpr int64_t kSmallCap = 16384;  // single-workgroup selection in LDS up to this many elements
+constexpr int64_t kFinalLdsCap = 12288;
+
+} // namespace li

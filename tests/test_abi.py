@@ -1,0 +1,151 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and rejects bad arguments on the host before anything reaches the GPU.
+
+No compute call runs here: every call below fails validation (or is empty)
+and returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_token_absorb_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "latentindex.h")
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_attention_token_absorb_amd import build
+        build.build()
+    return B.lib()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\bLI_API\s+[\w\s\*]+?\b(li_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = header_symbols()
+    assert syms == sorted(B.EXPORTED), syms
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert text_syms == sorted(header_symbols()), text_syms
+
+
+def test_version_and_status_strings(L):
+    assert L.li_abi_version() == 1
+    assert L.li_status_str(0) == b"LI_OK"
+    assert L.li_status_str(4) == b"LI_ERR_WORKSPACE"
+    assert L.li_status_str(99) == b"LI_ERR_UNKNOWN"
+
+
+def cache(**kw):
+    d = dict(pool=FAKE.value, block_table=FAKE.value, seq_lens=FAKE.value, batch=1, max_pages=4, page_size=64,
+             num_pages=4, r=256, dtype=B.LI_BF16)
+    d.update(kw)
+    return B._Cache(**d)
+
+
+def queries(**kw):
+    d = dict(seq=FAKE.value, pos=FAKE.value, Q=1, max_valid=256)
+    d.update(kw)
+    return B._Queries(**d)
+
+
+def score_topk(L, c=None, q=None, H=64, k=16, k_inner=0, inner=None, ws_bytes=1 << 30, ws=FAKE, scores=None, ld=0,
+               qt=FAKE, w=FAKE, idx=FAKE, cnt=FAKE):
+    c = cache() if c is None else c
+    q = queries() if q is None else q
+    return L.li_score_topk(ctypes.byref(c) if c is not False else None, ctypes.byref(q) if q is not False else None,
+                           qt, w, H, k, idx, cnt, k_inner, inner, inner, scores, ld, ws, ws_bytes, None)
+
+
+def test_score_topk_validation(L):
+    assert score_topk(L, c=False) == B.LI_ERR_NULL
+    assert score_topk(L, q=False) == B.LI_ERR_NULL
+    assert score_topk(L, c=cache(pool=None)) == B.LI_ERR_NULL
+    assert score_topk(L, c=cache(page_size=32)) == B.LI_ERR_UNSUPPORTED
+    assert score_topk(L, c=cache(r=100)) == B.LI_ERR_UNSUPPORTED
+    assert score_topk(L, c=cache(dtype=7)) == B.LI_ERR_UNSUPPORTED
+    assert score_topk(L, c=cache(batch=0)) == B.LI_ERR_SHAPE
+    assert score_topk(L, q=queries(max_valid=4 * 64 + 1)) == B.LI_ERR_SHAPE
+    assert score_topk(L, q=queries(Q=-1)) == B.LI_ERR_SHAPE
+    assert score_topk(L, q=queries(seq=None)) == B.LI_ERR_NULL
+    assert score_topk(L, H=0) == B.LI_ERR_SHAPE
+    assert score_topk(L, H=65) == B.LI_ERR_SHAPE
+    assert score_topk(L, k=0) == B.LI_ERR_SHAPE
+    assert score_topk(L, k=65537) == B.LI_ERR_SHAPE
+    assert score_topk(L, k=16, k_inner=17) == B.LI_ERR_SHAPE
+    assert score_topk(L, k=16, k_inner=4, inner=None) == B.LI_ERR_NULL
+    assert score_topk(L, qt=None) == B.LI_ERR_NULL
+    assert score_topk(L, ws_bytes=16) == B.LI_ERR_WORKSPACE
+    assert score_topk(L, ws=None) == B.LI_ERR_WORKSPACE
+    assert score_topk(L, scores=FAKE, ld=10) == B.LI_ERR_SHAPE
+    assert b"ld=10" in L.li_last_error()
+    # nothing to do: Q = 0 succeeds without touching any pointer
+    assert score_topk(L, q=queries(Q=0, seq=None, pos=None), qt=None, w=None, idx=None, cnt=None) == B.LI_OK
+    assert L.li_last_error() == b""
+
+
+def test_hs_select_validation(L):
+    c, q = cache(), queries()
+
+    def call(M=64, k=16, cand=FAKE, ws_bytes=1 << 30, H=64):
+        return L.li_hs_select(ctypes.byref(c), ctypes.byref(q), cand, FAKE, M, FAKE, FAKE, H, k, FAKE, FAKE, None,
+                              FAKE, ws_bytes, None)
+
+    assert call(M=0) == B.LI_ERR_SHAPE
+    assert call(M=70000) == B.LI_ERR_SHAPE
+    assert call(k=0) == B.LI_ERR_SHAPE
+    assert call(H=100) == B.LI_ERR_SHAPE
+    assert call(cand=None) == B.LI_ERR_NULL
+    assert call(ws_bytes=8) == B.LI_ERR_WORKSPACE
+
+
+def test_absorb_and_append_validation(L):
+    a = lambda **kw: L.li_absorb_query(kw.get("q", FAKE), FAKE, FAKE, kw.get("Q", 1), kw.get("H", 64), kw.get("d", 128),
+                                      kw.get("r", 256), kw.get("dt", B.LI_BF16), None)
+    assert a(d=48) == B.LI_ERR_UNSUPPORTED
+    assert a(r=96) == B.LI_ERR_UNSUPPORTED
+    assert a(dt=B.LI_FP32, r=300) == B.LI_ERR_UNSUPPORTED
+    assert a(H=0) == B.LI_ERR_SHAPE
+    assert a(Q=-2) == B.LI_ERR_SHAPE
+    assert a(q=None) == B.LI_ERR_NULL
+    assert a(Q=0) == B.LI_OK
+    c = cache()
+    assert L.li_append_latent(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == B.LI_ERR_SHAPE
+    assert L.li_append_latent(ctypes.byref(c), None, FAKE, FAKE, 3, None) == B.LI_ERR_NULL
+    assert L.li_append_latent(ctypes.byref(c), None, None, None, 0, None) == B.LI_OK
+    c2 = cache(page_size=16)
+    assert L.li_append_latent(ctypes.byref(c2), FAKE, FAKE, FAKE, 3, None) == B.LI_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(L):
+    ws = lambda *a: B.workspace_bytes(*a)
+    assert ws(B.LI_OP_SCORE_TOPK, 4, 131072, 64, 256, 2048, 0) > 4 * 131072 * 4
+    assert ws(B.LI_OP_SCORE_TOPK_EXT_SCORES, 4, 131072, 64, 256, 2048, 0) < ws(B.LI_OP_SCORE_TOPK, 4, 131072, 64, 256,
+                                                                                2048, 0)
+    assert ws(B.LI_OP_HS_SELECT, 4, 0, 64, 256, 2048, 8192) >= 4 * 8192 * 4
+    assert ws(B.LI_OP_HS_SELECT, 4, 0, 64, 256, 2048, 0) == 0
+    assert ws(B.LI_OP_SCORE_TOPK, -1, 10, 64, 256, 16, 0) == 0
+    assert ws(99, 1, 10, 64, 256, 16, 0) == 0
+    small, big = ws(B.LI_OP_SCORE_TOPK, 2, 1000, 64, 256, 16, 0), ws(B.LI_OP_SCORE_TOPK, 2, 100000, 64, 256, 16, 0)
+    assert big > small
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        B.absorb_query(torch.zeros(1, 4, 32), torch.zeros(32, 64))
