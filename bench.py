@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the LatentIndex indexer hot path on one MI355X.
+
+One step = one decode step of one layer group (G = 4) for a batch of 4
+sequences at 131072 rows of context, run the three ways the long-context
+workload names:
+  (b) full LatentIndex: the anchor appends the new latent rows, every layer
+      absorbs its decoder into its query, scores all rows, selects top-2048;
+  (c) hierarchical selection: the anchor selects its top-8192 candidates
+      (with its own top-2048 nested), the 3 followers rescore only those;
+  (a) the per-layer baseline indexer: 4 separate [N][128] key caches, each
+      scored in full with the un-absorbed query.
+Inputs are seeded synthetic data resident in HBM before timing starts.  The
+step is captured once as a HIP graph and replayed; `value` is indexer rows
+scored per second over the whole step.
+
+Extra fields: per-mode µs/layer, the scoring kernel's HBM roofline (kernel
+durations from HIP events the library records around each launch), a
+context sweep 8K..128K, chunked prefill scoring (4096 queries x 65536 rows,
+one layer) against the bf16 MFMA peak, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer decode us/layer + latent rows scored/s, 8K-128K ctx; % HBM peak"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--context", type=int, default=131072)
+    ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the indexer path here is "
+              f"single-GPU and has no multi-GPU mode.", file=sys.stderr, flush=True)
+        return 2
+    import numpy as np
+    import torch
+
+    from sparse_attention_token_absorb_amd import binding as B
+    from sparse_attention_token_absorb_amd import synth
+
+    B.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    def tdev(x, dt):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dt).to(dev)
+
+    # ------------------------------------------------------------------
+    # Inputs (seeded, synthetic), resident on the GPU
+    # ------------------------------------------------------------------
+    N, Bn = args.context, args.batch
+    log(f"generating inputs B={Bn} N={N}")
+    g = synth.config4(N=N, B=Bn)
+    H, d, r, k, M, G = g.H, g.d, g.r, g.k, g.M, g.G
+
+    def make_cache(latent, width):
+        pool = torch.zeros((g.num_pages, 64, width), dtype=bf, device=dev)
+        c = B.LatentCache(pool, i32(g.block_table), i32(g.lens))
+        for b in range(Bn):
+            n = int(g.lens[b])
+            B.append_latent(c, tdev(latent[b], bf), i32(np.full(n, b)), i32(np.arange(n)))
+        return c
+
+    cache = make_cache(g.latent, r)
+    key_caches = [make_cache(g.keys_a[l], d) for l in range(G)]
+    seq, pos = i32(g.qseq), i32(g.qpos)
+    q = [tdev(g.q[l], bf) for l in range(G)]
+    W = [tdev(g.W[l], bf) for l in range(G)]
+    w = [torch.from_numpy(g.w[l]).to(dev) for l in range(G)]
+    new_rows = torch.stack([tdev(g.latent[b][N - 1], bf) for b in range(Bn)]).contiguous()
+    new_seq, new_pos = i32(np.arange(Bn)), i32(np.full(Bn, N - 1))
+    qt = [torch.empty((Bn, H, r), dtype=bf, device=dev) for _ in range(G)]
+    ws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, Bn, N, H, r, M, 0), dtype=torch.uint8, device=dev)
+    ws_hs = torch.empty(B.workspace_bytes(B.LI_OP_HS_SELECT, Bn, 0, H, r, k, M), dtype=torch.uint8, device=dev)
+
+    def topk_out(kk, inner=0):
+        o = B.TopK(torch.empty((Bn, kk), dtype=torch.int32, device=dev), torch.empty(Bn, dtype=torch.int32, device=dev))
+        if inner:
+            o.idx_inner = torch.empty((Bn, inner), dtype=torch.int32, device=dev)
+            o.count_inner = torch.empty(Bn, dtype=torch.int32, device=dev)
+        return o
+
+    out_b = [topk_out(k) for _ in range(G)]
+    out_anchor = topk_out(M, k)
+    out_f = [topk_out(k) for _ in range(G - 1)]
+    out_a = [topk_out(k) for _ in range(G)]
+    del g.keys_a
+
+    def prep():
+        B.append_latent(cache, new_rows, new_seq, new_pos)
+        for l in range(G):
+            B.absorb_query(q[l], W[l], out=qt[l])
+
+    def mode_b(max_valid=N, sq=None, sp=None):
+        for l in range(G):
+            B.score_topk(cache, sq if sq is not None else seq, sp if sp is not None else pos, max_valid, qt[l], w[l], k,
+                         ws=ws, out=out_b[l])
+
+    def mode_c():
+        B.score_topk(cache, seq, pos, N, qt[0], w[0], M, k_inner=k, ws=ws, out=out_anchor)
+        for l in range(1, G):
+            B.hs_select(cache, seq, pos, N, out_anchor.idx, out_anchor.count, qt[l], w[l], k, ws=ws_hs, out=out_f[l - 1])
+
+    def mode_a():
+        for l in range(G):
+            B.score_topk(key_caches[l], seq, pos, N, q[l], w[l], k, ws=ws, out=out_a[l])
+
+    def step():
+        prep()
+        mode_b()
+        mode_c()
+        mode_a()
+
+    stream = torch.cuda.Stream(device=dev)
+
+    def capture(fn):
+        with torch.cuda.stream(stream):
+            fn()  # eager warm-up on the capture stream
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        return graph
+
+    def time_graph(graph, reps, warm=2):
+        for _ in range(warm):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    # ------------------------------------------------------------------
+    # Headline: the whole step as one graph
+    # ------------------------------------------------------------------
+    log("capturing the step")
+    g_step = capture(step)
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g_step.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows_b = G * Bn * N
+    rows_c = Bn * N + (G - 1) * Bn * min(M, N)
+    rows_a = G * Bn * N
+    rows_step = rows_b + rows_c + rows_a
+    value = rows_step / (ms_per_step * 1e-3)
+    log(f"step {ms_per_step:.3f} ms, {value / 1e9:.2f} G rows/s")
+
+    # graph replays must agree with eager execution
+    snap = [o.idx.clone() for o in out_b] + [out_anchor.idx.clone()] + [o.idx.clone() for o in out_f]
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    for a, bb in zip(snap, [o.idx for o in out_b] + [out_anchor.idx] + [o.idx for o in out_f]):
+        for i in range(Bn):
+            sa, sb = set(a[i].tolist()), set(bb[i].tolist())
+            assert len(sa ^ sb) <= 2, "graph replay disagrees with eager execution"
+
+    # ------------------------------------------------------------------
+    # Per-mode µs/layer (graphs of one mode each)
+    # ------------------------------------------------------------------
+    reps = max(args.steps, 10)
+    ms_prep = time_graph(capture(prep), reps)
+    ms_b = time_graph(capture(mode_b), reps)
+    ms_c = time_graph(capture(mode_c), reps)
+    ms_a = time_graph(capture(mode_a), reps)
+    modes = {
+        "append_plus_absorb_x4_us": round(ms_prep * 1e3, 2),
+        "full_latentindex_us_per_layer": round(ms_b * 1e3 / G, 2),
+        "hs_us_per_group": round(ms_c * 1e3, 2),
+        "hs_us_per_layer_avg": round(ms_c * 1e3 / G, 2),
+        "baseline_per_layer_indexer_us_per_layer": round(ms_a * 1e3 / G, 2),
+        "group_us": {"full": round(ms_b * 1e3, 1), "hs": round(ms_c * 1e3, 1), "baseline": round(ms_a * 1e3, 1)},
+        "rows_per_step": {"full": rows_b, "hs": rows_c, "baseline": rows_a},
+        "hs_speedup_over_baseline_group": round(ms_a / ms_c, 3) if ms_c > 0 else None,
+    }
+    log(f"modes {modes}")
+
+    # ------------------------------------------------------------------
+    # Roofline of the decode scoring kernel (HIP events around each launch)
+    # ------------------------------------------------------------------
+    def kernel_time(fn, cls, reps_):
+        B.timing_read(cls)
+        B.timing_enable(True)
+        try:
+            with torch.cuda.stream(stream):
+                for _ in range(reps_):
+                    fn()
+            torch.cuda.synchronize()
+        finally:
+            B.timing_enable(False)
+        tot, n = B.timing_read(cls)
+        for other in range(6):  # recycle the events of the other classes
+            if other != cls:
+                B.timing_read(other)
+        return tot / max(n, 1), n
+
+    bytes_row = 2 * r
+    bytes_query = H * r * 2 + H * 4
+    bytes_launch = Bn * N * bytes_row + Bn * bytes_query
+    score_ms, n_launch = kernel_time(mode_b, B.LI_KERNEL_SCORE_DECODE, reps)
+    sel_ms, _ = kernel_time(mode_b, B.LI_KERNEL_SELECT, reps)
+    achieved = bytes_launch / (score_ms * 1e-3) / 1e9
+    # cold: a 1 GiB scrub between launches evicts the 256 MB Infinity Cache
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def cold_b():
+        for l in range(G):
+            scrub.add_(1.0)
+            B.score_topk(cache, seq, pos, N, qt[l], w[l], k, ws=ws, out=out_b[l])
+
+    cold_ms, _ = kernel_time(cold_b, B.LI_KERNEL_SCORE_DECODE, max(reps // 2, 4))
+    del scrub
+    a_score_ms, _ = kernel_time(mode_a, B.LI_KERNEL_SCORE_DECODE, reps)
+    a_bytes = Bn * N * 2 * d + Bn * (H * d * 2 + H * 4)
+    f_ms, _ = kernel_time(mode_c, B.LI_KERNEL_SCORE_GATHER, reps)
+    f_bytes = Bn * min(M, N) * (bytes_row + 4) + Bn * bytes_query
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "kernel": f"k_score_decode<r={r},64 heads> (full LatentIndex, B={Bn}, N={N})",
+        "avg_launch_us": round(score_ms * 1e3, 2), "launches": n_launch, "bytes_per_launch": bytes_launch,
+        "cold_avg_launch_us": round(cold_ms * 1e3, 2),
+        "cold_achieved_GBs": round(bytes_launch / (cold_ms * 1e-3) / 1e9, 1),
+        "select_us_per_layer": round(sel_ms * 1e3, 2),
+        "baseline_r128_score_us": round(a_score_ms * 1e3, 2),
+        "baseline_r128_GBs": round(a_bytes / (a_score_ms * 1e-3) / 1e9, 1),
+        "hs_follower_gather_score_us": round(f_ms * 1e3, 2),
+        "hs_follower_gather_GBs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
+    }
+    log(f"roofline {roofline}")
+
+    # ------------------------------------------------------------------
+    # Context sweep 8K..128K (full LatentIndex, same cache, shorter prefixes)
+    # ------------------------------------------------------------------
+    sweep = {}
+    if not args.no_sweep:
+        for n_ctx in (8192, 16384, 32768, 65536, 131072):
+            if n_ctx > N:
+                continue
+            sp = i32(np.full(Bn, n_ctx - 1))
+            gr = capture(lambda: mode_b(n_ctx, seq, sp))
+            ms = time_graph(gr, reps)
+            sc_ms, _ = kernel_time(lambda: mode_b(n_ctx, seq, sp), B.LI_KERNEL_SCORE_DECODE, reps)
+            by = Bn * n_ctx * bytes_row + Bn * bytes_query
+            sweep[str(n_ctx)] = {"us_per_layer": round(ms * 1e3 / G, 2),
+                                 "rows_per_s": round(G * Bn * n_ctx / (ms * 1e-3), 1),
+                                 "score_kernel_us": round(sc_ms * 1e3, 2),
+                                 "score_frac_hbm": round(by / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del gr
+        log(f"sweep {sweep}")
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the fp64 oracle on a bounded sample of the same workload
+    # ------------------------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        rows_done = 0
+        layers_done = 0
+        for l in range(G):
+            oracle.full_layer(g.q[l], g.W[l], g.w[l], g.latent, g.qseq, g.qpos, g.lens, k)
+            rows_done += Bn * N
+            layers_done += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        el = time.perf_counter() - t0
+        cpu = {"value": round(rows_done / el, 1), "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"full LatentIndex (mode b), {layers_done} layer(s) x {Bn} queries x {N} rows: absorb, "
+                         f"fp64 scoring and top-{k} sort; {el:.1f} s"}
+        log(f"cpu baseline {cpu}")
+
+    # ------------------------------------------------------------------
+    # Chunked prefill scoring: 4096 queries x 65536 causal rows, one layer
+    # ------------------------------------------------------------------
+    prefill = None
+    if not args.no_prefill:
+        del cache, key_caches
+        torch.cuda.empty_cache()
+        log("prefill inputs")
+        p5 = synth.make_prefill("prefill", 5, N=65536, Qn=4096, r=r, H=H, d=d, G=1, k=k)
+        pcache = make_cache_from(p5, B, tdev, i32, bf, dev)
+        pseq, ppos = i32(p5.qseq), i32(p5.qpos)
+        pq, pW, pw = tdev(p5.q[0], bf), tdev(p5.W[0], bf), torch.from_numpy(p5.w[0]).to(dev)
+        pqt = torch.empty((p5.Q, H, r), dtype=bf, device=dev)
+        pws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, p5.Q, 65536, H, r, k, 0), dtype=torch.uint8,
+                          device=dev)
+        pout = B.TopK(torch.empty((p5.Q, k), dtype=torch.int32, device=dev),
+                      torch.empty(p5.Q, dtype=torch.int32, device=dev))
+
+        def prefill_layer():
+            B.absorb_query(pq, pW, out=pqt)
+            B.score_topk(pcache, pseq, ppos, 65536, pqt, pw, k, ws=pws, out=pout)
+
+        with torch.cuda.stream(stream):
+            prefill_layer()
+        torch.cuda.synchronize()
+        preps = 5
+        sc_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_SCORE_PREFILL, preps)
+        sel_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_SELECT, preps)
+        ab_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_ABSORB, preps)
+        pairs = int(np.sum(np.minimum(p5.qpos.astype(np.int64) + 1, 65536)))
+        flops = 2.0 * H * r * pairs
+        tf = flops / (sc_ms * 1e-3) / 1e12
+        prefill = {"workload": "4096 queries at positions 61440..65535 of a 65536-row cache, one layer",
+                   "score_ms": round(sc_ms, 3), "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
+                   "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "select_ms": round(sel_ms, 3),
+                   "absorb_ms": round(ab_ms, 3), "valid_pairs": pairs}
+        log(f"prefill {prefill}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode step of one layer group, B={Bn}, context {N}: full LatentIndex x{G} layers "
+                               f"+ HS (M={M}) + per-layer baseline indexer x{G}",
+                   "batch": Bn, "context": N, "heads": H, "d": d, "r": r, "k": k, "M": M, "group": G,
+                   "parallelism": "single GPU"},
+        "modes": modes, "roofline": roofline, "sweep": sweep, "prefill": prefill, "cpu_baseline": cpu,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+    return 0
+
+
+def make_cache_from(g, B, tdev, i32, bf, dev):
+    import numpy as np
+    import torch
+    pool = torch.zeros((g.num_pages, 64, g.r), dtype=bf, device=dev)
+    c = B.LatentCache(pool, i32(g.block_table), i32(g.lens))
+    for b in range(g.B):
+        n = int(g.lens[b])
+        B.append_latent(c, tdev(g.latent[b], bf), i32(np.full(n, b)), i32(np.arange(n)))
+    return c
+
+
+if __name__ == "__main__":
+    sys.exit(main())

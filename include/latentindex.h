@@ -173,6 +173,32 @@ enum { LI_OP_SCORE_TOPK = 0, LI_OP_HS_SELECT = 1, LI_OP_SCORE_TOPK_EXT_SCORES = 
 LI_API size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32_t r, int32_t k,
                           int32_t M);
 
+/*
+ * Kernel timing (instrumentation for benchmarks and profiling).  While
+ * enabled, the library brackets each launch of a kernel class with a pair of
+ * HIP events recorded on the call's stream.  li_timing_read waits for the
+ * recorded events of one class, returns their summed milliseconds and the
+ * number of bracketed launches since the previous read of that class, and
+ * forgets them.  Enabling timing creates HIP events (host-side objects; no
+ * device memory).  Do not enable it while capturing a HIP graph.
+ *   LI_KERNEL_SCORE_DECODE   full-prefix scoring, few queries per sequence
+ *   LI_KERNEL_SCORE_PREFILL  full-prefix scoring, many queries per sequence
+ *   LI_KERNEL_SCORE_GATHER   HS follower candidate scoring
+ *   LI_KERNEL_SELECT         one top-k selection (all of its kernels)
+ *   LI_KERNEL_ABSORB, LI_KERNEL_APPEND
+ */
+typedef enum {
+    LI_KERNEL_SCORE_DECODE = 0,
+    LI_KERNEL_SCORE_PREFILL = 1,
+    LI_KERNEL_SCORE_GATHER = 2,
+    LI_KERNEL_SELECT = 3,
+    LI_KERNEL_ABSORB = 4,
+    LI_KERNEL_APPEND = 5,
+    LI_KERNEL_CLASSES = 6
+} li_kernel_class;
+LI_API li_status li_timing_enable(int on);
+LI_API li_status li_timing_read(int kernel_class, double *total_ms, int64_t *launches);
+
 LI_API const char *li_status_str(li_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 LI_API const char *li_last_error(void);

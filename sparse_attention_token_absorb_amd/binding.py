@@ -23,7 +23,9 @@ LI_BF16, LI_FP32 = 0, 1
 LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
 EXPORTED = ["li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select", "li_workspace_bytes",
-            "li_status_str", "li_last_error", "li_abi_version"]
+            "li_timing_enable", "li_timing_read", "li_status_str", "li_last_error", "li_abi_version"]
+(LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
+ LI_KERNEL_APPEND) = range(6)
 
 
 class LIError(RuntimeError):
@@ -66,6 +68,10 @@ def lib():
         L.li_last_error.argtypes = []
         L.li_last_error.restype = ctypes.c_char_p
         L.li_abi_version.restype = i32
+        L.li_timing_enable.argtypes = [ctypes.c_int]
+        L.li_timing_enable.restype = ctypes.c_int
+        L.li_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.li_timing_read.restype = ctypes.c_int
         for f in ("li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -161,6 +167,19 @@ def _queries(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid
     if seq.dim() != 1 or pos.shape != seq.shape:
         raise ValueError("seq and pos must be [Q]")
     return _Queries(seq.data_ptr(), pos.data_ptr(), int(seq.shape[0]), int(max_valid))
+
+
+def timing_enable(on: bool) -> None:
+    """li_timing_enable: bracket every kernel-class launch with HIP events."""
+    _check(lib().li_timing_enable(1 if on else 0), "li_timing_enable")
+
+
+def timing_read(kernel_class: int) -> Tuple[float, int]:
+    """li_timing_read: (summed ms, launches) of one class since the last read."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(lib().li_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n)), "li_timing_read")
+    return float(ms.value), int(n.value)
 
 
 def workspace_bytes(op: int, Q: int, max_valid: int, H: int, r: int, k: int, M: int = 0) -> int:

@@ -11,6 +11,7 @@
 
 #include "../../include/latentindex.h"
 #include "li_internal.hpp"
+#include "li_timing.hpp"
 
 namespace {
 
@@ -138,8 +139,12 @@ li_status li_append_latent(const li_cache *cache, const void *rows, const int32_
     if (T == 0) return ok();
     if (!rows || !seq || !pos) return fail(LI_ERR_NULL, "rows/seq/pos is NULL");
     const int esize = cache->dtype == LI_BF16 ? 2 : 4;
-    hipError_t e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos,
-                                     T, stream);
+    hipError_t e;
+    {
+        li::TimedScope ts(LI_KERNEL_APPEND, stream);
+        e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos, T,
+                              stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "append_latent launch");
     return ok();
 }
@@ -156,7 +161,11 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
     if (dtype == LI_FP32 && (d <= 0 || d > 1024)) return fail(LI_ERR_SHAPE, "d=%d outside [1, 1024]", d);
     if (Q == 0) return ok();
     if (!q || !w_dec || !q_tilde) return fail(LI_ERR_NULL, "q/w_dec/q_tilde is NULL");
-    hipError_t e = li::launch_absorb(q, w_dec, q_tilde, (int64_t)Q * H, d, r, dtype == LI_BF16, stream);
+    hipError_t e;
+    {
+        li::TimedScope ts(LI_KERNEL_ABSORB, stream);
+        e = li::launch_absorb(q, w_dec, q_tilde, (int64_t)Q * H, d, r, dtype == LI_BF16, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "absorb_query launch");
     return ok();
 }
@@ -206,18 +215,26 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     sc.idx = idx;
     sc.count = count;
 
-    hipError_t e = li::launch_sel_prep(sc, sw, stream);
+    const bool many = Q >= 4 * cache->batch;
+    hipError_t e;
+    {
+        li::TimedScope ts(LI_KERNEL_SELECT, stream);
+        e = li::launch_sel_prep(sc, sw, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "score_topk prep");
     if (queries->max_valid > 0) {
         li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
         a.out = S;
         a.out_ld = sld;
         a.max_rows = queries->max_valid;
-        const bool many = Q >= 4 * cache->batch;
+        li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
         e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
         if (e != hipSuccess) return hip_fail(e, "score launch");
     }
-    e = li::launch_select(sc, sw, stream);
+    {
+        li::TimedScope ts(LI_KERNEL_SELECT, stream);
+        e = li::launch_select(sc, sw, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "select launch");
 
     if (k_inner > 0) {
@@ -232,6 +249,7 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         ic.max_n = std::min<int64_t>(k, max_n);
         ic.idx = idx_inner;
         ic.count = count_inner;
+        li::TimedScope ts(LI_KERNEL_SELECT, stream);
         e = li::launch_sel_prep(ic, sw, stream);
         if (e != hipSuccess) return hip_fail(e, "inner prep");
         e = li::launch_select(ic, sw, stream);
@@ -275,7 +293,11 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     sc.max_n = M;
     sc.idx = idx;
     sc.count = count;
-    hipError_t e = li::launch_sel_prep(sc, sw, stream);
+    hipError_t e;
+    {
+        li::TimedScope ts(LI_KERNEL_SELECT, stream);
+        e = li::launch_sel_prep(sc, sw, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "hs prep");
 
     li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
@@ -285,10 +307,32 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.out = S;
     a.out_ld = M;
     a.max_rows = M;
-    e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
+    {
+        li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
+        e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "hs score launch");
-    e = li::launch_select(sc, sw, stream);
+    {
+        li::TimedScope ts(LI_KERNEL_SELECT, stream);
+        e = li::launch_select(sc, sw, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "hs select launch");
+    return ok();
+}
+
+li_status li_timing_enable(int on)
+{
+    li::timing_enable(on != 0);
+    return ok();
+}
+
+li_status li_timing_read(int kernel_class, double *total_ms, int64_t *launches)
+{
+    if (kernel_class < 0 || kernel_class >= LI_KERNEL_CLASSES)
+        return fail(LI_ERR_SHAPE, "kernel class %d outside [0, %d)", kernel_class, (int)LI_KERNEL_CLASSES);
+    if (!total_ms || !launches) return fail(LI_ERR_NULL, "total_ms/launches is NULL");
+    hipError_t e = li::timing_read(kernel_class, total_ms, launches);
+    if (e != hipSuccess) return hip_fail(e, "timing read");
     return ok();
 }
 

@@ -284,7 +284,8 @@ __global__ __launch_bounds__(256) void k_sel_final(SelCall c, SelWorkspace ws)
             const uint32_t need = (uint32_t)(K - above);
             const int64_t nc = ws.ctr[q * kCtr + 1];
             const uint2 *cand = ws.cand + (int64_t)q * ws.cap;
-            if (nc <= kFinalLdsCap) {
+            // The list holds min(nc, cap) entries: use it only when complete.
+            if (nc <= ws.cap && nc <= kFinalLdsCap) {
                 for (int64_t i = threadIdx.x; i < nc; i += kBlock) {
                     const uint2 p = cand[i];
                     sk[i] = p.x;
