@@ -216,24 +216,26 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     sc.count = count;
 
     const bool many = Q >= 4 * cache->batch;
-    hipError_t e;
-    {
-        li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_sel_prep(sc, sw, stream);
-    }
-    if (e != hipSuccess) return hip_fail(e, "score_topk prep");
-    if (queries->max_valid > 0) {
+    const bool scored = queries->max_valid > 0;
+    hipError_t e = hipSuccess;
+    if (scored) {
+        {
+            li::TimedScope ts(LI_KERNEL_SELECT, stream);
+            e = li::launch_hist_clear(sw, Q, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "histogram clear");
         li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
         a.out = S;
         a.out_ld = sld;
         a.max_rows = queries->max_valid;
+        a.hist = sw.hist;
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
         e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
         if (e != hipSuccess) return hip_fail(e, "score launch");
     }
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(sc, sw, stream);
+        e = li::launch_select(sc, sw, scored, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "select launch");
 
@@ -250,9 +252,7 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         ic.idx = idx_inner;
         ic.count = count_inner;
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_sel_prep(ic, sw, stream);
-        if (e != hipSuccess) return hip_fail(e, "inner prep");
-        e = li::launch_select(ic, sw, stream);
+        e = li::launch_select(ic, sw, false, stream);
         if (e != hipSuccess) return hip_fail(e, "inner select");
     }
     return ok();
@@ -293,13 +293,13 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     sc.max_n = M;
     sc.idx = idx;
     sc.count = count;
+
     hipError_t e;
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_sel_prep(sc, sw, stream);
+        e = li::launch_hist_clear(sw, Q, stream);
     }
-    if (e != hipSuccess) return hip_fail(e, "hs prep");
-
+    if (e != hipSuccess) return hip_fail(e, "histogram clear");
     li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
     a.cand = cand;
     a.cand_count = cand_count;
@@ -307,6 +307,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.out = S;
     a.out_ld = M;
     a.max_rows = M;
+    a.hist = sw.hist;
     {
         li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
         e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
@@ -314,7 +315,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     if (e != hipSuccess) return hip_fail(e, "hs score launch");
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(sc, sw, stream);
+        e = li::launch_select(sc, sw, true, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "hs select launch");
     return ok();

@@ -16,8 +16,7 @@ constexpr int kPage = 64;        // rows per cache page
 constexpr int kTile = 32;        // latent rows per MFMA column tile
 constexpr int kWave = 64;
 constexpr int kBlock = 256;      // threads per workgroup of every kernel here
-constexpr int kDigit0Shift = 21; // first radix digit: key bits [31:21]
-constexpr int kBins0 = 2048;
+constexpr int kDigit0Shift = 20; // first radix digit: key bits [31:20]
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger
 // key).  -0.0 is folded onto +0.0 so equal scores give equal keys.
@@ -45,6 +44,18 @@ __device__ __forceinline__ u16 f32_to_bf16_rne(float f)
 }
 
 __device__ __forceinline__ float bf16_to_f32(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+    return v;
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 // The memory clobber keeps the compiler from moving LDS reads above it.

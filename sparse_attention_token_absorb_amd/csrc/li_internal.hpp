@@ -9,6 +9,10 @@
 
 namespace li {
 
+constexpr int kHistBins = 4096;   // first radix digit: key bits [31:20]
+constexpr int kHistStride = kHistBins + 4; // per query: histogram, then 4 counters
+constexpr int kSelThreads = 1024; // threads of the per-query selection workgroup
+
 // Rows to score for one call.
 //   contiguous mode (cand == nullptr): query i scores its causal prefix
 //     rows 0..n_i-1, n_i = min(qpos[i] + 1, seq_lens[qseq[i]]);
@@ -31,6 +35,7 @@ struct ScoreArgs {
     float *out;
     int64_t out_ld;
     int64_t max_rows; // bound on every query's row count (rows past it are not scored)
+    int32_t *hist;    // optional [Q][kHistStride]: first-digit counts of the keys written (accumulated)
 };
 
 // Scoring.  `max_rows` bounds every query's row count (grid sizing).
@@ -49,11 +54,8 @@ hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, in
 // Top-k selection over per-query virtual rows of scores.
 // ---------------------------------------------------------------------------
 struct SelWorkspace {
-    int32_t *nvalid;  // [Q]
-    int32_t *kq;      // [Q]
-    int32_t *ctr;     // [Q][4]
-    uint32_t *hist;   // [Q][kBins0]   (contiguous after ctr)
-    uint2 *cand;      // [Q][cap]
+    int32_t *hist; // [Q][kHistStride]: first-digit counts, then counters (rows emitted, rows tied)
+    uint2 *cand;   // [Q][cap] (key, index) of rows tied on the threshold digit
     int64_t cap;
 };
 
@@ -75,17 +77,13 @@ struct SelCall {
     int32_t *count;  // [Q]
 };
 
-// Sizes/layout of the selection workspace for Q queries with n <= max_n.
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n);
 SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n);
 
-// Zero counters/histograms and compute n, K per query (must precede scoring
-// when the score kernel accumulates into the histogram).
-hipError_t launch_sel_prep(const SelCall &c, const SelWorkspace &ws, hipStream_t s);
-// The selection proper (after scores exist).
-hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, hipStream_t s);
-
-constexpr int64_t kSmallCap = 16384;  // single-workgroup selection in LDS up to this many elements
-constexpr int64_t kFinalLdsCap = 12288;
+// Zero the histograms (before a scoring kernel accumulates into them).
+hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s);
+// The selection proper (after scores exist).  have_hist: a scoring kernel
+// filled ws.hist for these very scores.
+hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s);
 
 } // namespace li

@@ -6,15 +6,18 @@
 // against N rows this is a dense (heads x r) . (r x rows) contraction, so
 // it runs on MFMA: v_mfma_f32_32x32x16_bf16 with
 //   A (32 heads x 16 k)  = absorbed query, held in VGPRs for the whole kernel,
-//   B (16 k x 32 rows)   = a 32-row latent tile staged in LDS,
+//   B (16 k x 32 rows)   = latent rows staged in LDS,
 //   D (32 heads x 32 rows) fp32; lane l owns row l%32 and 16 heads of it,
 // so the ReLU, the head weights and the head sum are a per-lane loop plus one
 // exchange between the two lane halves.
 //
-// Latent tiles travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-// staging).  Each 1 KiB DMA instruction copies 512/r whole rows; within a
-// row the 16-byte chunks are XOR-swizzled by the row index so that the MFMA
-// operand reads (32 rows, same chunk) hit distinct LDS banks.
+// Latent rows travel HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+// staging); within a row the 16-byte pieces are XOR-swizzled by the row
+// index so that the MFMA operand reads (32 rows, same piece) hit distinct
+// LDS banks.  The epilogue also counts each score's first radix digit
+// (key >> 20) into an LDS histogram that is merged into the query's global
+// histogram at the end (only non-empty bins), so the top-k selection that
+// follows starts from a known threshold bin.
 #include "li_internal.hpp"
 
 #include <algorithm>
@@ -51,31 +54,22 @@ __device__ __forceinline__ void wait_lds()
 
 __device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
 
-__device__ __forceinline__ int64_t shfl64(int64_t v, int src)
+// Wait until at most `after` * PER vector-memory operations are in flight
+// (the count must be an immediate, hence the switch).
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_after(int after)
 {
-    int lo = __shfl((int)(uint32_t)(uint64_t)v, src);
-    int hi = __shfl((int)(uint32_t)((uint64_t)v >> 32), src);
-    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-// Dynamic-count wait (the count must be an immediate).
-template <int NIW>
-__device__ __forceinline__ void wait_after(int tiles_after)
-{
-    switch (tiles_after) {
+    static_assert(PER * MAXA < 64, "vmcnt range");
+    switch (after) {
     case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<NIW>(); break;
-    case 2: wait_vmcnt<2 * NIW < 63 ? 2 * NIW : 0>(); break;
-    default: wait_vmcnt<3 * NIW < 63 ? 3 * NIW : 0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<(MAXA >= 2 ? 2 : 1) * PER>(); break;
+    case 3: wait_vmcnt<(MAXA >= 3 ? 3 : 1) * PER>(); break;
+    case 4: wait_vmcnt<(MAXA >= 4 ? 4 : 1) * PER>(); break;
+    case 5: wait_vmcnt<(MAXA >= 5 ? 5 : 1) * PER>(); break;
+    case 6: wait_vmcnt<(MAXA >= 6 ? 6 : 1) * PER>(); break;
+    default: wait_vmcnt<(MAXA >= 7 ? 7 : 1) * PER>(); break;
     }
-}
-
-// LDS byte offset of 16-byte chunk c of tile row nr.
-template <int R>
-__device__ __forceinline__ int lds_chunk(int nr, int c)
-{
-    constexpr int CH = R / 8;
-    return (nr * CH + (c ^ (nr % CH))) * 16;
 }
 
 // Absorbed-query fragments (MFMA A operand) and per-lane head weights.
@@ -108,84 +102,84 @@ struct QueryRegs {
     }
 };
 
-// Score of tile row (lane % 32), complete in every lane.
-template <int R, int HB>
-__device__ __forceinline__ float tile_score(const lds_u8 *buf, const QueryRegs<R, HB> &qr)
+// MFMA steps over the LDS buffer holding columns [S0*16, (S0+KS)*16) of a
+// 32-row tile, `CH` 16-byte pieces per buffer row.
+template <int R, int HB, int S0, int KS, int CH>
+__device__ __forceinline__ void mfma_steps(const lds_u8 *buf, const QueryRegs<R, HB> &qr, f32x16 (&acc)[HB])
 {
     const int lane = threadIdx.x & 63;
     const int nr = lane & 31, g = lane >> 5;
-    f32x16 acc[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        f32x16 z = {};
-        acc[hb] = z;
-    }
-#pragma unroll
-    for (int s = 0; s < R / 16; ++s) {
-        const bf16x8 b = *(lds_bf16x8 *)(buf + lds_chunk<R>(nr, 2 * s + g));
+    for (int s = 0; s < KS; ++s) {
+        const int c = 2 * s + g;
+        const bf16x8 b = *(lds_bf16x8 *)(buf + (nr * CH + (c ^ (nr % CH))) * 16);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][s], b, acc[hb], 0, 0, 0);
+            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][S0 + s], b, acc[hb], 0, 0, 0);
     }
+}
+
+// ReLU, head weights and head sum: the score of tile row (lane % 32).
+template <int HB>
+__device__ __forceinline__ float epilogue(const f32x16 (&acc)[HB], const float (&w)[HB][16])
+{
     float p = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            p += qr.w[hb][r] * fmaxf(acc[hb][r], 0.0f);
-    p += __shfl_xor(p, 32);
-    return p;
+            p += w[hb][r] * fmaxf(acc[hb][r], 0.0f);
+    return p + __shfl_xor(p, 32);
 }
 
-// One wave copies a 32-row tile whose rows start at the given pool element
-// offsets (rowoff of tile row i lives in lane i).
-template <int R>
-__device__ __forceinline__ void issue_tile_rows(const u16 *pool, int64_t rowoff, lds_u8 *buf)
+// Copy `NIC` KiB of a 32-row tile (CH pieces of 16 B per row, starting at
+// column `col0`) into LDS: instruction ii moves 64/CH rows.  rowoff(nr)
+// gives the pool element offset of tile row nr.
+template <int R, int CH, int NIC, class RowOff>
+__device__ __forceinline__ void issue_rows(const u16 *pool, const RowOff &rowoff, int col0, lds_u8 *buf, int ii0,
+                                           int nii)
 {
-    constexpr int CH = R / 8, NI = R / 16;
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-        const int p = ii * 64 + lane;
-        const int nr = p / CH, cs = p % CH;
-        const int c = cs ^ (nr % CH);
-        const int64_t off = shfl64(rowoff, nr);
-        dma16(pool + off + c * 8, buf + ii * 1024);
-    }
-}
-
-// Part `part` of `parts` of a 32-row tile of physically contiguous rows.
-template <int R>
-__device__ __forceinline__ void issue_tile_contig(const u16 *tile_base, lds_u8 *buf, int part, int parts)
-{
-    constexpr int CH = R / 8, NI = R / 16;
-    const int lane = threadIdx.x & 63;
-    const int per = NI / parts;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        if (j < per) {
-            const int ii = part * per + j;
+    for (int j = 0; j < NIC; ++j) {
+        if (j < nii) {
+            const int ii = ii0 + j;
             const int p = ii * 64 + lane;
             const int nr = p / CH, cs = p % CH;
             const int c = cs ^ (nr % CH);
-            dma16(tile_base + nr * R + c * 8, buf + ii * 1024);
+            dma16(pool + rowoff(nr) + col0 + c * 8, buf + ii * 1024);
         }
     }
 }
 
+__device__ __forceinline__ void hist_zero(uint32_t *h, int nthreads, int tid)
+{
+    for (int i = tid; i < kHistBins; i += nthreads) h[i] = 0;
+}
+
+__device__ __forceinline__ void hist_flush(const uint32_t *h, int32_t *g, int nthreads, int tid)
+{
+    for (int i = tid; i < kHistBins; i += nthreads)
+        if (h[i]) atomicAdd(&g[i], (int)h[i]);
+}
+
 // ---------------------------------------------------------------------------
-// Decode: few queries, long rows.  Workgroup = 4 waves of one query; each
-// wave streams its own tiles (rows row0 + (wave + 4 i) * 32) through two LDS
-// buffers, keeping one tile in flight while it computes the other.
+// Decode: few queries, long rows.  Workgroup = 4 waves of one query; wave w
+// streams tiles row0 + (w + 4 i) * 32.  Each tile moves as two half-width
+// chunks (32 rows x r/2 columns) through a per-wave ring of NB chunk
+// buffers, so NB-1 chunks stay in flight while the wave computes.
 // ---------------------------------------------------------------------------
-template <int R, int HB, bool GATHER>
+template <int R, int HB, bool GATHER, int NB>
 __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per_wave)
 {
-    constexpr int TILE_BYTES = kTile * R * 2;
-    constexpr int NI = R / 16;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[4 * 2 * TILE_BYTES];
-    __shared__ int64_t s_off[GATHER ? 4 * kGatherTiles * kTile : 1];
-    lds_u8 *lds = (lds_u8 *)lds_raw;
+    constexpr int HALF = R / 2;                 // columns per chunk
+    constexpr int CHUNK = kTile * HALF * 2;     // bytes per chunk
+    constexpr int NIC = CHUNK / 1024;           // DMA instructions per chunk
+    constexpr int CH = HALF / 8;                // 16-byte pieces per chunk row
+    constexpr int KSH = HALF / 16;              // MFMA k-steps per chunk
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * CHUNK];
+    __shared__ int32_t s_row[GATHER ? 4 * kGatherTiles * kTile : 1];
+    __shared__ uint32_t s_hist[kHistBins];
 
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -193,64 +187,79 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     const int b = a.qseq[q];
     int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
-    const int64_t rows_per_wg = (int64_t)4 * tiles_per_wave * kTile;
-    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     if (row0 >= n) return;
-    // tiles of this wave: t = row0 + (wv + 4 i) * 32, i < nt
+    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     const int64_t first = row0 + (int64_t)wv * kTile;
     int nt = 0;
     if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
+    const int nchunks = 2 * nt;
 
     const u16 *pool = (const u16 *)a.pool;
     const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
-    lds_u8 *const wbuf = lds + wv * 2 * TILE_BYTES;
-    auto buf = [&](int i) -> lds_u8 * { return wbuf + (i & 1) * TILE_BYTES; };
-
+    lds_u8 *const ring = (lds_u8 *)ring_raw + wv * NB * CHUNK;
     auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
-    // element offset in the pool of row (lane & 31) of tile i
-    auto gather_off = [&](int i) -> int64_t {
-        int64_t j = tile_row0(i) + (lane & 31);
-        j = j < n ? j : n - 1;
-        const int pos = a.cand[(int64_t)q * a.cand_ld + j];
-        const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
-        return ((int64_t)page * kPage + (pos & 63)) * R;
-    };
-    auto issue = [&](int i) {
-        if constexpr (GATHER) {
-            issue_tile_rows<R>(pool, s_off[(wv * kGatherTiles + i) * kTile + (lane & 31)], buf(i));
-        } else {
-            const int64_t t0 = tile_row0(i);
-            const int page = bt[t0 >> 6];
-            issue_tile_contig<R>(pool + ((int64_t)page * kPage + (t0 & 63)) * R, buf(i), 0, 1);
-        }
-    };
 
     if constexpr (GATHER) {
-        // Row offsets of every tile of this wave, resolved once up front.
+        // Physical rows of every tile of this wave, resolved once up front.
         for (int i = 0; i < nt; ++i) {
-            const int64_t off = gather_off(i);
-            if (lane < 32) s_off[(wv * kGatherTiles + i) * kTile + lane] = off;
+            int64_t j = tile_row0(i) + (lane & 31);
+            j = j < n ? j : n - 1;
+            const int pos = a.cand[(int64_t)q * a.cand_ld + j];
+            const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
+            if (lane < 32) s_row[(wv * kGatherTiles + i) * kTile + lane] = page * kPage + (pos & 63);
         }
         wait_vmcnt<0>();
         wait_lds();
     }
+    auto issue = [&](int c) {
+        const int i = c >> 1;
+        lds_u8 *buf = ring + (c % NB) * CHUNK;
+        if constexpr (GATHER) {
+            const __attribute__((address_space(3))) int32_t *rows =
+                (const __attribute__((address_space(3))) int32_t *)s_row + (wv * kGatherTiles + i) * kTile;
+            issue_rows<R, CH, NIC>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c & 1) * HALF, buf, 0, NIC);
+        } else {
+            const int64_t t0 = tile_row0(i);
+            const int64_t base = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63)) * R;
+            issue_rows<R, CH, NIC>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c & 1) * HALF, buf, 0, NIC);
+        }
+    };
 
-    if (nt > 0) issue(0);
+    for (int c = 0; c < NB - 1 && c < nchunks; ++c) issue(c);
     QueryRegs<R, HB> qr;
     qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
-    if (nt > 1) issue(1);
+    if (a.hist) wg_barrier(); // histogram cleared before any wave counts into it
 
     float *out = a.out + (int64_t)q * a.out_ld;
-    for (int i = 0; i < nt; ++i) {
-        if (i + 1 < nt) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
-        const float p = tile_score<R, HB>(buf(i), qr);
-        const int64_t j = tile_row0(i) + lane;
-        if (lane < 32 && j < n) out[j] = p;
-        if (i + 2 < nt) {
-            wait_lds(); // this wave's reads of the buffer are done before it is refilled
-            issue(i + 2);
+    f32x16 acc[HB];
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + NB - 1 < nchunks) {
+            wait_lds(); // this wave's reads of that buffer (chunk c-1) are complete
+            issue(c + NB - 1);
         }
+        wait_after<NIC, NB - 1>(min(NB - 1, nchunks - 1 - c));
+        const lds_u8 *buf = ring + (c % NB) * CHUNK;
+        if ((c & 1) == 0) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                f32x16 z = {};
+                acc[hb] = z;
+            }
+            mfma_steps<R, HB, 0, KSH, CH>(buf, qr, acc);
+        } else {
+            mfma_steps<R, HB, KSH, KSH, CH>(buf, qr, acc);
+            const float p = epilogue<HB>(acc, qr.w);
+            const int64_t j = tile_row0(c >> 1) + lane;
+            if (lane < 32 && j < n) {
+                out[j] = p;
+                if (a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+            }
+        }
+    }
+    if (a.hist) {
+        __syncthreads();
+        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
     }
 }
 
@@ -264,11 +273,13 @@ template <int R, int HB, int NBUF>
 __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_per_split)
 {
     constexpr int TILE_BYTES = kTile * R * 2;
+    constexpr int CH = R / 8;
     constexpr int NI = R / 16;
     constexpr int NIW = NI / 4;
     static_assert(NIW >= 1, "tile must split over 4 waves");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[NBUF * TILE_BYTES];
-    lds_u8 *lds = (lds_u8 *)lds_raw;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * TILE_BYTES];
+    __shared__ uint32_t s_hist[4][kHistBins];
+    lds_u8 *ring = (lds_u8 *)ring_raw;
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -291,6 +302,8 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
             my_b = sb[u];
             my_n = sn[u];
         }
+    uint32_t *hist = s_hist[wv];
+    if (a.hist) hist_zero(hist, 64, lane);
     QueryRegs<R, HB> qr;
     if (q < a.Q) {
         qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
@@ -320,55 +333,77 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
         const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
         auto issue = [&](int i) {
             const int64_t t0 = (int64_t)(ts + i) * kTile;
-            const int page = bt[t0 >> 6];
-            issue_tile_contig<R>(pool + ((int64_t)page * kPage + (t0 & 63)) * R,
-                                 lds + (i % NBUF) * TILE_BYTES, wv, 4);
+            const int64_t base = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63)) * R;
+            issue_rows<R, CH, NIW>(pool, [&](int nr) { return base + (int64_t)nr * R; }, 0,
+                                   ring + (i % NBUF) * TILE_BYTES, wv * NIW, NIW);
         };
         for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i);
 #pragma unroll 1
         for (int i = 0; i < nt; ++i) {
             if (i + NBUF - 1 < nt) issue(i + NBUF - 1);
-            wait_after<NIW>(min(NBUF - 1, nt - 1 - i));
+            wait_after<NIW, NBUF - 1>(min(NBUF - 1, nt - 1 - i));
             wg_barrier();
             if (active) {
-                const float p = tile_score<R, HB>(lds + (i % NBUF) * TILE_BYTES, qr);
+                f32x16 acc[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    f32x16 z = {};
+                    acc[hb] = z;
+                }
+                mfma_steps<R, HB, 0, R / 16, CH>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
+                const float p = epilogue<HB>(acc, qr.w);
                 const int j = (ts + i) * kTile + lane;
-                if (lane < 32 && j < my_n) out[j] = p;
+                if (lane < 32 && j < my_n) {
+                    out[j] = p;
+                    if (a.hist) atomicAdd(&hist[score_key(p) >> kDigit0Shift], 1u);
+                }
             }
             wg_barrier();
         }
+    }
+    if (a.hist && q < a.Q) {
+        wait_lds();
+        hist_flush(hist, a.hist + (int64_t)q * kHistStride, 64, lane);
     }
 }
 
 // ---------------------------------------------------------------------------
 // fp32 latent (any r <= 256): plain VALU dot products, one row per thread.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R)
+__global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_per_wg)
 {
     __shared__ float sq[64 * 256];
     __shared__ float sw[64];
+    __shared__ uint32_t s_hist[kHistBins];
     const int q = blockIdx.y;
     const int b = a.qseq[q];
     int n = a.cand ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
-    const int64_t row0 = (int64_t)blockIdx.x * 256;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     if (row0 >= n) return;
+    const int64_t row1 = min64(row0 + rows_per_wg, n);
     const float *qt = (const float *)a.qt + (int64_t)q * a.H * R;
     for (int i = threadIdx.x; i < a.H * R; i += 256) sq[i] = qt[i];
     for (int i = threadIdx.x; i < a.H; i += 256) sw[i] = a.w[(int64_t)q * a.H + i];
+    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     __syncthreads();
-    const int64_t j = row0 + threadIdx.x;
-    if (j >= n) return;
-    const int pos = a.cand ? a.cand[(int64_t)q * a.cand_ld + j] : (int)j;
-    const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
-    const float *row = (const float *)a.pool + ((int64_t)page * kPage + (pos & 63)) * R;
-    float s = 0.0f;
-    for (int h = 0; h < a.H; ++h) {
-        float dot = 0.0f;
-        for (int t = 0; t < R; ++t) dot = fmaf(sq[h * R + t], row[t], dot);
-        s = fmaf(sw[h], fmaxf(dot, 0.0f), s);
+    for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
+        const int pos = a.cand ? a.cand[(int64_t)q * a.cand_ld + j] : (int)j;
+        const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
+        const float *row = (const float *)a.pool + ((int64_t)page * kPage + (pos & 63)) * R;
+        float sc = 0.0f;
+        for (int h = 0; h < a.H; ++h) {
+            float dot = 0.0f;
+            for (int t = 0; t < R; ++t) dot = fmaf(sq[h * R + t], row[t], dot);
+            sc = fmaf(sw[h], fmaxf(dot, 0.0f), sc);
+        }
+        a.out[(int64_t)q * a.out_ld + j] = sc;
+        if (a.hist) atomicAdd(&s_hist[score_key(sc) >> kDigit0Shift], 1u);
     }
-    a.out[(int64_t)q * a.out_ld + j] = s;
+    if (a.hist) {
+        __syncthreads();
+        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
+    }
 }
 
 template <int R, int HB>
@@ -386,18 +421,19 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
         hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF>), dim3(qblocks, splits), dim3(256), 0, s, a, tps);
         return hipGetLastError();
     }
-    // decode: aim for ~2 rounds of one workgroup per CU
-    const int64_t want_wgs = 512;
-    int64_t per_q = (want_wgs + a.Q - 1) / a.Q;
+    // decode: about one round of one workgroup per CU
+    const int64_t want_wgs = 256;
+    const int64_t per_q = (want_wgs + a.Q - 1) / a.Q;
     int64_t tpw = (tiles + 4 * per_q - 1) / (4 * per_q);
     if (tpw < 1) tpw = 1;
-    if (tpw > 64) tpw = 64;
     if (a.cand && tpw > kGatherTiles) tpw = kGatherTiles;
     const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    // chunk ring depth: as deep as LDS allows next to the histogram
+    constexpr int NB = R == 256 ? 4 : 8;
     if (a.cand)
-        hipLaunchKernelGGL((k_score_decode<R, HB, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
     else
-        hipLaunchKernelGGL((k_score_decode<R, HB, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
     return hipGetLastError();
 }
 
@@ -416,8 +452,10 @@ hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_
     if (a.Q <= 0 || max_rows <= 0) return hipSuccess;
     const bool prefill = many_queries_per_seq && a.cand == nullptr;
     if (!bf16) {
-        const int64_t wgs = (max_rows + 255) / 256;
-        hipLaunchKernelGGL(k_score_f32, dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, r);
+        const int64_t wgs = std::min<int64_t>((max_rows + 255) / 256, 1024);
+        const int64_t per = ((max_rows + wgs - 1) / wgs + 255) / 256 * 256;
+        hipLaunchKernelGGL(k_score_f32, dim3((unsigned)((max_rows + per - 1) / per), a.Q), dim3(256), 0, s, a, r,
+                           (int)per);
         return hipGetLastError();
     }
     switch (r) {

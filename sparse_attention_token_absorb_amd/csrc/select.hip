@@ -5,16 +5,21 @@
 // (§C.4); the HS anchor picks its top-M candidates and its own top-k inside
 // them (§3.2, §C.4).
 //
-// Scores become order-preserving uint32 keys and are selected by radix
-// digits of 11, 11 and 10 bits (most significant first), on LDS histograms.
-//   * Long rows (decode at 8K-128K): the first digit's histogram is built by
-//     many workgroups per query (global atomics on 2048 bins); a filter pass
-//     then writes every row whose first digit beats the threshold digit
-//     straight to the output and compacts the rows that tie on it into a
-//     candidate list; one workgroup per query resolves the last two digits
-//     among the candidates in LDS.
-//   * Short rows (HS followers, nested anchor selection, <= 16384): one
-//     workgroup per query holds all keys in LDS and runs all three digits.
+// Scores become order-preserving uint32 keys, selected by radix digits of
+// 12, 11 and 9 bits (most significant first).  The scoring kernels already
+// count the first digit (key >> 20) into a per-query 4096-bin histogram as
+// they write the scores, so the threshold bin is known before the rows are
+// read again.  One pass over each row then emits the rows above the
+// threshold digit and compacts the rows on it; the last two digits are
+// resolved among those few in LDS.
+//   * Few queries with long rows (decode at 8K-128K): the pass is spread
+//     over many workgroups per query (k_filter), and one workgroup per
+//     query finishes (k_final).
+//   * Many queries or short rows (prefill, HS followers, the anchor's nested
+//     selection): one 1024-thread workgroup per query does it all (k_select).
+// Rows are read 16 bytes per lane, several loads in flight per thread (the
+// scores were written by other XCDs, so every load misses the local L2).
+// Emission uses wavefront ballots (one LDS atomic per wave, mbcnt offsets).
 // Rows whose key equals the final threshold key are taken in arbitrary
 // order, as many as the budget needs: equal scores are interchangeable.
 #include "li_internal.hpp"
@@ -24,7 +29,12 @@
 namespace li {
 namespace {
 
-constexpr int kCtr = 4; // per-query counters: 0 out, 1 cand
+constexpr int NT = kSelThreads;
+constexpr int kB = 4;              // 16-byte loads in flight per thread per round
+constexpr int kCandCap = 8192;     // tied rows kept in LDS
+constexpr int kKeyCache = 16384;   // rows cached in LDS when the histogram is built here
+constexpr int kFilterThreads = 256;
+constexpr int kFilterChunk = kFilterThreads * kB * 4; // rows per filter workgroup (4096)
 
 __device__ __forceinline__ uint32_t key_at(const SelRow &r, int q, int64_t i)
 {
@@ -32,39 +42,81 @@ __device__ __forceinline__ uint32_t key_at(const SelRow &r, int q, int64_t i)
     return score_key(r.S[(int64_t)q * r.ld + j]);
 }
 
+// Keys of rows i..i+3 (zero past n).
+__device__ __forceinline__ void keys4(const SelRow &r, int q, int64_t i, int64_t n, uint32_t (&k)[4])
+{
+    if (!r.gmap && (r.ld & 3) == 0 && i + 3 < n) {
+        const float4 v = *(const float4 *)(r.S + (int64_t)q * r.ld + i);
+        k[0] = score_key(v.x);
+        k[1] = score_key(v.y);
+        k[2] = score_key(v.z);
+        k[3] = score_key(v.w);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) k[t] = i + t < n ? key_at(r, q, i + t) : 0u;
+    }
+}
+
 __device__ __forceinline__ int32_t out_id(const SelRow &r, int q, int64_t i)
 {
     return r.omap ? r.omap[(int64_t)q * r.old + i] : (int32_t)i;
 }
 
-// Block-wide search on an LDS histogram: the bin b holding the `remaining`-th
-// largest element, and `above` = elements in bins > b.  Writes res[0] = b
-// (-1 if remaining exceeds the total), res[1] = above.  256 threads.
-__device__ void find_bin(const uint32_t *h, int nbins, uint32_t remaining, uint32_t *scan, int *res)
+__device__ __forceinline__ int query_n(const SelCall &c, int q)
 {
-    const int tid = threadIdx.x;
-    const int per = nbins / kBlock;
-    uint32_t sum = 0;
-    for (int j = 0; j < per; ++j) sum += h[tid * per + j];
-    if (tid == 0) res[0] = -1;
-    scan[tid] = sum;
-    __syncthreads();
-    // inclusive suffix sums: scan[t] = sum over threads >= t
-    for (int off = 1; off < kBlock; off <<= 1) {
-        const uint32_t v = tid + off < kBlock ? scan[tid + off] : 0u;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    int n;
+    if (c.src_mode == kSrcCausal) {
+        n = valid_rows(c.qpos[q], c.seq_lens[c.qseq[q]]);
+    } else {
+        n = c.cnt[q] < c.cnt_cap ? c.cnt[q] : c.cnt_cap;
+        n = n > 0 ? n : 0;
     }
-    const uint32_t incl = scan[tid];
+    return n < c.max_n ? n : (int)c.max_n; // the caller's bound sizes every buffer
+}
+
+__device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & 63)) - 1ull; }
+
+template <int T>
+struct Scratch {
+    uint32_t hist[2048];
+    uint32_t wtot[T / 64];
+    int res[2];
+    int cnt[4];
+};
+
+// Block-wide search on an LDS histogram of nbins bins: the bin b holding
+// the `remaining`-th largest element and `above` = elements in bins > b.
+// sh.res[0] = b (-1 if remaining exceeds the total), sh.res[1] = above.
+template <int T>
+__device__ void find_bin(const uint32_t *h, int nbins, uint32_t remaining, Scratch<T> &sh)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int per = (nbins + T - 1) / T;
+    uint32_t sum = 0;
+    for (int j = 0; j < per; ++j) {
+        const int bb = tid * per + j;
+        if (bb < nbins) sum += h[bb];
+    }
+    uint32_t suf = sum; // suffix sum within the wave: lanes >= lane
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_down(suf, off);
+        if (lane + off < 64) suf += v;
+    }
+    if (lane == 0) sh.wtot[wv] = suf;
+    if (tid == 0) sh.res[0] = -1;
+    __syncthreads();
+    uint32_t later = 0;
+    for (int w2 = wv + 1; w2 < T / 64; ++w2) later += sh.wtot[w2];
+    const uint32_t incl = suf + later;
     const uint32_t excl = incl - sum;
     if (excl < remaining && incl >= remaining) {
         uint32_t acc = excl;
         for (int j = per - 1; j >= 0; --j) {
             const int bb = tid * per + j;
+            if (bb >= nbins) continue;
             if (acc + h[bb] >= remaining) {
-                res[0] = bb;
-                res[1] = (int)acc;
+                sh.res[0] = bb;
+                sh.res[1] = (int)acc;
                 break;
             }
             acc += h[bb];
@@ -73,69 +125,73 @@ __device__ void find_bin(const uint32_t *h, int nbins, uint32_t remaining, uint3
     __syncthreads();
 }
 
-// Key/id sources for the in-block radix passes.
-struct LdsKeys { // keys in LDS, id = index
-    const uint32_t *k;
-    __device__ uint32_t key(int64_t i) const { return k[i]; }
-    __device__ int64_t id(int64_t i) const { return i; }
-};
-struct LdsPairs { // keys and ids in LDS
+// Lanes with e set append `val` at out[*cnt ...] (one LDS atomic per wave).
+// Whole waves must reach it.
+__device__ __forceinline__ void emit(bool e, int32_t val, int32_t *out, int *cnt)
+{
+    const uint64_t m = __ballot(e);
+    if (m == 0ull) return;
+    int base = 0;
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, __popcll(m));
+    base = __shfl(base, 0);
+    if (e) out[base + __popcll(m & lanes_below())] = val;
+}
+
+// Digits below the first: bits [19:9] then [8:0].
+__device__ __forceinline__ int lvl_shift(int l) { return l == 1 ? 9 : 0; }
+__device__ __forceinline__ int lvl_bins(int l) { return l == 1 ? 2048 : 512; }
+
+// Element sources for the in-block levels: key(i), id(i).
+struct CandLds {
     const uint32_t *k;
     const int32_t *d;
-    __device__ uint32_t key(int64_t i) const { return k[i]; }
-    __device__ int64_t id(int64_t i) const { return d[i]; }
+    __device__ uint32_t key(int i) const { return k[i]; }
+    __device__ int64_t id(int i) const { return d[i]; }
 };
-struct GlobalPairs { // candidate list in global memory
-    const uint2 *p;
-    __device__ uint32_t key(int64_t i) const { return p[i].x; }
-    __device__ int64_t id(int64_t i) const { return (int32_t)p[i].y; }
+struct CacheLds {
+    const uint32_t *k;
+    __device__ uint32_t key(int i) const { return k[i]; }
+    __device__ int64_t id(int i) const { return i; }
 };
-struct RowKeys { // the query's whole score row
+struct RowGlobal {
     SelRow r;
     int q;
-    __device__ uint32_t key(int64_t i) const { return key_at(r, q, i); }
-    __device__ int64_t id(int64_t i) const { return i; }
+    __device__ uint32_t key(int i) const { return key_at(r, q, i); }
+    __device__ int64_t id(int i) const { return i; }
 };
 
-struct BlockScratch {
-    uint32_t hist[kBins0];
-    uint32_t scan[kBlock];
-    int res[2];
-    int cnt[2];
-};
-
-// Radix levels `level`..2 over m elements of `src` restricted to keys with
-// (key & pmask) == prefix; emits the `remaining` best of them into
-// out[out_base ...] (ids mapped through the row's omap).
-template <class Src>
-__device__ void radix_levels(const Src &src, int64_t m, int level, uint32_t prefix, uint32_t pmask,
-                             uint32_t remaining, int32_t *out, int out_base, const SelRow &row, int q,
-                             BlockScratch &sh)
+// Levels 1 and 2 over m elements restricted to (key & pmask) == prefix;
+// emits the `remaining` best of them at out[sh.cnt[0] ...].  All threads.
+template <int T, class Src>
+__device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
+                              int32_t *out, const SelRow &row, int q, Scratch<T> &sh)
 {
-    const int tid = threadIdx.x;
-    if (tid == 0) sh.cnt[0] = out_base;
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wbase = tid - lane;
+    int level = 1;
     for (; level < 3 && remaining > 0; ++level) {
-        const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-        const int nb = level == 2 ? 1024 : 2048;
+        const int shift = lvl_shift(level);
+        const int nb = lvl_bins(level);
         const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int j = tid; j < nb; j += kBlock) sh.hist[j] = 0;
+        for (int j = tid; j < nb; j += T) sh.hist[j] = 0;
         __syncthreads();
-        for (int64_t i = tid; i < m; i += kBlock) {
+        for (int i = tid; i < m; i += T) {
             const uint32_t key = src.key(i);
             if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
         }
         __syncthreads();
-        find_bin(sh.hist, nb, remaining, sh.scan, sh.res);
+        find_bin<T>(sh.hist, nb, remaining, sh);
         const int bin = sh.res[0];
         const uint32_t above = (uint32_t)sh.res[1];
         if (bin < 0) break; // inconsistent counts: nothing sensible to emit
-        for (int64_t i = tid; i < m; i += kBlock) {
-            const uint32_t key = src.key(i);
-            if ((key & pmask) == prefix && ((key >> shift) & dmask) > (uint32_t)bin) {
-                const int o = atomicAdd(&sh.cnt[0], 1);
-                out[o] = out_id(row, q, src.id(i));
+        for (int i0 = wbase; i0 < m; i0 += T) {
+            const int i = i0 + lane;
+            bool e = false;
+            if (i < m) {
+                const uint32_t key = src.key(i);
+                e = (key & pmask) == prefix && ((key >> shift) & dmask) > (uint32_t)bin;
             }
+            emit(e, e ? out_id(row, q, src.id(i)) : 0, out, &sh.cnt[0]);
         }
         remaining -= above;
         prefix |= (uint32_t)bin << shift;
@@ -143,240 +199,312 @@ __device__ void radix_levels(const Src &src, int64_t m, int level, uint32_t pref
         __syncthreads();
     }
     if (remaining > 0 && level == 3) {
-        if (tid == 0) sh.cnt[1] = 0;
+        // all 32 bits resolved: the survivors share one key
+        if (tid == 0) sh.cnt[2] = 0;
         __syncthreads();
-        for (int64_t i = tid; i < m; i += kBlock) {
-            const uint32_t key = src.key(i);
-            if (key == prefix) {
-                const int slot = atomicAdd(&sh.cnt[1], 1);
-                if ((uint32_t)slot < remaining) {
-                    const int o = atomicAdd(&sh.cnt[0], 1);
-                    out[o] = out_id(row, q, src.id(i));
+        for (int i0 = wbase; i0 < m; i0 += T) {
+            const int i = i0 + lane;
+            const bool tie = i < m && src.key(i) == prefix;
+            const uint64_t tm = __ballot(tie);
+            if (tm == 0ull) continue;
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&sh.cnt[2], __popcll(tm));
+            base = __shfl(base, 0);
+            const bool take = tie && (uint32_t)(base + __popcll(tm & lanes_below())) < remaining;
+            emit(take, take ? out_id(row, q, src.id(i)) : 0, out, &sh.cnt[0]);
+        }
+    }
+    __syncthreads();
+}
+
+// Threshold bin of the first digit from the query's global histogram.
+template <int T>
+__device__ void threshold_from_hist(const int32_t *g, uint32_t *h0, int K, Scratch<T> &sh)
+{
+    constexpr int PER = kHistBins / T;
+    uint32_t v[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = (uint32_t)g[e * T + threadIdx.x];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) h0[e * T + threadIdx.x] = v[e];
+    __syncthreads();
+    find_bin<T>(h0, kHistBins, (uint32_t)K, sh);
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per query.  HIST: the scoring kernel counted the first digit
+// into the global histogram; otherwise it is counted here (rows cached in
+// LDS when they fit).
+// ---------------------------------------------------------------------------
+template <bool HIST>
+__global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
+{
+    __shared__ Scratch<NT> sh;
+    __shared__ uint32_t h0[kHistBins];
+    __shared__ uint32_t ck[kCandCap];
+    __shared__ int32_t ci[kCandCap];
+    __shared__ uint32_t cache[HIST ? 1 : kKeyCache];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int q = blockIdx.x;
+    const int n = query_n(c, q);
+    const int K = min(n, c.k);
+    int32_t *out = c.idx + (int64_t)q * c.k;
+    const bool cached = !HIST && n <= kKeyCache;
+    constexpr int64_t ROUND = (int64_t)NT * kB * 4;
+    if (K > 0) {
+        if (tid == 0) {
+            sh.cnt[0] = 0;
+            sh.cnt[1] = 0;
+        }
+        if constexpr (HIST) {
+            threshold_from_hist<NT>(ws.hist + (int64_t)q * kHistStride, h0, K, sh);
+        } else {
+            for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
+            __syncthreads();
+            for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
+                uint32_t kk[kB][4];
+#pragma unroll
+                for (int b = 0; b < kB; ++b) keys4(c.row, q, r0 + 4 * ((int64_t)b * NT + tid), n, kk[b]);
+#pragma unroll
+                for (int b = 0; b < kB; ++b)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
+                        if (i < n) {
+                            atomicAdd(&h0[kk[b][t] >> kDigit0Shift], 1u);
+                            if (cached) cache[i] = kk[b][t];
+                        }
+                    }
+            }
+            __syncthreads();
+            find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+        }
+        const int bin = sh.res[0];
+        const int above = sh.res[1];
+        if (bin >= 0) {
+            // one pass over the row: emit above, keep ties
+            for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
+                uint32_t kk[kB][4];
+#pragma unroll
+                for (int b = 0; b < kB; ++b) {
+                    const int64_t i = r0 + 4 * ((int64_t)b * NT + tid);
+                    if (cached) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) kk[b][t] = i + t < n ? cache[i + t] : 0u;
+                    } else {
+                        keys4(c.row, q, i, n, kk[b]);
+                    }
                 }
+#pragma unroll
+                for (int b = 0; b < kB; ++b)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
+                        const int dg = (int)(kk[b][t] >> kDigit0Shift);
+                        const bool ok = i < n;
+                        const bool up = ok && dg > bin;
+                        emit(up, up ? out_id(c.row, q, i) : 0, out, &sh.cnt[0]);
+                        const bool tie = ok && dg == bin;
+                        const uint64_t tm = __ballot(tie);
+                        if (tm) {
+                            int base = 0;
+                            if (lane == 0) base = atomicAdd(&sh.cnt[1], __popcll(tm));
+                            base = __shfl(base, 0);
+                            const int slot = base + __popcll(tm & lanes_below());
+                            if (tie && slot < kCandCap) {
+                                ck[slot] = kk[b][t];
+                                ci[slot] = (int32_t)i;
+                            }
+                        }
+                    }
+            }
+            __syncthreads();
+            const int nc = sh.cnt[1];
+            const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
+            const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
+            const uint32_t need = (uint32_t)(K - above);
+            if (nc <= kCandCap) {
+                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, c.row, q, sh);
+            } else if (cached) {
+                finish_levels<NT>(CacheLds{cache}, n, prefix, pmask, need, out, c.row, q, sh);
+            } else {
+                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, c.row, q, sh);
             }
         }
     }
-    __syncthreads();
+    for (int i = K + tid; i < c.k; i += NT) out[i] = -1;
+    if (tid == 0) c.count[q] = K;
 }
 
-__device__ __forceinline__ void pad_and_count(int32_t *out, int K, int k, int32_t *count, int q)
+// ---------------------------------------------------------------------------
+// Few queries, long rows: many workgroups per query stream the row once.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspace ws)
 {
-    for (int i = K + threadIdx.x; i < k; i += kBlock) out[i] = -1;
-    if (threadIdx.x == 0) count[q] = K;
-}
-
-// n, K per query; zero counters and histograms.
-__global__ __launch_bounds__(256) void k_sel_prep(SelCall c, SelWorkspace ws)
-{
-    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t words = (int64_t)c.Q * (kCtr + kBins0);
-    for (int64_t i = tid; i < words; i += (int64_t)gridDim.x * kBlock) ws.ctr[i] = 0; // ctr then hist
-    if (tid < c.Q) {
-        const int q = (int)tid;
-        int n;
-        if (c.src_mode == kSrcCausal) {
-            n = valid_rows(c.qpos[q], c.seq_lens[c.qseq[q]]);
-        } else {
-            n = c.cnt[q] < c.cnt_cap ? c.cnt[q] : c.cnt_cap;
-            n = n > 0 ? n : 0;
-        }
-        if (n > c.max_n) n = (int)c.max_n; // the caller's bound sizes every buffer
-        ws.nvalid[q] = n;
-        ws.kq[q] = n < c.k ? n : c.k;
-    }
-}
-
-// First-digit histogram, many workgroups per query.
-__global__ __launch_bounds__(256) void k_sel_hist(SelCall c, SelWorkspace ws, int chunk)
-{
-    __shared__ uint32_t h[kBins0];
-    const int q = blockIdx.y;
-    const int n = ws.nvalid[q];
-    const int64_t i0 = (int64_t)blockIdx.x * chunk;
-    if (i0 >= n || ws.kq[q] == 0) return;
-    for (int j = threadIdx.x; j < kBins0; j += kBlock) h[j] = 0;
-    __syncthreads();
-    const int64_t i1 = std::min<int64_t>(i0 + chunk, n);
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) atomicAdd(&h[key_at(c.row, q, i) >> kDigit0Shift], 1u);
-    __syncthreads();
-    uint32_t *g = ws.hist + (int64_t)q * kBins0;
-    for (int j = threadIdx.x; j < kBins0; j += kBlock)
-        if (h[j]) atomicAdd(&g[j], h[j]);
-}
-
-// Rows above the threshold digit go to the output; rows on it to the
-// candidate list.
-template <int EPT>
-__global__ __launch_bounds__(256) void k_sel_filter(SelCall c, SelWorkspace ws)
-{
-    __shared__ BlockScratch sh;
+    constexpr int T = kFilterThreads;
+    __shared__ Scratch<T> sh;
+    __shared__ uint32_t h0[kHistBins];
     __shared__ int s_base[4];
+    const int tid = threadIdx.x;
     const int q = blockIdx.y;
-    const int n = ws.nvalid[q];
-    const int K = ws.kq[q];
-    const int64_t i0 = (int64_t)blockIdx.x * (EPT * kBlock);
-    if (i0 >= n || K == 0) return;
-    const uint32_t *g = ws.hist + (int64_t)q * kBins0;
-    for (int j = threadIdx.x; j < kBins0; j += kBlock) sh.hist[j] = g[j];
-    if (threadIdx.x < 4) s_base[threadIdx.x] = 0;
-    __syncthreads();
-    find_bin(sh.hist, kBins0, (uint32_t)K, sh.scan, sh.res);
+    const int n = query_n(c, q);
+    const int K = min(n, c.k);
+    const int64_t i0 = (int64_t)blockIdx.x * kFilterChunk;
+    if (K == 0 || i0 >= n) return;
+    int32_t *hist = ws.hist + (int64_t)q * kHistStride;
+    threshold_from_hist<T>(hist, h0, K, sh);
     const int bin = sh.res[0];
     if (bin < 0) return;
-    uint32_t keys[EPT];
-    int nout = 0, ncand = 0;
+    if (tid < 4) s_base[tid] = 0;
+    uint32_t kk[kB][4];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int64_t i = i0 + (int64_t)e * kBlock + threadIdx.x;
-        keys[e] = i < n ? key_at(c.row, q, i) : 0u;
-        const int dg = (int)(keys[e] >> kDigit0Shift);
-        if (i < n) {
-            nout += dg > bin;
-            ncand += dg == bin;
+    for (int b = 0; b < kB; ++b) keys4(c.row, q, i0 + 4 * ((int64_t)b * T + tid), n, kk[b]);
+    int nup = 0, ntie = 0;
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t i = i0 + 4 * ((int64_t)b * T + tid) + t;
+            const int dg = (int)(kk[b][t] >> kDigit0Shift);
+            if (i < n) {
+                nup += dg > bin;
+                ntie += dg == bin;
+            }
         }
-    }
-    const int lo = nout ? atomicAdd(&s_base[0], nout) : 0;
-    const int lc = ncand ? atomicAdd(&s_base[1], ncand) : 0;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        s_base[2] = s_base[0] ? atomicAdd(&ws.ctr[q * kCtr + 0], s_base[0]) : 0;
-        s_base[3] = s_base[1] ? atomicAdd(&ws.ctr[q * kCtr + 1], s_base[1]) : 0;
+    const int lu = nup ? atomicAdd(&s_base[0], nup) : 0;
+    const int lt = ntie ? atomicAdd(&s_base[1], ntie) : 0;
+    __syncthreads();
+    if (tid == 0) {
+        s_base[2] = s_base[0] ? atomicAdd(&hist[kHistBins + 0], s_base[0]) : 0;
+        s_base[3] = s_base[1] ? atomicAdd(&hist[kHistBins + 1], s_base[1]) : 0;
     }
     __syncthreads();
-    int po = s_base[2] + lo, pc = s_base[3] + lc;
+    int pu = s_base[2] + lu, pt = s_base[3] + lt;
     int32_t *out = c.idx + (int64_t)q * c.k;
     uint2 *cand = ws.cand + (int64_t)q * ws.cap;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int64_t i = i0 + (int64_t)e * kBlock + threadIdx.x;
-        if (i < n) {
-            const int dg = (int)(keys[e] >> kDigit0Shift);
-            if (dg > bin) {
-                out[po++] = out_id(c.row, q, i);
-            } else if (dg == bin) {
-                if (pc < ws.cap) cand[pc] = make_uint2(keys[e], (uint32_t)i);
-                ++pc;
+    for (int b = 0; b < kB; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t i = i0 + 4 * ((int64_t)b * T + tid) + t;
+            if (i < n) {
+                const int dg = (int)(kk[b][t] >> kDigit0Shift);
+                if (dg > bin) {
+                    out[pu++] = out_id(c.row, q, i);
+                } else if (dg == bin) {
+                    if (pt < ws.cap) cand[pt] = make_uint2(kk[b][t], (uint32_t)i);
+                    ++pt;
+                }
             }
         }
-    }
 }
 
-// Last two digits among the candidates, one workgroup per query.
-__global__ __launch_bounds__(256) void k_sel_final(SelCall c, SelWorkspace ws)
+// The remaining digits among the tied rows, one workgroup per query.
+__global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
 {
-    __shared__ BlockScratch sh;
-    __shared__ uint32_t sk[kFinalLdsCap];
-    __shared__ int32_t sd[kFinalLdsCap];
+    __shared__ Scratch<NT> sh;
+    __shared__ uint32_t h0[kHistBins];
+    __shared__ uint32_t ck[kCandCap];
+    __shared__ int32_t ci[kCandCap];
+    const int tid = threadIdx.x;
     const int q = blockIdx.x;
-    const int K = ws.kq[q];
+    const int n = query_n(c, q);
+    const int K = min(n, c.k);
     int32_t *out = c.idx + (int64_t)q * c.k;
     if (K > 0) {
-        const uint32_t *g = ws.hist + (int64_t)q * kBins0;
-        for (int j = threadIdx.x; j < kBins0; j += kBlock) sh.hist[j] = g[j];
-        __syncthreads();
-        find_bin(sh.hist, kBins0, (uint32_t)K, sh.scan, sh.res);
+        const int32_t *hist = ws.hist + (int64_t)q * kHistStride;
+        threshold_from_hist<NT>(hist, h0, K, sh);
         const int bin = sh.res[0];
         const int above = sh.res[1];
-        __syncthreads();
         if (bin >= 0) {
-            const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
-            const uint32_t pmask = 0xFFE00000u;
-            const uint32_t need = (uint32_t)(K - above);
-            const int64_t nc = ws.ctr[q * kCtr + 1];
+            const int nc = hist[kHistBins + 1];
             const uint2 *cand = ws.cand + (int64_t)q * ws.cap;
-            // The list holds min(nc, cap) entries: use it only when complete.
-            if (nc <= ws.cap && nc <= kFinalLdsCap) {
-                for (int64_t i = threadIdx.x; i < nc; i += kBlock) {
-                    const uint2 p = cand[i];
-                    sk[i] = p.x;
-                    sd[i] = (int32_t)p.y;
+            if (tid == 0) sh.cnt[0] = above;
+            const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
+            const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
+            const uint32_t need = (uint32_t)(K - above);
+            if (nc <= kCandCap && nc <= ws.cap) {
+                for (int i0 = 0; i0 < nc; i0 += NT * 4) {
+                    uint2 p[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = i0 + e * NT + tid;
+                        p[e] = i < nc ? cand[i] : make_uint2(0u, 0u);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = i0 + e * NT + tid;
+                        if (i < nc) {
+                            ck[i] = p[e].x;
+                            ci[i] = (int32_t)p[e].y;
+                        }
+                    }
                 }
                 __syncthreads();
-                radix_levels(LdsPairs{sk, sd}, nc, 1, prefix, pmask, need, out, above, c.row, q, sh);
-            } else if (nc <= ws.cap) {
-                radix_levels(GlobalPairs{cand}, nc, 1, prefix, pmask, need, out, above, c.row, q, sh);
+                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, c.row, q, sh);
             } else {
-                radix_levels(RowKeys{c.row, q}, ws.nvalid[q], 1, prefix, pmask, need, out, above, c.row, q, sh);
+                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, c.row, q, sh);
             }
         }
     }
-    pad_and_count(out, K, c.k, c.count, q);
+    for (int i = K + tid; i < c.k; i += NT) out[i] = -1;
+    if (tid == 0) c.count[q] = K;
 }
 
-// Whole selection in one workgroup per query (n <= kSmallCap).
-__global__ __launch_bounds__(256) void k_sel_small(SelCall c, SelWorkspace ws)
+// Clears the per-query histograms and counters before a scoring kernel
+// accumulates into them.
+__global__ __launch_bounds__(256) void k_hist_clear(int32_t *hist, int64_t words)
 {
-    __shared__ BlockScratch sh;
-    __shared__ uint32_t sk[kSmallCap];
-    const int q = blockIdx.x;
-    const int n = ws.nvalid[q];
-    const int K = ws.kq[q];
-    int32_t *out = c.idx + (int64_t)q * c.k;
-    if (K > 0) {
-        for (int64_t i = threadIdx.x; i < n; i += kBlock) sk[i] = key_at(c.row, q, i);
-        __syncthreads();
-        radix_levels(LdsKeys{sk}, n, 0, 0u, 0u, (uint32_t)K, out, 0, c.row, q, sh);
-    }
-    pad_and_count(out, K, c.k, c.count, q);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) hist[i] = 0;
 }
+
+bool use_filter(int64_t Q, int64_t max_n) { return max_n > kKeyCache && Q <= 64; }
+
+int64_t cand_cap(int64_t Q, int64_t max_n) { return use_filter(Q, max_n) ? std::min<int64_t>(max_n, 65536) : 0; }
 
 } // namespace
 
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n)
 {
-    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(max_n, Q <= 64 ? 65536 : 8192));
-    size_t b = 0;
-    b += (size_t)Q * 4 * 2;                         // nvalid, kq
+    size_t b = (size_t)Q * kHistStride * 4;
     b = (b + 255) & ~(size_t)255;
-    b += (size_t)Q * (kCtr + kBins0) * 4;           // ctr + hist
-    b = (b + 255) & ~(size_t)255;
-    b += (size_t)Q * cap * 8;                       // candidates
-    return b;
+    return b + (size_t)Q * cand_cap(Q, max_n) * 8;
 }
 
 SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n)
 {
-    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(max_n, Q <= 64 ? 65536 : 8192));
-    uint8_t *p = (uint8_t *)base;
     SelWorkspace w;
-    w.nvalid = (int32_t *)p;
-    w.kq = w.nvalid + Q;
-    size_t off = ((size_t)Q * 8 + 255) & ~(size_t)255;
-    w.ctr = (int32_t *)(p + off);
-    w.hist = (uint32_t *)(w.ctr + Q * kCtr);
-    off += (size_t)Q * (kCtr + kBins0) * 4;
-    off = (off + 255) & ~(size_t)255;
-    w.cand = (uint2 *)(p + off);
-    w.cap = cap;
+    w.hist = (int32_t *)base;
+    size_t off = ((size_t)Q * kHistStride * 4 + 255) & ~(size_t)255;
+    w.cand = (uint2 *)((uint8_t *)base + off);
+    w.cap = cand_cap(Q, max_n);
     return w;
 }
 
-hipError_t launch_sel_prep(const SelCall &c, const SelWorkspace &ws, hipStream_t s)
+hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s)
 {
-    const int64_t words = (int64_t)c.Q * (kCtr + kBins0);
-    int64_t blocks = std::max<int64_t>((words + kBlock - 1) / kBlock, (c.Q + kBlock - 1) / kBlock);
-    blocks = std::min<int64_t>(blocks, 4096);
-    hipLaunchKernelGGL(k_sel_prep, dim3((unsigned)blocks), dim3(kBlock), 0, s, c, ws);
+    const int64_t words = Q * kHistStride;
+    const int64_t blocks = std::min<int64_t>((words + 255) / 256, 2048);
+    hipLaunchKernelGGL(k_hist_clear, dim3((unsigned)blocks), dim3(256), 0, s, ws.hist, words);
     return hipGetLastError();
 }
 
-hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, hipStream_t s)
+hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s)
 {
     if (c.Q <= 0) return hipSuccess;
-    if (c.max_n <= kSmallCap) {
-        hipLaunchKernelGGL(k_sel_small, dim3(c.Q), dim3(kBlock), 0, s, c, ws);
+    if (have_hist && use_filter(c.Q, c.max_n)) {
+        const int64_t chunks = (c.max_n + kFilterChunk - 1) / kFilterChunk;
+        hipLaunchKernelGGL(k_filter, dim3((unsigned)chunks, c.Q), dim3(kFilterThreads), 0, s, c, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_final, dim3(c.Q), dim3(NT), 0, s, c, ws);
         return hipGetLastError();
     }
-    constexpr int EPT = 16;
-    const int chunk = EPT * kBlock;
-    const int64_t chunks = (c.max_n + chunk - 1) / chunk;
-    hipLaunchKernelGGL(k_sel_hist, dim3((unsigned)chunks, c.Q), dim3(kBlock), 0, s, c, ws, chunk);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sel_filter<EPT>, dim3((unsigned)chunks, c.Q), dim3(kBlock), 0, s, c, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sel_final, dim3(c.Q), dim3(kBlock), 0, s, c, ws);
+    if (have_hist)
+        hipLaunchKernelGGL(k_select<true>, dim3(c.Q), dim3(NT), 0, s, c, ws);
+    else
+        hipLaunchKernelGGL(k_select<false>, dim3(c.Q), dim3(NT), 0, s, c, ws);
     return hipGetLastError();
 }
 

@@ -347,3 +347,19 @@ def test_repeat_calls_are_deterministic_in_sets():
     r2 = h.full_layer(g, cache, qs, 0)
     assert np.array_equal(h.host(r1.scores), h.host(r2.scores))
     assert set(h.host(r1.idx)[0].tolist()) == set(h.host(r2.idx)[0].tolist())
+
+
+def test_long_rows_with_massive_ties():
+    """Few queries, long rows, and a threshold digit shared by ~40K rows:
+    the tie list overflows LDS and the final pass re-reads the row."""
+    h = H()
+    say("long rows + massive ties")
+    g = synth.make_decode("bigties", 56, B=2, lens=[40000, 30000], r=128, H=16, d=64, k=2048, M=8192)
+    g.latent[0][:39000] = 0.0
+    g.latent[1][:] = g.latent[1][7]
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    for l in (0, 1):
+        verify_full(g, l, h.full_layer(g, cache, qs, l), tag="bigties")
+    anchor, followers = h.hs_group(g, cache, qs)
+    verify_hs(g, anchor, followers, tag="bigties")
