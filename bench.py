@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--counters", action="store_true",
+                    help="hardware-counter pass: a few eager full-LatentIndex layers, then a plain 1 GiB copy "
+                         "whose counter readings scale the others to bytes; prints no JSON line")
     return ap.parse_args()
 
 
@@ -146,6 +149,18 @@ def main() -> int:
         mode_a()
 
     stream = torch.cuda.Stream(device=dev)
+
+    if args.counters:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            mode_b()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"counter pass done: 3 x {G} full-LatentIndex layers, 3 x copy of {src.numel() * 4} bytes")
+        return 0
 
     def capture(fn):
         with torch.cuda.stream(stream):

@@ -57,6 +57,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(N), other counters untouched.
+template <int N>
+struct VmcntImm {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    static constexpr int value = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+};
+
+// Wait for vector-memory operations through the compiler's own waitcnt
+// model (it then knows the wait happened), not through inline asm.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_known()
+{
+    __builtin_amdgcn_s_waitcnt(VmcntImm<N>::value);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 // The memory clobber keeps the compiler from moving LDS reads above it.
 template <int N>

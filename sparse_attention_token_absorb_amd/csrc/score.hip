@@ -20,18 +20,25 @@
 // follows starts from a known threshold bin.
 #include "li_internal.hpp"
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <algorithm>
 
 namespace li {
 namespace {
 
 constexpr int kGatherTiles = 16; // max tiles per wave in gather mode (row offsets kept in LDS)
+constexpr int kVrMaxTiles = 32;  // max tiles per wave of the register-staged decode kernel
 
 // LDS-typed pointers keep every access a ds_* instruction (a generic pointer
 // would become a flat access that also waits on global memory).
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef const __attribute__((address_space(3))) float lds_f32;
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
 __device__ __forceinline__ void dma16(const void *g, lds_u8 *lds_uniform)
@@ -264,6 +271,185 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
 }
 
 // ---------------------------------------------------------------------------
+// Decode, register-staged variant: the MFMA B fragments are loaded straight
+// from HBM into VGPRs (lane l reads 16 bytes of tile row l % 32 per k-step),
+// DEPTH tiles deep per wave.  The VGPR file (512 KiB per CU) holds far more
+// bytes in flight than the 160 KiB of LDS, which is what an HBM-bound
+// stream needs; LDS keeps only the histogram (and the gather row table).
+// ---------------------------------------------------------------------------
+template <int R, int HB, bool GATHER, int DEPTH>
+__global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_per_wave)
+{
+    constexpr int KS = R / 16;
+    constexpr int QT_BYTES = HB * 32 * R * 2; // absorbed query, heads padded to the MFMA tile
+    __shared__ __attribute__((aligned(1024))) uint8_t s_qt_raw[QT_BYTES];
+    __shared__ int32_t s_row[GATHER ? 4 * kGatherTiles * kTile : 1];
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ float s_out[4][kVrMaxTiles * kTile]; // scores, written out after the stream
+    __shared__ float s_w[64];                       // head weights, zero past H
+
+    const int q = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b = a.qseq[q];
+    int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
+    n = (int)min64(n, a.max_rows);
+    const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
+    if (row0 >= n) return;
+    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
+    const int64_t first = row0 + (int64_t)wv * kTile;
+    int nt = 0;
+    if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
+
+    const u16 *pool = (const u16 *)a.pool;
+    const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
+    auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
+    const int nr = lane & 31;
+    if constexpr (GATHER) {
+        for (int i = 0; i < nt; ++i) {
+            int64_t j = tile_row0(i) + nr;
+            j = j < n ? j : n - 1;
+            const int pos = a.cand[(int64_t)q * a.cand_ld + j];
+            const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
+            if (lane < 32) s_row[(wv * kGatherTiles + i) * kTile + lane] = page * kPage + (pos & 63);
+        }
+        wait_lds();
+    }
+
+    // this lane's row of tile i (rows past n read row n-1), first element of its k-half
+    auto lane_ptr = [&](int i) -> const u16 * {
+        int64_t off;
+        if constexpr (GATHER) {
+            off = (int64_t)s_row[(wv * kGatherTiles + i) * kTile + nr] * R;
+        } else {
+            const int64_t t0 = tile_row0(i);
+            int64_t j = nr;
+            if (t0 + j >= n) j = n - 1 - t0; // stay inside the sequence's last page
+            off = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63) + j) * R;
+        }
+        return pool + off + (lane >> 5) * 8;
+    };
+    bf16x8 bf[DEPTH][KS];
+    auto load = [&](bf16x8(&dst)[KS], int i) {
+        const u16 *p = lane_ptr(i);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) dst[s] = *(const bf16x8 *)(p + s * 16);
+    };
+
+    // Prologue: this wave's quarter of the absorbed query and the head
+    // weights go HBM/L2 -> VGPR -> LDS (plain loads: an LDS DMA or a weight
+    // held in a VMEM-loaded register makes the compiler drain every load
+    // inside the stream loop), then the first DEPTH tiles are issued.  The
+    // loop is entered with exactly DEPTH tiles of loads pending, the same
+    // state its back edge carries, so every wait in it stays exact.
+    constexpr int QCH = (QT_BYTES / 1024 + 3) / 4; // 1 KiB pieces of the query per wave
+    u32x4 qv[QCH];
+    const int qbytes = a.H * R * 2;
+    {
+        const uint8_t *src = (const uint8_t *)((const u16 *)a.qt + (int64_t)q * a.H * R);
+#pragma unroll
+        for (int c = 0; c < QCH; ++c) {
+            int off = (c * 4 + wv) * 1024 + lane * 16;
+            off = off < qbytes ? off : qbytes - 16;
+            qv[c] = *(const u32x4 *)(src + off);
+        }
+    }
+    const float wv_lane = a.w[(int64_t)q * a.H + (lane < a.H ? lane : a.H - 1)];
+    if (nt > 0) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load(bf[d], d < nt ? d : nt - 1);
+    }
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+        const int off = (c * 4 + wv) * 1024 + lane * 16;
+        if (off < qbytes) *(lds_u32x4 *)((lds_u8 *)s_qt_raw + off) = qv[c];
+    }
+    if (wv == 0) s_w[lane] = lane < a.H ? wv_lane : 0.0f;
+    wg_barrier(); // every wave's part of the query is in LDS; histogram cleared
+    QueryRegs<R, HB> qr;
+    {
+        const int h = lane & 31;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                if (hb * 32 + h < a.H) {
+                    qr.a[hb][s] = *(lds_bf16x8 *)((lds_u8 *)s_qt_raw +
+                                                   ((hb * 32 + h) * R + s * 16 + (lane >> 5) * 8) * 2);
+                } else {
+                    bf16x8 z = {};
+                    qr.a[hb][s] = z;
+                }
+            }
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                qr.w[hb][r] = ((const lds_f32 *)s_w)[hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+    }
+
+    float *out = a.out + (int64_t)q * a.out_ld;
+    auto compute = [&](const bf16x8(&src)[KS]) {
+        f32x16 acc[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            f32x16 z = {};
+            acc[hb] = z;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][s], src[s], acc[hb], 0, 0, 0);
+        return epilogue<HB>(acc, qr.w);
+    };
+    // Scores wait in LDS until the stream is done: a global store among the
+    // loads would make every wait in the loop a full drain.
+    auto store = [&](float p, int i) {
+        const int64_t j = tile_row0(i) + nr;
+        if (lane < 32) {
+            s_out[wv][i * kTile + lane] = p;
+            if (j < n && a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+        }
+    };
+    if (nt > 0) {
+        int i0 = 0;
+        // Steady state: every slot is refilled right after use, unconditionally,
+        // so each wait is for exactly the oldest tile's loads.
+        for (; i0 + 2 * DEPTH <= nt; i0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const float p = compute(bf[d]);
+                load(bf[d], i0 + d + DEPTH);
+                store(p, i0 + d);
+            }
+        }
+        // Tail: the last (< 2 DEPTH) tiles.
+        for (; i0 < nt; i0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int i = i0 + d;
+                if (i < nt) {
+                    const float p = compute(bf[d]);
+                    if (i + DEPTH < nt) load(bf[d], i + DEPTH);
+                    store(p, i);
+                }
+            }
+        }
+    }
+    // this wave's scores: two tiles per store instruction
+    wait_lds();
+    for (int i = lane >> 5; i < nt; i += 2) {
+        const int64_t j = tile_row0(i) + nr;
+        if (j < n) out[j] = s_out[wv][i * kTile + nr];
+    }
+    if (a.hist) {
+        __syncthreads();
+        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Prefill: many queries per sequence.  Workgroup = 4 consecutive queries,
 // one per wave; the 4 waves share every latent tile (one DMA per tile,
 // split across the waves) through an NBUF-deep LDS ring.  Queries of a
@@ -406,6 +592,28 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     }
 }
 
+// Decode kernel choice.  Measured on MI355X: the register-staged kernel is
+// faster for r <= 128 over contiguous prefixes (its deeper in-flight window
+// matters most when each tile is small); the LDS ring is faster for r = 256
+// and for gathered rows.  LI_DECODE_PATH=lds|vgpr overrides (read once).
+int decode_path_override()
+{
+    static const int path = [] {
+        const char *e = getenv("LI_DECODE_PATH");
+        if (e && strcmp(e, "lds") == 0) return 0;
+        if (e && strcmp(e, "vgpr") == 0) return 1;
+        return -1;
+    }();
+    return path;
+}
+
+bool use_vgpr_decode(int r, bool gather)
+{
+    const int o = decode_path_override();
+    if (o >= 0) return o == 1;
+    return r <= 128 && !gather;
+}
+
 template <int R, int HB>
 hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStream_t s)
 {
@@ -427,7 +635,21 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     int64_t tpw = (tiles + 4 * per_q - 1) / (4 * per_q);
     if (tpw < 1) tpw = 1;
     if (a.cand && tpw > kGatherTiles) tpw = kGatherTiles;
-    const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    if (use_vgpr_decode(R, a.cand != nullptr)) {
+        constexpr int DEPTH = R == 256 ? 3 : (R == 128 ? 5 : 8);
+        if (tpw > kVrMaxTiles) {
+            tpw = kVrMaxTiles;
+            wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+        }
+        if (a.cand)
+            hipLaunchKernelGGL((k_score_decode_vr<R, HB, true, DEPTH>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                               (int)tpw);
+        else
+            hipLaunchKernelGGL((k_score_decode_vr<R, HB, false, DEPTH>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                               (int)tpw);
+        return hipGetLastError();
+    }
     // chunk ring depth: as deep as LDS allows next to the histogram
     constexpr int NB = R == 256 ? 4 : 8;
     if (a.cand)
