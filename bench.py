@@ -275,7 +275,9 @@ def main() -> int:
     f_bytes = Bn * min(M, N) * (bytes_row + 4) + Bn * bytes_query
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(os.path.join(ROOT, "profiles", "score_decode_r256_h64_b4_n131072.md"),
+                                    os.path.join(ROOT, "sparse_attention_token_absorb_amd", "csrc", "score.hip")),
         "kernel": f"k_score_decode<r={r},64 heads> (full LatentIndex, B={Bn}, N={N})",
         "avg_launch_us": round(score_ms * 1e3, 2), "launches": n_launch, "bytes_per_launch": bytes_launch,
         "cold_avg_launch_us": round(cold_ms * 1e3, 2),
@@ -315,10 +317,12 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
+        # the group's layers in turn until about 10 s of CPU work is done
         t0 = time.perf_counter()
         rows_done = 0
         layers_done = 0
-        for l in range(G):
+        while layers_done < 256:
+            l = layers_done % G
             oracle.full_layer(g.q[l], g.W[l], g.w[l], g.latent, g.qseq, g.qpos, g.lens, k)
             rows_done += Bn * N
             layers_done += 1
@@ -326,8 +330,9 @@ def main() -> int:
                 break
         el = time.perf_counter() - t0
         cpu = {"value": round(rows_done / el, 1), "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"full LatentIndex (mode b), {layers_done} layer(s) x {Bn} queries x {N} rows: absorb, "
-                         f"fp64 scoring and top-{k} sort; {el:.1f} s"}
+               "sample": f"full LatentIndex (mode b) at B={Bn}, N={N}: {layers_done} layer passes (the group's "
+                         f"{G} layers in turn) x {Bn} queries x {N} rows, each absorb + fp64 scoring + top-{k} "
+                         f"sort; {el:.1f} s on {cpu_model()}"}
         log(f"cpu baseline {cpu}")
 
     # ------------------------------------------------------------------
@@ -384,6 +389,38 @@ def main() -> int:
         with open(args.out, "w") as f:
             f.write(s + "\n")
     return 0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def measured_traffic(path: str, source: str):
+    """HBM bytes per launch of the decode scoring kernel, from a committed
+    counter summary, or None when that summary was taken on other kernel
+    source (its recorded sha256 no longer matches) or is absent."""
+    import hashlib
+    try:
+        with open(source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    key, val = line[2:].split(": ", 1)
+                    fields[key.strip()] = val.strip().strip("`")
+        if fields.get("source_sha256") != sha:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def make_cache_from(g, B, tdev, i32, bf, dev):
