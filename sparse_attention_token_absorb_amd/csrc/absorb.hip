@@ -8,51 +8,72 @@
 // single round-to-nearest-even to bf16 at the end.
 //
 // Both MFMA operands want K-contiguous fragments; q rows already are, W_dec is
-// not, so every workgroup stages W_dec transposed in LDS (row stride d + 8
-// halves keeps the fragment reads conflict-free) and reuses it for 128 rows.
+// not, so every workgroup stages its column slice of W_dec transposed in LDS
+// (row stride d + 8 halves keeps the fragment reads conflict-free) and reuses
+// it for 128 rows.
 #include "li_internal.hpp"
 
 namespace li {
 namespace {
 
-template <int R, int D>
+template <int R, int D, int NC>
 __global__ __launch_bounds__(256) void k_absorb_bf16(const u16 *q, const u16 *W, u16 *qt, int64_t QH)
 {
     constexpr int LD = D + 8; // halves per transposed row
     constexpr int KS = D / 16;
-    __shared__ __attribute__((aligned(16))) u16 wt[R * LD];
+    constexpr int ITEMS = (D / 2) * (NC / 8); // (row pair, 8 columns) pieces of this column slice of W
+    constexpr int NIT = (ITEMS + 255) / 256;
+    __shared__ __attribute__((aligned(16))) u16 wt[NC * LD];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    // W [D][R] -> wt [R][LD], two source rows per item so LDS writes are 32-bit.
-    for (int it = tid; it < (D / 2) * (R / 8); it += 256) {
-        const int e = (it / (R / 8)) * 2;
-        const int t0 = (it % (R / 8)) * 8;
-        const bf16x8 r0 = *(const bf16x8 *)(W + (int64_t)e * R + t0);
-        const bf16x8 r1 = *(const bf16x8 *)(W + (int64_t)(e + 1) * R + t0);
-        const u16 *h0 = (const u16 *)&r0;
-        const u16 *h1 = (const u16 *)&r1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *(uint32_t *)(wt + (t0 + i) * LD + e) = (uint32_t)h0[i] | ((uint32_t)h1[i] << 16);
-    }
-    __syncthreads();
+    const int c0 = blockIdx.y * NC; // first column of W (and of qt) this workgroup covers
     const int64_t m0 = (int64_t)blockIdx.x * 128 + wv * 32;
-    if (m0 >= QH) return;
+
+    // A fragments (rows of q are K-contiguous already), issued first so their
+    // latency overlaps the W loads.
     bf16x8 a[KS];
     {
         const int64_t m = m0 + (lane & 31);
+        const int64_t mc = m < QH ? m : QH - 1;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (m < QH) {
-                a[s] = *(const bf16x8 *)(q + m * D + s * 16 + (lane >> 5) * 8);
-            } else {
+        for (int s = 0; s < KS; ++s) a[s] = *(const bf16x8 *)(q + mc * D + s * 16 + (lane >> 5) * 8);
+        if (m >= QH) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
                 bf16x8 z = {};
                 a[s] = z;
             }
         }
     }
+    // W[:, c0:c0+NC] -> wt [NC][LD] (transposed), two source rows per piece so
+    // the LDS writes are 32-bit; all loads are issued before any write.
+    bf16x8 r0[NIT], r1[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        int it = tid + k * 256;
+        it = it < ITEMS ? it : ITEMS - 1;
+        const int e = (it / (NC / 8)) * 2;
+        const int t0 = c0 + (it % (NC / 8)) * 8;
+        r0[k] = *(const bf16x8 *)(W + (int64_t)e * R + t0);
+        r1[k] = *(const bf16x8 *)(W + (int64_t)(e + 1) * R + t0);
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = tid + k * 256;
+        if (it < ITEMS) {
+            const int e = (it / (NC / 8)) * 2;
+            const int tl = (it % (NC / 8)) * 8;
+            const u16 *h0 = (const u16 *)&r0[k];
+            const u16 *h1 = (const u16 *)&r1[k];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *(uint32_t *)(wt + (tl + i) * LD + e) = (uint32_t)h0[i] | ((uint32_t)h1[i] << 16);
+        }
+    }
+    __syncthreads();
+    if (m0 >= QH) return;
 #pragma unroll 1
-    for (int nt = 0; nt < R / 32; ++nt) {
+    for (int nt = 0; nt < NC / 32; ++nt) {
         f32x16 acc = {};
         const int n = nt * 32 + (lane & 31);
 #pragma unroll
@@ -63,7 +84,7 @@ __global__ __launch_bounds__(256) void k_absorb_bf16(const u16 *q, const u16 *W,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t m = m0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (m < QH) qt[m * R + n] = f32_to_bf16_rne(acc[r]);
+            if (m < QH) qt[m * R + c0 + n] = f32_to_bf16_rne(acc[r]);
         }
     }
 }
@@ -80,18 +101,32 @@ __global__ __launch_bounds__(256) void k_absorb_f32(const float *q, const float 
     qt[i] = acc;
 }
 
+template <int R, int D>
+void launch_rd(const u16 *q, const u16 *W, u16 *qt, int64_t QH, hipStream_t s)
+{
+    const int64_t mblocks = (QH + 127) / 128;
+    if (mblocks >= 256) {
+        // many rows (prefill): each workgroup covers all columns, W staged once per 128 rows
+        hipLaunchKernelGGL((k_absorb_bf16<R, D, R>), dim3((unsigned)mblocks, 1), dim3(256), 0, s, q, W, qt, QH);
+    } else {
+        // few rows (decode): one 32-column slice per workgroup, so the W loads
+        // and the MFMA work spread over R/32 times more workgroups
+        hipLaunchKernelGGL((k_absorb_bf16<R, D, 32>), dim3((unsigned)mblocks, R / 32), dim3(256), 0, s, q, W, qt,
+                           QH);
+    }
+}
+
 template <int R>
 hipError_t launch_bf16_r(const void *q, const void *W, void *qt, int64_t QH, int d, hipStream_t s)
 {
-    const unsigned blocks = (unsigned)((QH + 127) / 128);
     const u16 *qq = (const u16 *)q;
     const u16 *ww = (const u16 *)W;
     u16 *oo = (u16 *)qt;
     switch (d) {
-    case 32: hipLaunchKernelGGL((k_absorb_bf16<R, 32>), dim3(blocks), dim3(256), 0, s, qq, ww, oo, QH); break;
-    case 64: hipLaunchKernelGGL((k_absorb_bf16<R, 64>), dim3(blocks), dim3(256), 0, s, qq, ww, oo, QH); break;
-    case 128: hipLaunchKernelGGL((k_absorb_bf16<R, 128>), dim3(blocks), dim3(256), 0, s, qq, ww, oo, QH); break;
-    case 256: hipLaunchKernelGGL((k_absorb_bf16<R, 256>), dim3(blocks), dim3(256), 0, s, qq, ww, oo, QH); break;
+    case 32: launch_rd<R, 32>(qq, ww, oo, QH, s); break;
+    case 64: launch_rd<R, 64>(qq, ww, oo, QH, s); break;
+    case 128: launch_rd<R, 128>(qq, ww, oo, QH, s); break;
+    case 256: launch_rd<R, 256>(qq, ww, oo, QH, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
