@@ -211,9 +211,13 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     sc.seq_lens = cache->seq_lens;
     sc.Q = Q;
     sc.k = k;
-    sc.max_n = max_n;
+    sc.max_n = queries->max_valid; // rows past the caller's bound are never scored
     sc.idx = idx;
     sc.count = count;
+    // HS anchor: its own top-k_inner inside its top-k (a subset by construction)
+    sc.k_inner = k_inner;
+    sc.idx_inner = idx_inner;
+    sc.count_inner = count_inner;
 
     const bool many = Q >= 4 * cache->batch;
     const bool scored = queries->max_valid > 0;
@@ -239,22 +243,6 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     }
     if (e != hipSuccess) return hip_fail(e, "select launch");
 
-    if (k_inner > 0) {
-        // Nested selection among the outer winners (HS anchor: its own top-k
-        // inside its top-M candidates).
-        li::SelCall ic = sc;
-        ic.row = li::SelRow{S, sld, idx, k, idx, k};
-        ic.src_mode = li::kSrcCount;
-        ic.cnt = count;
-        ic.cnt_cap = k;
-        ic.k = k_inner;
-        ic.max_n = std::min<int64_t>(k, max_n);
-        ic.idx = idx_inner;
-        ic.count = count_inner;
-        li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(ic, sw, false, stream);
-        if (e != hipSuccess) return hip_fail(e, "inner select");
-    }
     return ok();
 }
 

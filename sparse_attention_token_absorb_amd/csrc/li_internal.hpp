@@ -10,8 +10,17 @@
 namespace li {
 
 constexpr int kHistBins = 4096;   // first radix digit: key bits [31:20]
-constexpr int kHistStride = kHistBins + 4; // per query: histogram, then 4 counters
+constexpr int kHistStride = kHistBins + 8; // per query: histogram, then the slots below
 constexpr int kSelThreads = 1024; // threads of the per-query selection workgroup
+
+// Per-query slots after the histogram.
+enum {
+    kSlotUpO = kHistBins + 0,  // rows emitted above the outer threshold digit (filter counter)
+    kSlotTieO = kHistBins + 1, // rows on the outer threshold digit (filter counter)
+    kSlotN = kHistBins + 2,    // the query's row count, recorded by the scoring kernel
+    kSlotUpI = kHistBins + 3,  // same two counters for the nested (inner) selection
+    kSlotTieI = kHistBins + 4,
+};
 
 // Rows to score for one call.
 //   contiguous mode (cand == nullptr): query i scores its causal prefix
@@ -35,7 +44,8 @@ struct ScoreArgs {
     float *out;
     int64_t out_ld;
     int64_t max_rows; // bound on every query's row count (rows past it are not scored)
-    int32_t *hist;    // optional [Q][kHistStride]: first-digit counts of the keys written (accumulated)
+    int32_t *hist;    // optional [Q][kHistStride]: first-digit counts of the keys written
+                      // (accumulated) and the query's row count in slot kSlotN
 };
 
 // Scoring.  `max_rows` bounds every query's row count (grid sizing).
@@ -54,8 +64,9 @@ hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, in
 // Top-k selection over per-query virtual rows of scores.
 // ---------------------------------------------------------------------------
 struct SelWorkspace {
-    int32_t *hist; // [Q][kHistStride]: first-digit counts, then counters (rows emitted, rows tied)
+    int32_t *hist; // [Q][kHistStride]: first-digit counts, then the slots above
     uint2 *cand;   // [Q][cap] (key, index) of rows tied on the threshold digit
+    uint2 *cand2;  // [Q][cap] the same for the nested selection's threshold digit
     int64_t cap;
 };
 
@@ -75,6 +86,11 @@ struct SelCall {
     int64_t max_n;   // host bound on every n
     int32_t *idx;    // [Q][k]
     int32_t *count;  // [Q]
+    // Optional nested selection (k_inner > 0): the top-k_inner rows, always a
+    // subset of the top-k ones.
+    int32_t k_inner;
+    int32_t *idx_inner;   // [Q][k_inner]
+    int32_t *count_inner; // [Q]
 };
 
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n);
@@ -83,7 +99,7 @@ SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n);
 // Zero the histograms (before a scoring kernel accumulates into them).
 hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s);
 // The selection proper (after scores exist).  have_hist: a scoring kernel
-// filled ws.hist for these very scores.
+// filled ws.hist (histogram and row counts) for these very scores.
 hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s);
 
 } // namespace li

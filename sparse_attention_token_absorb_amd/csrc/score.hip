@@ -194,6 +194,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     const int b = a.qseq[q];
     int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     if (row0 >= n) return;
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
@@ -294,6 +295,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
     const int b = a.qseq[q];
     int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     if (row0 >= n) return;
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
@@ -488,6 +490,7 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
             my_b = sb[u];
             my_n = sn[u];
         }
+    if (a.hist && blockIdx.y == 0 && lane == 0 && q < a.Q) a.hist[(int64_t)q * kHistStride + kSlotN] = my_n;
     uint32_t *hist = s_hist[wv];
     if (a.hist) hist_zero(hist, 64, lane);
     QueryRegs<R, HB> qr;
@@ -565,6 +568,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     const int b = a.qseq[q];
     int n = a.cand ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     if (row0 >= n) return;
     const int64_t row1 = min64(row0 + rows_per_wg, n);

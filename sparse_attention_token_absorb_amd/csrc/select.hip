@@ -62,6 +62,14 @@ __device__ __forceinline__ int32_t out_id(const SelRow &r, int q, int64_t i)
     return r.omap ? r.omap[(int64_t)q * r.old + i] : (int32_t)i;
 }
 
+__device__ __forceinline__ int clamp_n(int n, int64_t max_n)
+{
+    n = n > 0 ? n : 0;
+    return n < max_n ? n : (int)max_n; // the caller's bound sizes every buffer
+}
+
+// Row count of query q computed from the call's own inputs (used when no
+// scoring kernel recorded it).
 __device__ __forceinline__ int query_n(const SelCall &c, int q)
 {
     int n;
@@ -69,9 +77,8 @@ __device__ __forceinline__ int query_n(const SelCall &c, int q)
         n = valid_rows(c.qpos[q], c.seq_lens[c.qseq[q]]);
     } else {
         n = c.cnt[q] < c.cnt_cap ? c.cnt[q] : c.cnt_cap;
-        n = n > 0 ? n : 0;
     }
-    return n < c.max_n ? n : (int)c.max_n; // the caller's bound sizes every buffer
+    return clamp_n(n, c.max_n);
 }
 
 __device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & 63)) - 1ull; }
@@ -82,6 +89,23 @@ struct Scratch {
     uint32_t wtot[T / 64];
     int res[2];
     int cnt[4];
+};
+
+// The first-digit histogram of one query, held in registers between its
+// (early) load and its store into LDS.
+template <int T>
+struct HistRegs {
+    uint32_t v[kHistBins / T];
+    __device__ __forceinline__ void load(const int32_t *g)
+    {
+#pragma unroll
+        for (int e = 0; e < kHistBins / T; ++e) v[e] = (uint32_t)g[e * T + threadIdx.x];
+    }
+    __device__ __forceinline__ void store(uint32_t *h) const
+    {
+#pragma unroll
+        for (int e = 0; e < kHistBins / T; ++e) h[e * T + threadIdx.x] = v[e];
+    }
 };
 
 // Block-wide search on an LDS histogram of nbins bins: the bin b holding
@@ -137,36 +161,56 @@ __device__ __forceinline__ void emit(bool e, int32_t val, int32_t *out, int *cnt
     if (e) out[base + __popcll(m & lanes_below())] = val;
 }
 
+// Lanes with e set append (key, id) to the LDS tie list (capacity kCandCap;
+// the slot count keeps growing past it so overflow is detectable).
+__device__ __forceinline__ void push_tie(bool e, uint32_t key, int32_t id, uint32_t *ck, int32_t *ci, int *cnt)
+{
+    const uint64_t m = __ballot(e);
+    if (m == 0ull) return;
+    int base = 0;
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, __popcll(m));
+    base = __shfl(base, 0);
+    const int slot = base + __popcll(m & lanes_below());
+    if (e && slot < kCandCap) {
+        ck[slot] = key;
+        ci[slot] = id;
+    }
+}
+
 // Digits below the first: bits [19:9] then [8:0].
 __device__ __forceinline__ int lvl_shift(int l) { return l == 1 ? 9 : 0; }
 __device__ __forceinline__ int lvl_bins(int l) { return l == 1 ? 2048 : 512; }
 
-// Element sources for the in-block levels: key(i), id(i).
+// Element sources for the in-block levels: key(i) and the id to output.
 struct CandLds {
     const uint32_t *k;
     const int32_t *d;
     __device__ uint32_t key(int i) const { return k[i]; }
-    __device__ int64_t id(int i) const { return d[i]; }
+    __device__ int32_t out(int i) const { return d[i]; }
 };
 struct CacheLds {
     const uint32_t *k;
+    SelRow r;
+    int q;
     __device__ uint32_t key(int i) const { return k[i]; }
-    __device__ int64_t id(int i) const { return i; }
+    __device__ int32_t out(int i) const { return out_id(r, q, i); }
 };
 struct RowGlobal {
     SelRow r;
     int q;
     __device__ uint32_t key(int i) const { return key_at(r, q, i); }
-    __device__ int64_t id(int i) const { return i; }
+    __device__ int32_t out(int i) const { return out_id(r, q, i); }
 };
 
 // Levels 1 and 2 over m elements restricted to (key & pmask) == prefix;
 // emits the `remaining` best of them at out[sh.cnt[0] ...].  All threads.
+// Rows left equal on all 32 bits are taken in element order, so two calls
+// over the same elements with budgets a <= b take nested sets.
 template <int T, class Src>
 __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
-                              int32_t *out, const SelRow &row, int q, Scratch<T> &sh)
+                              int32_t *out, Scratch<T> &sh)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wbase = tid - lane;
     int level = 1;
     for (; level < 3 && remaining > 0; ++level) {
@@ -191,7 +235,7 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
                 const uint32_t key = src.key(i);
                 e = (key & pmask) == prefix && ((key >> shift) & dmask) > (uint32_t)bin;
             }
-            emit(e, e ? out_id(row, q, src.id(i)) : 0, out, &sh.cnt[0]);
+            emit(e, e ? src.out(i) : 0, out, &sh.cnt[0]);
         }
         remaining -= above;
         prefix |= (uint32_t)bin << shift;
@@ -199,42 +243,35 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
         __syncthreads();
     }
     if (remaining > 0 && level == 3) {
-        // all 32 bits resolved: the survivors share one key
-        if (tid == 0) sh.cnt[2] = 0;
-        __syncthreads();
-        for (int i0 = wbase; i0 < m; i0 += T) {
-            const int i = i0 + lane;
+        // All 32 bits resolved: the survivors share one key.  Take the first
+        // `remaining` of them in element order (rank by a block-wide count).
+        uint32_t base = 0;
+        for (int i0 = 0; i0 < m && base < remaining; i0 += T) {
+            const int i = i0 + tid;
             const bool tie = i < m && src.key(i) == prefix;
             const uint64_t tm = __ballot(tie);
-            if (tm == 0ull) continue;
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&sh.cnt[2], __popcll(tm));
-            base = __shfl(base, 0);
-            const bool take = tie && (uint32_t)(base + __popcll(tm & lanes_below())) < remaining;
-            emit(take, take ? out_id(row, q, src.id(i)) : 0, out, &sh.cnt[0]);
+            if (lane == 0) sh.wtot[wv] = (uint32_t)__popcll(tm);
+            __syncthreads();
+            uint32_t before = base, total = 0;
+            for (int w2 = 0; w2 < T / 64; ++w2) {
+                const uint32_t v = sh.wtot[w2];
+                before += w2 < wv ? v : 0u;
+                total += v;
+            }
+            const bool take = tie && before + (uint32_t)__popcll(tm & lanes_below()) < remaining;
+            __syncthreads();
+            emit(take, take ? src.out(i) : 0, out, &sh.cnt[0]);
+            base += total;
         }
     }
     __syncthreads();
 }
 
-// Threshold bin of the first digit from the query's global histogram.
-template <int T>
-__device__ void threshold_from_hist(const int32_t *g, uint32_t *h0, int K, Scratch<T> &sh)
-{
-    constexpr int PER = kHistBins / T;
-    uint32_t v[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) v[e] = (uint32_t)g[e * T + threadIdx.x];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) h0[e * T + threadIdx.x] = v[e];
-    __syncthreads();
-    find_bin<T>(h0, kHistBins, (uint32_t)K, sh);
-}
-
 // ---------------------------------------------------------------------------
 // One workgroup per query.  HIST: the scoring kernel counted the first digit
-// into the global histogram; otherwise it is counted here (rows cached in
-// LDS when they fit).
+// into the global histogram and recorded n; otherwise both are found here.
+// Rows of at most kCandCap elements are loaded once, all at the start
+// (keys, output ids, histogram), and everything after that runs in LDS.
 // ---------------------------------------------------------------------------
 template <bool HIST>
 __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
@@ -244,91 +281,146 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
     __shared__ uint32_t ck[kCandCap];
     __shared__ int32_t ci[kCandCap];
     __shared__ uint32_t cache[HIST ? 1 : kKeyCache];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int q = blockIdx.x;
-    const int n = query_n(c, q);
-    const int K = min(n, c.k);
+    const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
     int32_t *out = c.idx + (int64_t)q * c.k;
-    const bool cached = !HIST && n <= kKeyCache;
-    constexpr int64_t ROUND = (int64_t)NT * kB * 4;
-    if (K > 0) {
-        if (tid == 0) {
-            sh.cnt[0] = 0;
-            sh.cnt[1] = 0;
+    if (tid == 0) {
+        sh.cnt[0] = 0;
+        sh.cnt[1] = 0;
+    }
+    int K = 0;
+    if (c.max_n <= kCandCap) {
+        constexpr int E = kCandCap / NT;
+        const int mx = (int)c.max_n;
+        uint32_t kk[E];
+        int32_t id[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = e * NT + tid;
+            kk[e] = 0u;
+            id[e] = 0;
+            if (i < mx) {
+                kk[e] = key_at(c.row, q, i);
+                id[e] = out_id(c.row, q, i);
+            }
         }
+        HistRegs<NT> hr;
+        int n;
         if constexpr (HIST) {
-            threshold_from_hist<NT>(ws.hist + (int64_t)q * kHistStride, h0, K, sh);
+            hr.load(hq);
+            n = clamp_n(hq[kSlotN], mx);
         } else {
-            for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
-            __syncthreads();
-            for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
-                uint32_t kk[kB][4];
+            n = query_n(c, q);
+        }
+        K = min(n, c.k);
+        if (K > 0) {
+            if constexpr (HIST) {
+                hr.store(h0);
+            } else {
+                for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
+                __syncthreads();
 #pragma unroll
-                for (int b = 0; b < kB; ++b) keys4(c.row, q, r0 + 4 * ((int64_t)b * NT + tid), n, kk[b]);
-#pragma unroll
-                for (int b = 0; b < kB; ++b)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
-                        if (i < n) {
-                            atomicAdd(&h0[kk[b][t] >> kDigit0Shift], 1u);
-                            if (cached) cache[i] = kk[b][t];
-                        }
-                    }
+                for (int e = 0; e < E; ++e)
+                    if (e * NT + tid < n) atomicAdd(&h0[kk[e] >> kDigit0Shift], 1u);
             }
             __syncthreads();
             find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
-        }
-        const int bin = sh.res[0];
-        const int above = sh.res[1];
-        if (bin >= 0) {
-            // one pass over the row: emit above, keep ties
-            for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
-                uint32_t kk[kB][4];
+            const int bin = sh.res[0];
+            const int above = sh.res[1];
+            if (bin >= 0) {
 #pragma unroll
-                for (int b = 0; b < kB; ++b) {
-                    const int64_t i = r0 + 4 * ((int64_t)b * NT + tid);
-                    if (cached) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) kk[b][t] = i + t < n ? cache[i + t] : 0u;
-                    } else {
-                        keys4(c.row, q, i, n, kk[b]);
-                    }
+                for (int e = 0; e < E; ++e) {
+                    const bool ok = e * NT + tid < n;
+                    const int dg = (int)(kk[e] >> kDigit0Shift);
+                    emit(ok && dg > bin, id[e], out, &sh.cnt[0]);
+                    push_tie(ok && dg == bin, kk[e], id[e], ck, ci, &sh.cnt[1]);
                 }
+                __syncthreads();
+                finish_levels<NT>(CandLds{ck, ci}, sh.cnt[1], (uint32_t)bin << kDigit0Shift,
+                                  0xFFFFFFFFu << kDigit0Shift, (uint32_t)(K - above), out, sh);
+            }
+        }
+    } else {
+        // Long rows: stream them (16-byte loads, kB rounds in flight).
+        int n;
+        if constexpr (HIST) {
+            n = clamp_n(hq[kSlotN], c.max_n);
+        } else {
+            n = query_n(c, q);
+        }
+        K = min(n, c.k);
+        const bool cached = !HIST && n <= kKeyCache;
+        constexpr int64_t ROUND = (int64_t)NT * kB * 4;
+        if (K > 0) {
+            if constexpr (HIST) {
+                HistRegs<NT> hr;
+                hr.load(hq);
+                hr.store(h0);
+                __syncthreads();
+                find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+            } else {
+                for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
+                __syncthreads();
+                for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
+                    uint32_t kk[kB][4];
 #pragma unroll
-                for (int b = 0; b < kB; ++b)
+                    for (int b = 0; b < kB; ++b) keys4(c.row, q, r0 + 4 * ((int64_t)b * NT + tid), n, kk[b]);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
-                        const int dg = (int)(kk[b][t] >> kDigit0Shift);
-                        const bool ok = i < n;
-                        const bool up = ok && dg > bin;
-                        emit(up, up ? out_id(c.row, q, i) : 0, out, &sh.cnt[0]);
-                        const bool tie = ok && dg == bin;
-                        const uint64_t tm = __ballot(tie);
-                        if (tm) {
-                            int base = 0;
-                            if (lane == 0) base = atomicAdd(&sh.cnt[1], __popcll(tm));
-                            base = __shfl(base, 0);
-                            const int slot = base + __popcll(tm & lanes_below());
-                            if (tie && slot < kCandCap) {
-                                ck[slot] = kk[b][t];
-                                ci[slot] = (int32_t)i;
+                    for (int b = 0; b < kB; ++b)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
+                            if (i < n) {
+                                atomicAdd(&h0[kk[b][t] >> kDigit0Shift], 1u);
+                                if (cached) cache[i] = kk[b][t];
                             }
                         }
-                    }
+                }
+                __syncthreads();
+                find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
             }
-            __syncthreads();
-            const int nc = sh.cnt[1];
-            const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
-            const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
-            const uint32_t need = (uint32_t)(K - above);
-            if (nc <= kCandCap) {
-                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, c.row, q, sh);
-            } else if (cached) {
-                finish_levels<NT>(CacheLds{cache}, n, prefix, pmask, need, out, c.row, q, sh);
-            } else {
-                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, c.row, q, sh);
+            const int bin = sh.res[0];
+            const int above = sh.res[1];
+            if (bin >= 0) {
+                // one pass over the row: emit above, keep ties
+                for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
+                    uint32_t kk[kB][4];
+#pragma unroll
+                    for (int b = 0; b < kB; ++b) {
+                        const int64_t i = r0 + 4 * ((int64_t)b * NT + tid);
+                        if (cached) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) kk[b][t] = i + t < n ? cache[i + t] : 0u;
+                        } else {
+                            keys4(c.row, q, i, n, kk[b]);
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < kB; ++b)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
+                            const int dg = (int)(kk[b][t] >> kDigit0Shift);
+                            const bool ok = i < n;
+                            const bool up = ok && dg > bin;
+                            emit(up, up ? out_id(c.row, q, i) : 0, out, &sh.cnt[0]);
+                            const bool tie = ok && dg == bin;
+                            push_tie(tie, kk[b][t], tie ? out_id(c.row, q, i) : 0, ck, ci, &sh.cnt[1]);
+                        }
+                }
+                __syncthreads();
+                const int nc = sh.cnt[1];
+                const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
+                const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
+                const uint32_t need = (uint32_t)(K - above);
+                if (nc <= kCandCap) {
+                    finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
+                } else if (cached) {
+                    finish_levels<NT>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, sh);
+                } else {
+                    finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
+                }
             }
         }
     }
@@ -338,28 +430,48 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
 
 // ---------------------------------------------------------------------------
 // Few queries, long rows: many workgroups per query stream the row once.
+// Each emits its rows above the threshold digit(s) and appends the rows on
+// them to the tie lists.  With a nested selection (k_inner > 0) the inner
+// threshold digit is found from the same histogram and served in the same
+// pass; its ties share the outer list when both digits coincide.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspace ws)
 {
     constexpr int T = kFilterThreads;
     __shared__ Scratch<T> sh;
     __shared__ uint32_t h0[kHistBins];
+    __shared__ int s_cnt[4];
     __shared__ int s_base[4];
     const int tid = threadIdx.x;
     const int q = blockIdx.y;
-    const int n = query_n(c, q);
-    const int K = min(n, c.k);
     const int64_t i0 = (int64_t)blockIdx.x * kFilterChunk;
-    if (K == 0 || i0 >= n) return;
-    int32_t *hist = ws.hist + (int64_t)q * kHistStride;
-    threshold_from_hist<T>(hist, h0, K, sh);
-    const int bin = sh.res[0];
-    if (bin < 0) return;
-    if (tid < 4) s_base[tid] = 0;
+    int32_t *hq = ws.hist + (int64_t)q * kHistStride;
+    // Loaded up front, together: this workgroup's keys (bounded by max_n,
+    // masked by n below), the histogram and n.
     uint32_t kk[kB][4];
 #pragma unroll
-    for (int b = 0; b < kB; ++b) keys4(c.row, q, i0 + 4 * ((int64_t)b * T + tid), n, kk[b]);
-    int nup = 0, ntie = 0;
+    for (int b = 0; b < kB; ++b) keys4(c.row, q, i0 + 4 * ((int64_t)b * T + tid), c.max_n, kk[b]);
+    HistRegs<T> hr;
+    hr.load(hq);
+    const int n = clamp_n(hq[kSlotN], c.max_n);
+    const int K = min(n, c.k);
+    const int Ki = c.k_inner > 0 ? min(n, c.k_inner) : 0;
+    if (K == 0 || i0 >= n) return;
+    if (tid < 4) s_cnt[tid] = 0;
+    hr.store(h0);
+    __syncthreads();
+    find_bin<T>(h0, kHistBins, (uint32_t)K, sh);
+    const int bin = sh.res[0];
+    int bin_i = -1;
+    if (Ki > 0) {
+        __syncthreads(); // every thread has read sh.res before it is rewritten
+        find_bin<T>(h0, kHistBins, (uint32_t)Ki, sh);
+        bin_i = sh.res[0];
+    }
+    if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
+    const bool inner = Ki > 0;
+    const bool sep = inner && bin_i != bin; // inner ties need a list of their own
+    int nup = 0, ntie = 0, nupi = 0, ntiei = 0;
 #pragma unroll
     for (int b = 0; b < kB; ++b)
 #pragma unroll
@@ -369,20 +481,28 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
             if (i < n) {
                 nup += dg > bin;
                 ntie += dg == bin;
+                if (inner) {
+                    nupi += dg > bin_i;
+                    ntiei += sep && dg == bin_i;
+                }
             }
         }
+    const int lu = nup ? atomicAdd(&s_cnt[0], nup) : 0;
+    const int lt = ntie ? atomicAdd(&s_cnt[1], ntie) : 0;
+    const int lui = nupi ? atomicAdd(&s_cnt[2], nupi) : 0;
+    const int lti = ntiei ? atomicAdd(&s_cnt[3], ntiei) : 0;
     __syncthreads();
-    const int lu = nup ? atomicAdd(&s_base[0], nup) : 0;
-    const int lt = ntie ? atomicAdd(&s_base[1], ntie) : 0;
-    __syncthreads();
-    if (tid == 0) {
-        s_base[2] = s_base[0] ? atomicAdd(&hist[kHistBins + 0], s_base[0]) : 0;
-        s_base[3] = s_base[1] ? atomicAdd(&hist[kHistBins + 1], s_base[1]) : 0;
+    if (tid < 4) {
+        const int slot = tid == 0 ? kSlotUpO : tid == 1 ? kSlotTieO : tid == 2 ? kSlotUpI : kSlotTieI;
+        const int v = s_cnt[tid];
+        s_base[tid] = v ? atomicAdd(&hq[slot], v) : 0;
     }
     __syncthreads();
-    int pu = s_base[2] + lu, pt = s_base[3] + lt;
+    int pu = s_base[0] + lu, pt = s_base[1] + lt, pui = s_base[2] + lui, pti = s_base[3] + lti;
     int32_t *out = c.idx + (int64_t)q * c.k;
+    int32_t *outi = inner ? c.idx_inner + (int64_t)q * c.k_inner : nullptr;
     uint2 *cand = ws.cand + (int64_t)q * ws.cap;
+    uint2 *cand2 = ws.cand2 + (int64_t)q * ws.cap;
 #pragma unroll
     for (int b = 0; b < kB; ++b)
 #pragma unroll
@@ -396,63 +516,99 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
                     if (pt < ws.cap) cand[pt] = make_uint2(kk[b][t], (uint32_t)i);
                     ++pt;
                 }
+                if (inner) {
+                    if (dg > bin_i) {
+                        outi[pui++] = out_id(c.row, q, i);
+                    } else if (sep && dg == bin_i) {
+                        if (pti < ws.cap) cand2[pti] = make_uint2(kk[b][t], (uint32_t)i);
+                        ++pti;
+                    }
+                }
             }
         }
 }
 
-// The remaining digits among the tied rows, one workgroup per query.
+// The remaining digits among the tied rows: blockIdx.y = 0 for the outer
+// selection, 1 for the nested one, one workgroup per query each.
 __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
 {
     __shared__ Scratch<NT> sh;
     __shared__ uint32_t h0[kHistBins];
     __shared__ uint32_t ck[kCandCap];
     __shared__ int32_t ci[kCandCap];
+    constexpr int E = kCandCap / NT;
     const int tid = threadIdx.x;
     const int q = blockIdx.x;
-    const int n = query_n(c, q);
+    const bool inner = blockIdx.y == 1;
+    const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
+    const int kout = inner ? c.k_inner : c.k;
+    int32_t *out = (inner ? c.idx_inner : c.idx) + (int64_t)q * kout;
+    // Loaded up front: the histogram, the counters, and the head of this
+    // part's tie list (the nested part's list is the likely one; the outer
+    // list is read later only when the two threshold digits coincide).
+    const int lim = (int)(ws.cap < kCandCap ? ws.cap : kCandCap);
+    const uint2 *list = (inner ? ws.cand2 : ws.cand) + (int64_t)q * ws.cap;
+    uint2 p[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = e * NT + tid;
+        p[e] = i < lim ? list[i] : make_uint2(0u, 0u);
+    }
+    HistRegs<NT> hr;
+    hr.load(hq);
+    const int n = clamp_n(hq[kSlotN], c.max_n);
+    const int tie_o = hq[kSlotTieO];
+    const int tie_i = hq[kSlotTieI];
     const int K = min(n, c.k);
-    int32_t *out = c.idx + (int64_t)q * c.k;
-    if (K > 0) {
-        const int32_t *hist = ws.hist + (int64_t)q * kHistStride;
-        threshold_from_hist<NT>(hist, h0, K, sh);
-        const int bin = sh.res[0];
-        const int above = sh.res[1];
-        if (bin >= 0) {
-            const int nc = hist[kHistBins + 1];
-            const uint2 *cand = ws.cand + (int64_t)q * ws.cap;
+    const int Kp = inner ? min(n, c.k_inner) : K;
+    if (Kp > 0) {
+        hr.store(h0);
+        __syncthreads();
+        find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+        const int bin_o = sh.res[0];
+        int bin = bin_o, above = sh.res[1];
+        if (inner) {
+            __syncthreads(); // every thread has read sh.res before it is rewritten
+            find_bin<NT>(h0, kHistBins, (uint32_t)Kp, sh);
+            bin = sh.res[0];
+            above = sh.res[1];
+        }
+        if (bin >= 0 && bin_o >= 0) {
+            const bool shared_list = inner && bin == bin_o;
+            const int nc = inner && !shared_list ? tie_i : tie_o;
+            if (shared_list) {
+                const uint2 *lo = ws.cand + (int64_t)q * ws.cap;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = e * NT + tid;
+                    p[e] = i < lim ? lo[i] : make_uint2(0u, 0u);
+                }
+            }
             if (tid == 0) sh.cnt[0] = above;
             const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
             const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
-            const uint32_t need = (uint32_t)(K - above);
-            if (nc <= kCandCap && nc <= ws.cap) {
-                for (int i0 = 0; i0 < nc; i0 += NT * 4) {
-                    uint2 p[4];
+            const uint32_t need = (uint32_t)(Kp - above);
+            if (nc <= lim) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = i0 + e * NT + tid;
-                        p[e] = i < nc ? cand[i] : make_uint2(0u, 0u);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = i0 + e * NT + tid;
-                        if (i < nc) {
-                            ck[i] = p[e].x;
-                            ci[i] = (int32_t)p[e].y;
-                        }
+                for (int e = 0; e < E; ++e) {
+                    const int i = e * NT + tid;
+                    if (i < nc) {
+                        ck[i] = p[e].x;
+                        ci[i] = out_id(c.row, q, (int64_t)p[e].y);
                     }
                 }
                 __syncthreads();
-                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, c.row, q, sh);
+                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
             } else {
-                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, c.row, q, sh);
+                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
             }
         }
     }
-    for (int i = K + tid; i < c.k; i += NT) out[i] = -1;
-    if (tid == 0) c.count[q] = K;
+    for (int i = Kp + tid; i < kout; i += NT) out[i] = -1;
+    if (tid == 0) (inner ? c.count_inner : c.count)[q] = Kp;
 }
 
-// Clears the per-query histograms and counters before a scoring kernel
+// Clears the per-query histograms and slots before a scoring kernel
 // accumulates into them.
 __global__ __launch_bounds__(256) void k_hist_clear(int32_t *hist, int64_t words)
 {
@@ -469,7 +625,7 @@ size_t sel_workspace_bytes(int64_t Q, int64_t max_n)
 {
     size_t b = (size_t)Q * kHistStride * 4;
     b = (b + 255) & ~(size_t)255;
-    return b + (size_t)Q * cand_cap(Q, max_n) * 8;
+    return b + 2 * (size_t)Q * cand_cap(Q, max_n) * 8;
 }
 
 SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n)
@@ -477,8 +633,9 @@ SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n)
     SelWorkspace w;
     w.hist = (int32_t *)base;
     size_t off = ((size_t)Q * kHistStride * 4 + 255) & ~(size_t)255;
-    w.cand = (uint2 *)((uint8_t *)base + off);
     w.cap = cand_cap(Q, max_n);
+    w.cand = (uint2 *)((uint8_t *)base + off);
+    w.cand2 = w.cand + Q * w.cap;
     return w;
 }
 
@@ -498,13 +655,29 @@ hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_his
         hipLaunchKernelGGL(k_filter, dim3((unsigned)chunks, c.Q), dim3(kFilterThreads), 0, s, c, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_final, dim3(c.Q), dim3(NT), 0, s, c, ws);
+        hipLaunchKernelGGL(k_final, dim3(c.Q, c.k_inner > 0 ? 2 : 1), dim3(NT), 0, s, c, ws);
         return hipGetLastError();
     }
     if (have_hist)
         hipLaunchKernelGGL(k_select<true>, dim3(c.Q), dim3(NT), 0, s, c, ws);
     else
         hipLaunchKernelGGL(k_select<false>, dim3(c.Q), dim3(NT), 0, s, c, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || c.k_inner <= 0) return e;
+    // Nested selection among the outer winners (a subset by construction).
+    SelCall ic = c;
+    ic.row = SelRow{c.row.S, c.row.ld, c.idx, c.k, c.idx, c.k};
+    ic.src_mode = kSrcCount;
+    ic.cnt = c.count;
+    ic.cnt_cap = c.k;
+    ic.k = c.k_inner;
+    ic.max_n = std::min<int64_t>(c.k, c.max_n);
+    ic.idx = c.idx_inner;
+    ic.count = c.count_inner;
+    ic.k_inner = 0;
+    ic.idx_inner = nullptr;
+    ic.count_inner = nullptr;
+    hipLaunchKernelGGL(k_select<false>, dim3(c.Q), dim3(NT), 0, s, ic, ws);
     return hipGetLastError();
 }
 

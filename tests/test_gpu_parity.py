@@ -363,3 +363,25 @@ def test_long_rows_with_massive_ties():
         verify_full(g, l, h.full_layer(g, cache, qs, l), tag="bigties")
     anchor, followers = h.hs_group(g, cache, qs)
     verify_hs(g, anchor, followers, tag="bigties")
+
+
+def test_hs_nested_selection_on_a_shared_tie_digit():
+    """The anchor's top-k and top-M thresholds fall on the same run of equal
+    scores (6000 identical rows), short enough to be resolved in LDS: the
+    nested set must still lie inside the outer one."""
+    h = H()
+    say("HS nested selection, shared tie digit")
+    g = synth.make_decode("nested", 57, B=1, lens=[20000], r=256, H=64, d=128, k=2048, M=4096)
+    lat = g.latent[0]
+    lat[7500:] = 0.0
+    s = oracle.score(oracle.absorb(g.q[0][0], g.W[0]), g.w[0][0], lat, 20000)
+    order = np.argsort(-s[:7500], kind="stable")
+    lat[order[1500:7500]] = lat[order[1500]]
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    anchor, followers = h.hs_group(g, cache, qs, M=4096, k=2048)
+    outer = set(h.host(anchor.idx)[0, :4096].tolist())
+    inner = set(h.host(anchor.idx_inner)[0, :2048].tolist())
+    assert int(h.host(anchor.count)[0]) == 4096 and int(h.host(anchor.count_inner)[0]) == 2048
+    assert len(inner) == 2048 and inner <= outer
+    verify_hs(g, anchor, followers, M=4096, k=2048, tag="nested")
