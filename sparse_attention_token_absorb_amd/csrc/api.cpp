@@ -221,9 +221,13 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
 
     const bool many = Q >= 4 * cache->batch;
     const bool scored = queries->max_valid > 0;
+    // Decode scoring counts the first radix digit as it writes (the row is
+    // read once more by selection anyway); prefill scoring is MFMA-bound and
+    // leaves the count to the selection pass.
+    const bool fused_hist = scored && !(many && cache->dtype == LI_BF16);
     hipError_t e = hipSuccess;
     if (scored) {
-        {
+        if (fused_hist) {
             li::TimedScope ts(LI_KERNEL_SELECT, stream);
             e = li::launch_hist_clear(sw, Q, stream);
         }
@@ -232,14 +236,14 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         a.out = S;
         a.out_ld = sld;
         a.max_rows = queries->max_valid;
-        a.hist = sw.hist;
+        a.hist = fused_hist ? sw.hist : nullptr;
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
         e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
         if (e != hipSuccess) return hip_fail(e, "score launch");
     }
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(sc, sw, scored, stream);
+        e = li::launch_select(sc, sw, fused_hist, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "select launch");
 

@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kGatherTiles = 16; // max tiles per wave in gather mode (row offsets kept in LDS)
 constexpr int kVrMaxTiles = 32;  // max tiles per wave of the register-staged decode kernel
+constexpr int kPrefillMaxTiles = 2048; // max tiles per prefill split (their page ids sit in LDS)
 
 // LDS-typed pointers keep every access a ds_* instruction (a generic pointer
 // would become a flat access that also waits on global memory).
@@ -39,11 +40,32 @@ typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef const __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
+// 16 bytes per lane from global memory straight into LDS at
+// lds_uniform + lane * 16 (global_load_lds_dwordx4, LDS base in M0).
+// Written as inline asm on purpose: the compiler then does not know that
+// LDS is being written, and does not drain every such load (vmcnt(0))
+// before each later LDS read.  The kernels wait for these loads themselves
+// (wait_after / wait_vmcnt, counting loads only: vector loads complete in
+// issue order) and publish them to other waves with a barrier.  The
+// instruction has no VGPR result, so no register is left in flight.  M0 is
+// saved and restored around it (with the wait state a write of M0 needs
+// before an LDS-direct load), so the compiler's own use of M0 is untouched.
 __device__ __forceinline__ void dma16(const void *g, lds_u8 *lds_uniform)
 {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_uniform, 16, 0, 0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[addr], off\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [addr] "v"(g), [lds] "s"(lds)
+                 : "memory");
 }
 
 // Workgroup barrier without the global-memory fences of __syncthreads():
@@ -454,20 +476,28 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
 // ---------------------------------------------------------------------------
 // Prefill: many queries per sequence.  Workgroup = 4 consecutive queries,
 // one per wave; the 4 waves share every latent tile (one DMA per tile,
-// split across the waves) through an NBUF-deep LDS ring.  Queries of a
-// workgroup that sit in different sequences are served in separate passes.
+// split across the waves) through an NBUF-deep LDS ring, one barrier per
+// tile.  The page ids of a split's tiles are staged in LDS first, so no
+// dependent global load sits in the stream.  Queries of a workgroup that
+// sit in different sequences are served in separate passes.  The LDS
+// footprint (ring + page ids) leaves room for two workgroups per CU, so a
+// second wave on each SIMD covers barriers and epilogues; the first radix
+// digit is counted by the selection pass instead of here.
 // ---------------------------------------------------------------------------
 template <int R, int HB, int NBUF>
-__global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_per_split)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill(ScoreArgs a,
+                                                                                            int tiles_per_split)
 {
     constexpr int TILE_BYTES = kTile * R * 2;
     constexpr int CH = R / 8;
     constexpr int NI = R / 16;
     constexpr int NIW = NI / 4;
     static_assert(NIW >= 1, "tile must split over 4 waves");
+    static_assert(NBUF >= 3, "ring depth");
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * TILE_BYTES];
-    __shared__ uint32_t s_hist[4][kHistBins];
+    __shared__ int32_t s_page_raw[kPrefillMaxTiles / 2 + 2];
     lds_u8 *ring = (lds_u8 *)ring_raw;
+    lds_i32 *s_page = (lds_i32 *)s_page_raw;
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -490,9 +520,6 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
             my_b = sb[u];
             my_n = sn[u];
         }
-    if (a.hist && blockIdx.y == 0 && lane == 0 && q < a.Q) a.hist[(int64_t)q * kHistStride + kSlotN] = my_n;
-    uint32_t *hist = s_hist[wv];
-    if (a.hist) hist_zero(hist, 64, lane);
     QueryRegs<R, HB> qr;
     if (q < a.Q) {
         qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
@@ -519,19 +546,26 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
         const int te = min(ts + tiles_per_split, ntiles_all);
         if (ts >= te) continue;
         const int nt = te - ts;
-        const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
+        // page ids of rows [ts*32, te*32): pages ts/2 .. (te-1)/2
+        const int p0 = ts >> 1;
+        const int np = ((te - 1) >> 1) - p0 + 1;
+        __syncthreads(); // the previous pass is done with the ring and the page ids
+        for (int pi = threadIdx.x; pi < np; pi += 256) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
+        __syncthreads();
         auto issue = [&](int i) {
-            const int64_t t0 = (int64_t)(ts + i) * kTile;
-            const int64_t base = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63)) * R;
+            const int t = ts + i;
+            const int page = s_page[(t >> 1) - p0];
+            const int64_t base = ((int64_t)page * kPage + (t & 1) * kTile) * R;
             issue_rows<R, CH, NIW>(pool, [&](int nr) { return base + (int64_t)nr * R; }, 0,
                                    ring + (i % NBUF) * TILE_BYTES, wv * NIW, NIW);
         };
         for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i);
 #pragma unroll 1
         for (int i = 0; i < nt; ++i) {
-            if (i + NBUF - 1 < nt) issue(i + NBUF - 1);
-            wait_after<NIW, NBUF - 1>(min(NBUF - 1, nt - 1 - i));
-            wg_barrier();
+            // tile i landed (this wave's part), tiles i+1..i+NBUF-2 may still fly
+            wait_after<NIW, NBUF - 2>(min(NBUF - 2, nt - 1 - i));
+            wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
+            if (i + NBUF - 1 < nt) issue(i + NBUF - 1); // into tile i-1's slot
             if (active) {
                 f32x16 acc[HB];
 #pragma unroll
@@ -542,17 +576,9 @@ __global__ __launch_bounds__(256) void k_score_prefill(ScoreArgs a, int tiles_pe
                 mfma_steps<R, HB, 0, R / 16, CH>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                 const float p = epilogue<HB>(acc, qr.w);
                 const int j = (ts + i) * kTile + lane;
-                if (lane < 32 && j < my_n) {
-                    out[j] = p;
-                    if (a.hist) atomicAdd(&hist[score_key(p) >> kDigit0Shift], 1u);
-                }
+                if (lane < 32 && j < my_n) out[j] = p;
             }
-            wg_barrier();
         }
-    }
-    if (a.hist && q < a.Q) {
-        wait_lds();
-        hist_flush(hist, a.hist + (int64_t)q * kHistStride, 64, lane);
     }
 }
 
@@ -625,12 +651,14 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     if (prefill) {
         constexpr int NBUF = R == 256 ? 4 : 6;
         const int qblocks = (a.Q + 3) / 4;
-        int splits = 1;
-        if (qblocks < 512) splits = (int)std::min<int64_t>((512 + qblocks - 1) / qblocks, tiles);
+        int64_t splits = 1;
+        if (qblocks < 512) splits = std::min<int64_t>((512 + qblocks - 1) / qblocks, tiles);
         if (splits < 1) splits = 1;
-        const int tps = (int)((tiles + splits - 1) / splits);
-        splits = (int)((tiles + tps - 1) / tps);
-        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF>), dim3(qblocks, splits), dim3(256), 0, s, a, tps);
+        int64_t tps = (tiles + splits - 1) / splits;
+        if (tps > kPrefillMaxTiles) tps = kPrefillMaxTiles;
+        splits = (tiles + tps - 1) / tps;
+        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s, a,
+                           (int)tps);
         return hipGetLastError();
     }
     // decode: about one round of one workgroup per CU
