@@ -52,9 +52,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--counters", action="store_true",
-                    help="hardware-counter pass: a few eager full-LatentIndex layers, then a plain 1 GiB copy "
-                         "whose counter readings scale the others to bytes; prints no JSON line")
+    ap.add_argument("--counters", choices=("decode", "prefill"), default=None,
+                    help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
+                         "then a plain 1 GiB copy whose counter readings scale the others to bytes; 'prefill' runs "
+                         "a few eager chunked-prefill layers")
     return ap.parse_args()
 
 
@@ -81,6 +82,14 @@ def main() -> int:
 
     def tdev(x, dt):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dt).to(dev)
+
+    if args.counters == "prefill":
+        pl = setup_prefill(B, synth, dev, bf, i32, tdev, args.context // 2)
+        for _ in range(3):
+            pl.layer()
+        torch.cuda.synchronize()
+        log("counter pass done: 3 chunked-prefill layers")
+        return 0
 
     # ------------------------------------------------------------------
     # Inputs (seeded, synthetic), resident on the GPU
@@ -150,7 +159,7 @@ def main() -> int:
 
     stream = torch.cuda.Stream(device=dev)
 
-    if args.counters:
+    if args.counters == "decode":
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -343,34 +352,21 @@ def main() -> int:
         del cache, key_caches
         torch.cuda.empty_cache()
         log("prefill inputs")
-        p5 = synth.make_prefill("prefill", 5, N=65536, Qn=4096, r=r, H=H, d=d, G=1, k=k)
-        pcache = make_cache_from(p5, B, tdev, i32, bf, dev)
-        pseq, ppos = i32(p5.qseq), i32(p5.qpos)
-        pq, pW, pw = tdev(p5.q[0], bf), tdev(p5.W[0], bf), torch.from_numpy(p5.w[0]).to(dev)
-        pqt = torch.empty((p5.Q, H, r), dtype=bf, device=dev)
-        pws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, p5.Q, 65536, H, r, k, 0), dtype=torch.uint8,
-                          device=dev)
-        pout = B.TopK(torch.empty((p5.Q, k), dtype=torch.int32, device=dev),
-                      torch.empty(p5.Q, dtype=torch.int32, device=dev))
-
-        def prefill_layer():
-            B.absorb_query(pq, pW, out=pqt)
-            B.score_topk(pcache, pseq, ppos, 65536, pqt, pw, k, ws=pws, out=pout)
-
+        pl = setup_prefill(B, synth, dev, bf, i32, tdev, N // 2)
         with torch.cuda.stream(stream):
-            prefill_layer()
+            pl.layer()
         torch.cuda.synchronize()
         preps = 5
-        sc_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_SCORE_PREFILL, preps)
-        sel_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_SELECT, preps)
-        ab_ms, _ = kernel_time(prefill_layer, B.LI_KERNEL_ABSORB, preps)
-        pairs = int(np.sum(np.minimum(p5.qpos.astype(np.int64) + 1, 65536)))
-        flops = 2.0 * H * r * pairs
+        sc_ms, _ = kernel_time(pl.layer, B.LI_KERNEL_SCORE_PREFILL, preps)
+        sel_ms, _ = kernel_time(pl.layer, B.LI_KERNEL_SELECT, preps)
+        ab_ms, _ = kernel_time(pl.layer, B.LI_KERNEL_ABSORB, preps)
+        flops = 2.0 * H * r * pl.pairs
         tf = flops / (sc_ms * 1e-3) / 1e12
-        prefill = {"workload": "4096 queries at positions 61440..65535 of a 65536-row cache, one layer",
+        prefill = {"workload": f"{pl.Q} queries at positions {pl.n - pl.Q}..{pl.n - 1} of a {pl.n}-row cache, "
+                               f"one layer",
                    "score_ms": round(sc_ms, 3), "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                    "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "select_ms": round(sel_ms, 3),
-                   "absorb_ms": round(ab_ms, 3), "valid_pairs": pairs}
+                   "absorb_ms": round(ab_ms, 3), "valid_pairs": pl.pairs}
         log(f"prefill {prefill}")
 
     line = {
@@ -421,6 +417,36 @@ def measured_traffic(path: str, source: str):
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+class PrefillLayer:
+    """Chunked prefill of one layer: 4096 queries at the last positions of a
+    `n`-row cache (n = 65536 by default), absorb + score + per-row top-k."""
+
+    def __init__(self, B, synth, dev, bf, i32, tdev, n):
+        import numpy as np
+        import torch
+        self.n, self.Q = n, 4096
+        p5 = synth.make_prefill("prefill", 5, N=n, Qn=self.Q, r=256, H=64, d=128, G=1, k=2048)
+        self.cache = make_cache_from(p5, B, tdev, i32, bf, dev)
+        self.seq, self.pos = i32(p5.qseq), i32(p5.qpos)
+        self.q, self.W, self.w = tdev(p5.q[0], bf), tdev(p5.W[0], bf), torch.from_numpy(p5.w[0]).to(dev)
+        self.qt = torch.empty((p5.Q, p5.H, p5.r), dtype=bf, device=dev)
+        self.ws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, p5.Q, n, p5.H, p5.r, p5.k, 0),
+                              dtype=torch.uint8, device=dev)
+        self.out = B.TopK(torch.empty((p5.Q, p5.k), dtype=torch.int32, device=dev),
+                          torch.empty(p5.Q, dtype=torch.int32, device=dev))
+        self.k = p5.k
+        self.pairs = int(np.sum(np.minimum(p5.qpos.astype(np.int64) + 1, n)))
+        self.B = B
+
+    def layer(self):
+        self.B.absorb_query(self.q, self.W, out=self.qt)
+        self.B.score_topk(self.cache, self.seq, self.pos, self.n, self.qt, self.w, self.k, ws=self.ws, out=self.out)
+
+
+def setup_prefill(B, synth, dev, bf, i32, tdev, n):
+    return PrefillLayer(B, synth, dev, bf, i32, tdev, n)
 
 
 def make_cache_from(g, B, tdev, i32, bf, dev):

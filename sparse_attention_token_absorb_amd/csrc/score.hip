@@ -148,17 +148,60 @@ __device__ __forceinline__ void mfma_steps(const lds_u8 *buf, const QueryRegs<R,
     }
 }
 
+// max(x, 0) in one integer max on the bit pattern (negative floats, -0.0
+// included, have the sign bit set and become +0.0).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ReLU, head weights and head sum: the score of tile row (lane % 32).
 template <int HB>
 __device__ __forceinline__ float epilogue(const f32x16 (&acc)[HB], const float (&w)[HB][16])
 {
-    float p = 0.0f;
+    float ps[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb) {
+        ps[hb] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            p += w[hb][r] * fmaxf(acc[hb][r], 0.0f);
+        for (int r = 0; r < 16; ++r) ps[hb] = fmaf(w[hb][r], relu(acc[hb][r]), ps[hb]);
+    }
+    float p = ps[0];
+#pragma unroll
+    for (int hb = 1; hb < HB; ++hb) p += ps[hb];
     return p + __shfl_xor(p, 32);
+}
+
+// All R/16 MFMA steps over one full-width tile in LDS, with the B fragments
+// read D steps ahead of their use so LDS latency hides behind the MFMAs.
+template <int R, int HB, int CH, int D>
+__device__ __forceinline__ void mfma_tile_prefetch(const lds_u8 *buf, const QueryRegs<R, HB> &qr,
+                                                   f32x16 (&acc)[HB])
+{
+    constexpr int KS = R / 16;
+    constexpr int DD = D < KS ? D : KS;
+    const int lane = threadIdx.x & 63;
+    const int nr = lane & 31, g = lane >> 5;
+    auto frag = [&](int s) -> bf16x8 {
+        const int c = 2 * s + g;
+        return *(lds_bf16x8 *)(buf + (nr * CH + (c ^ (nr % CH))) * 16);
+    };
+    bf16x8 b[DD];
+#pragma unroll
+    for (int s = 0; s < DD; ++s) b[s] = frag(s);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const bf16x8 cur = b[s % DD];
+        if (s + DD < KS) b[s % DD] = frag(s + DD);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][s], cur, acc[hb], 0, 0, 0);
+    }
+    // Keep that order in the schedule: the first DD reads, then per step
+    // its HB MFMAs followed by the read for step s + DD.
+    __builtin_amdgcn_sched_group_barrier(0x100, DD, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, HB, 0);
+        if (s + DD < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
 }
 
 // Copy `NIC` KiB of a 32-row tile (CH pieces of 16 B per row, starting at
@@ -552,20 +595,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         __syncthreads(); // the previous pass is done with the ring and the page ids
         for (int pi = threadIdx.x; pi < np; pi += 256) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
         __syncthreads();
-        auto issue = [&](int i) {
-            const int t = ts + i;
-            const int page = s_page[(t >> 1) - p0];
-            const int64_t base = ((int64_t)page * kPage + (t & 1) * kTile) * R;
+        auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
+        auto issue = [&](int i, int page) {
+            const int64_t base = ((int64_t)page * kPage + ((ts + i) & 1) * kTile) * R;
             issue_rows<R, CH, NIW>(pool, [&](int nr) { return base + (int64_t)nr * R; }, 0,
                                    ring + (i % NBUF) * TILE_BYTES, wv * NIW, NIW);
         };
-        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i);
+        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i));
 #pragma unroll 1
         for (int i = 0; i < nt; ++i) {
+            const int inext = i + NBUF - 1;
+            const int pnext = inext < nt ? page_of(inext) : 0; // read before the barrier
             // tile i landed (this wave's part), tiles i+1..i+NBUF-2 may still fly
             wait_after<NIW, NBUF - 2>(min(NBUF - 2, nt - 1 - i));
             wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
-            if (i + NBUF - 1 < nt) issue(i + NBUF - 1); // into tile i-1's slot
+            if (inext < nt) issue(inext, pnext); // into tile i-1's slot
             if (active) {
                 f32x16 acc[HB];
 #pragma unroll
@@ -573,7 +617,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     f32x16 z = {};
                     acc[hb] = z;
                 }
-                mfma_steps<R, HB, 0, R / 16, CH>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
+                mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                 const float p = epilogue<HB>(acc, qr.w);
                 const int j = (ts + i) * kTile + lane;
                 if (lane < 32 && j < my_n) out[j] = p;
