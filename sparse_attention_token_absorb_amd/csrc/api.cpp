@@ -80,6 +80,7 @@ li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt
     a.pool = c->pool;
     a.bt = c->block_table;
     a.max_pages = c->max_pages;
+    a.num_pages = c->num_pages;
     a.seq_lens = c->seq_lens;
     a.qseq = qs->seq;
     a.qpos = qs->pos;

@@ -31,6 +31,7 @@ struct ScoreArgs {
     const void *pool;
     const int32_t *bt;
     int32_t max_pages;
+    int32_t num_pages; // pages in the pool (page ids read ahead of the row count are clamped to it)
     const int32_t *seq_lens;
     const int32_t *qseq;
     const int32_t *qpos;

@@ -256,33 +256,59 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int b = a.qseq[q];
-    int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
-    n = (int)min64(n, a.max_rows);
-    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
-    if (row0 >= n) return;
-    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     const int64_t first = row0 + (int64_t)wv * kTile;
-    int nt = 0;
-    if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
-    const int nchunks = 2 * nt;
+    auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
+    // This wave's tile count if the query had max_rows rows (its real count,
+    // known once the row count arrives, is at most that).
+    const int nt_max =
+        first < a.max_rows ? (int)min64(tiles_per_wave, (a.max_rows - first + 4 * kTile - 1) / (4 * kTile)) : 0;
 
+    // Start-up is a chain of dependent loads (sequence id, then page ids and
+    // the row count).  The query's fragments do not depend on it and go first;
+    // the first chunks are issued as soon as the page ids arrive, before the
+    // row count: a page id that is not in use is clamped into the pool, and
+    // what such a chunk brings in is never scored.
+    QueryRegs<R, HB> qr;
+    qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
+    // Scalar loads (constant address space): waited on with lgkmcnt, so
+    // waiting for them never waits for the chunk loads below.
+    const int b = ((const_i32_t *)a.qseq)[q];
+    int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
+                   : valid_rows(((const_i32_t *)a.qpos)[q], ((const_i32_t *)a.seq_lens)[b]);
+    n = (int)min64(n, a.max_rows);
     const u16 *pool = (const u16 *)a.pool;
     const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
     lds_u8 *const ring = (lds_u8 *)ring_raw + wv * NB * CHUNK;
-    auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
+    auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
 
     if constexpr (GATHER) {
-        // Physical rows of every tile of this wave, resolved once up front.
-        for (int i = 0; i < nt; ++i) {
-            int64_t j = tile_row0(i) + (lane & 31);
-            j = j < n ? j : n - 1;
-            const int pos = a.cand[(int64_t)q * a.cand_ld + j];
-            const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
-            if (lane < 32) s_row[(wv * kGatherTiles + i) * kTile + lane] = page * kPage + (pos & 63);
+        // Physical rows of every tile of this wave, resolved once up front
+        // (candidate slots past the count read slot cand_ld-1; positions and
+        // pages are clamped into the cache).
+        // Two phases, so that the loads of each phase are in flight
+        // together: one round trip for the candidates, one for the pages.
+        const int64_t max_pos = (int64_t)a.max_pages * kPage - 1;
+        int pos[kGatherTiles], page[kGatherTiles];
+#pragma unroll
+        for (int i = 0; i < kGatherTiles; ++i) {
+            pos[i] = 0;
+            if (i < nt_max) {
+                int64_t j = tile_row0(i) + (lane & 31);
+                j = j < a.cand_ld ? j : a.cand_ld - 1;
+                pos[i] = a.cand[(int64_t)q * a.cand_ld + j];
+            }
         }
-        wait_vmcnt<0>();
+#pragma unroll
+        for (int i = 0; i < kGatherTiles; ++i) {
+            pos[i] = pos[i] < 0 ? 0 : (pos[i] > max_pos ? (int)max_pos : pos[i]);
+            page[i] = 0;
+            if (i < nt_max) page[i] = a.bt[(int64_t)b * a.max_pages + (pos[i] >> 6)];
+        }
+#pragma unroll
+        for (int i = 0; i < kGatherTiles; ++i)
+            if (i < nt_max && lane < 32)
+                s_row[(wv * kGatherTiles + i) * kTile + lane] = clamp_page(page[i]) * kPage + (pos[i] & 63);
         wait_lds();
     }
     auto issue = [&](int c) {
@@ -294,14 +320,22 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
             issue_rows<R, CH, NIC>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c & 1) * HALF, buf, 0, NIC);
         } else {
             const int64_t t0 = tile_row0(i);
-            const int64_t base = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63)) * R;
+            const int64_t base = ((int64_t)clamp_page(bt[t0 >> 6]) * kPage + (t0 & 63)) * R;
             issue_rows<R, CH, NIC>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c & 1) * HALF, buf, 0, NIC);
         }
     };
+    const int npro = min(NB - 1, 2 * nt_max);
+    for (int c = 0; c < npro; ++c) issue(c);
 
-    for (int c = 0; c < NB - 1 && c < nchunks; ++c) issue(c);
-    QueryRegs<R, HB> qr;
-    qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (row0 >= n) {
+        wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
+        return;
+    }
+    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
+    int nt = 0;
+    if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
+    const int nchunks = 2 * nt; // <= 2 * nt_max: chunks issued above past it are waited for, never used
     if (a.hist) wg_barrier(); // histogram cleared before any wave counts into it
 
     float *out = a.out + (int64_t)q * a.out_ld;
@@ -330,6 +364,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
             }
         }
     }
+    wait_vmcnt<0>(); // chunks issued ahead of the row count and never used
     if (a.hist) {
         __syncthreads();
         hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
