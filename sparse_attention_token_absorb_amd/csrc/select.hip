@@ -6,22 +6,27 @@
 // them (§3.2, §C.4).
 //
 // Scores become order-preserving uint32 keys, selected by radix digits of
-// 12, 11 and 9 bits (most significant first).  The scoring kernels already
-// count the first digit (key >> 20) into a per-query 4096-bin histogram as
-// they write the scores, so the threshold bin is known before the rows are
-// read again.  One pass over each row then emits the rows above the
-// threshold digit and compacts the rows on it; the last two digits are
-// resolved among those few in LDS.
+// 12, 11 and 9 bits (most significant first).  The decode scoring kernels
+// already count the first digit (key >> 20) into a per-query 4096-bin
+// histogram as they write the scores, and record the row count beside it,
+// so the threshold bin is known before the rows are read again; otherwise
+// the selection counts it itself.  One pass over each row then emits the
+// rows above the threshold digit and compacts the rows on it; the last two
+// digits are resolved among those few in LDS.
 //   * Few queries with long rows (decode at 8K-128K): the pass is spread
 //     over many workgroups per query (k_filter), and one workgroup per
-//     query finishes (k_final).
+//     query finishes (k_final).  A nested selection (the HS anchor's top-k
+//     inside its top-M) rides along in the same two kernels.
 //   * Many queries or short rows (prefill, HS followers, the anchor's nested
-//     selection): one 1024-thread workgroup per query does it all (k_select).
-// Rows are read 16 bytes per lane, several loads in flight per thread (the
-// scores were written by other XCDs, so every load misses the local L2).
-// Emission uses wavefront ballots (one LDS atomic per wave, mbcnt offsets).
-// Rows whose key equals the final threshold key are taken in arbitrary
-// order, as many as the budget needs: equal scores are interchangeable.
+//     selection elsewhere): one 1024-thread workgroup per query does it all
+//     (k_select); rows of at most 8192 elements are loaded once, up front.
+// Every kernel issues all of its input loads before its first wait (rows
+// are read 16 bytes per lane; the scores were written by other XCDs, so
+// each load misses the local L2).  Emission uses wavefront ballots (one LDS
+// atomic per wave, mbcnt offsets).  Rows whose key equals the final
+// threshold key are taken in element order, as many as the budget needs:
+// equal scores are interchangeable, and the fixed order keeps nested
+// selections nested.
 #include "li_internal.hpp"
 
 #include <algorithm>
