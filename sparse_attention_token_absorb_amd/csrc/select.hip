@@ -166,8 +166,9 @@ __device__ __forceinline__ void emit(bool e, int32_t val, int32_t *out, int *cnt
     if (e) out[base + __popcll(m & lanes_below())] = val;
 }
 
-// Lanes with e set append (key, id) to the LDS tie list (capacity kCandCap;
-// the slot count keeps growing past it so overflow is detectable).
+// Lanes with e set append (key, id) to the LDS tie list (capacity CAP; the
+// slot count keeps growing past it so overflow is detectable).
+template <int CAP = kCandCap>
 __device__ __forceinline__ void push_tie(bool e, uint32_t key, int32_t id, uint32_t *ck, int32_t *ci, int *cnt)
 {
     const uint64_t m = __ballot(e);
@@ -176,7 +177,7 @@ __device__ __forceinline__ void push_tie(bool e, uint32_t key, int32_t id, uint3
     if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, __popcll(m));
     base = __shfl(base, 0);
     const int slot = base + __popcll(m & lanes_below());
-    if (e && slot < kCandCap) {
+    if (e && slot < CAP) {
         ck[slot] = key;
         ci[slot] = id;
     }
@@ -275,17 +276,26 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
 // ---------------------------------------------------------------------------
 // One workgroup per query.  HIST: the scoring kernel counted the first digit
 // into the global histogram and recorded n; otherwise both are found here.
-// Rows of at most kCandCap elements are loaded once, all at the start
-// (keys, output ids, histogram), and everything after that runs in LDS.
+//   kSmall  (max_n <= kCandCap): keys, output ids, histogram and n load once,
+//           all at the start, and everything after that runs in LDS;
+//   kCached (no histogram, max_n <= kKeyCache): the counting pass keeps the
+//           keys in LDS for the emission pass;
+//   kStream (longer rows): two passes over the row (one with a histogram),
+//           a smaller LDS footprint so that two workgroups share a CU.
 // ---------------------------------------------------------------------------
-template <bool HIST>
-__global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
+enum { kSmall = 0, kCached = 1, kStream = 2 };
+constexpr int kStreamCap = 4096; // tied rows kept in LDS by the streaming mode
+
+template <bool HIST, int MODE>
+__device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspace &ws)
 {
+    constexpr int CAP = MODE == kStream ? kStreamCap : kCandCap;
+    constexpr int KB = kB;
     __shared__ Scratch<NT> sh;
     __shared__ uint32_t h0[kHistBins];
-    __shared__ uint32_t ck[kCandCap];
-    __shared__ int32_t ci[kCandCap];
-    __shared__ uint32_t cache[HIST ? 1 : kKeyCache];
+    __shared__ uint32_t ck[CAP];
+    __shared__ int32_t ci[CAP];
+    __shared__ uint32_t cache[MODE == kCached ? kKeyCache : 1];
     const int tid = threadIdx.x;
     const int q = blockIdx.x;
     const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
         sh.cnt[1] = 0;
     }
     int K = 0;
-    if (c.max_n <= kCandCap) {
+    if constexpr (MODE == kSmall) {
         constexpr int E = kCandCap / NT;
         const int mx = (int)c.max_n;
         uint32_t kk[E];
@@ -347,7 +357,6 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
             }
         }
     } else {
-        // Long rows: stream them (16-byte loads, kB rounds in flight).
         int n;
         if constexpr (HIST) {
             n = clamp_n(hq[kSlotN], c.max_n);
@@ -355,8 +364,8 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
             n = query_n(c, q);
         }
         K = min(n, c.k);
-        const bool cached = !HIST && n <= kKeyCache;
-        constexpr int64_t ROUND = (int64_t)NT * kB * 4;
+        const bool cached = MODE == kCached && n <= kKeyCache;
+        constexpr int64_t ROUND = (int64_t)NT * KB * 4;
         if (K > 0) {
             if constexpr (HIST) {
                 HistRegs<NT> hr;
@@ -368,17 +377,18 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
                 for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
                 __syncthreads();
                 for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
-                    uint32_t kk[kB][4];
+                    uint32_t kk[KB][4];
 #pragma unroll
-                    for (int b = 0; b < kB; ++b) keys4(c.row, q, r0 + 4 * ((int64_t)b * NT + tid), n, kk[b]);
+                    for (int b = 0; b < KB; ++b) keys4(c.row, q, r0 + 4 * ((int64_t)b * NT + tid), n, kk[b]);
 #pragma unroll
-                    for (int b = 0; b < kB; ++b)
+                    for (int b = 0; b < KB; ++b)
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
                             if (i < n) {
                                 atomicAdd(&h0[kk[b][t] >> kDigit0Shift], 1u);
-                                if (cached) cache[i] = kk[b][t];
+                                if constexpr (MODE == kCached)
+                                    if (cached) cache[i] = kk[b][t];
                             }
                         }
                 }
@@ -390,9 +400,9 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
             if (bin >= 0) {
                 // one pass over the row: emit above, keep ties
                 for (int64_t r0 = 0; r0 < n; r0 += ROUND) {
-                    uint32_t kk[kB][4];
+                    uint32_t kk[KB][4];
 #pragma unroll
-                    for (int b = 0; b < kB; ++b) {
+                    for (int b = 0; b < KB; ++b) {
                         const int64_t i = r0 + 4 * ((int64_t)b * NT + tid);
                         if (cached) {
 #pragma unroll
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
                         }
                     }
 #pragma unroll
-                    for (int b = 0; b < kB; ++b)
+                    for (int b = 0; b < KB; ++b)
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
@@ -411,7 +421,7 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
                             const bool up = ok && dg > bin;
                             emit(up, up ? out_id(c.row, q, i) : 0, out, &sh.cnt[0]);
                             const bool tie = ok && dg == bin;
-                            push_tie(tie, kk[b][t], tie ? out_id(c.row, q, i) : 0, ck, ci, &sh.cnt[1]);
+                            push_tie<CAP>(tie, kk[b][t], tie ? out_id(c.row, q, i) : 0, ck, ci, &sh.cnt[1]);
                         }
                 }
                 __syncthreads();
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
                 const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
                 const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
                 const uint32_t need = (uint32_t)(K - above);
-                if (nc <= kCandCap) {
+                if (nc <= CAP) {
                     finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
                 } else if (cached) {
                     finish_levels<NT>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, sh);
@@ -431,6 +441,38 @@ __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
     }
     for (int i = K + tid; i < c.k; i += NT) out[i] = -1;
     if (tid == 0) c.count[q] = K;
+}
+
+template <bool HIST, int MODE>
+__global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
+{
+    select_query<HIST, MODE>(c, ws);
+}
+
+// Streaming mode: its LDS footprint lets two 1024-thread workgroups share a
+// CU once the registers fit 8 waves per SIMD.
+template <bool HIST>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void k_select_stream(SelCall c,
+                                                                                            SelWorkspace ws)
+{
+    select_query<HIST, kStream>(c, ws);
+}
+
+template <bool HIST>
+hipError_t launch_k_select(const SelCall &c, const SelWorkspace &ws, hipStream_t s)
+{
+    if (c.max_n <= kCandCap) {
+        hipLaunchKernelGGL((k_select<HIST, kSmall>), dim3(c.Q), dim3(NT), 0, s, c, ws);
+        return hipGetLastError();
+    }
+    if constexpr (!HIST) {
+        if (c.max_n <= kKeyCache) {
+            hipLaunchKernelGGL((k_select<HIST, kCached>), dim3(c.Q), dim3(NT), 0, s, c, ws);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_select_stream<HIST>), dim3(c.Q), dim3(NT), 0, s, c, ws);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -663,11 +705,7 @@ hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_his
         hipLaunchKernelGGL(k_final, dim3(c.Q, c.k_inner > 0 ? 2 : 1), dim3(NT), 0, s, c, ws);
         return hipGetLastError();
     }
-    if (have_hist)
-        hipLaunchKernelGGL(k_select<true>, dim3(c.Q), dim3(NT), 0, s, c, ws);
-    else
-        hipLaunchKernelGGL(k_select<false>, dim3(c.Q), dim3(NT), 0, s, c, ws);
-    hipError_t e = hipGetLastError();
+    hipError_t e = have_hist ? launch_k_select<true>(c, ws, s) : launch_k_select<false>(c, ws, s);
     if (e != hipSuccess || c.k_inner <= 0) return e;
     // Nested selection among the outer winners (a subset by construction).
     SelCall ic = c;
@@ -682,8 +720,7 @@ hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_his
     ic.k_inner = 0;
     ic.idx_inner = nullptr;
     ic.count_inner = nullptr;
-    hipLaunchKernelGGL(k_select<false>, dim3(c.Q), dim3(NT), 0, s, ic, ws);
-    return hipGetLastError();
+    return launch_k_select<false>(ic, ws, s);
 }
 
 } // namespace li

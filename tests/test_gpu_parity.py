@@ -385,3 +385,24 @@ def test_hs_nested_selection_on_a_shared_tie_digit():
     assert int(h.host(anchor.count)[0]) == 4096 and int(h.host(anchor.count_inner)[0]) == 2048
     assert len(inner) == 2048 and inner <= outer
     verify_hs(g, anchor, followers, M=4096, k=2048, tag="nested")
+
+
+def test_many_queries_rows_between_8k_and_16k():
+    """Prefill-style selection whose rows fit the LDS key cache (8K < n <= 16K),
+    with a run of equal scores at the threshold."""
+    h = H()
+    say("many queries, 8K-16K rows")
+    g = synth.make_decode("mid", 58, B=2, lens=[12000, 9000], r=256, H=64, d=128, k=2048, M=4096)
+    Q = 40
+    g.qseq = np.array([i % 2 for i in range(Q)], dtype=np.int32)
+    rng = np.random.default_rng(11)
+    g.qpos = np.array([rng.integers(8500, int(g.lens[b])) for b in g.qseq], dtype=np.int32)
+    g.qpos[:2] = g.lens - 1
+    g.latent[1][:5000] = g.latent[1][5000]  # 5001 identical rows in sequence 1
+    for l in range(g.G):
+        g.q[l] = synth.round_bf16(np.random.default_rng(300 + l).standard_normal((Q, g.H, g.d)).astype(np.float32))
+        g.w[l] = synth.softplus(np.random.default_rng(400 + l).standard_normal((Q, g.H)).astype(np.float32))
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    for l in (0, 1):
+        verify_full(g, l, h.full_layer(g, cache, qs, l), tag="mid")
