@@ -48,7 +48,7 @@ def build(force: bool = True) -> str:
     """Compile li_oracle.c with gcc (OpenMP) into liboracle.so."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC,
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", _SRC,
                                "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -76,6 +76,21 @@ def _bind(lib):
     lib.lio_topk.restype = _i64
     lib.lio_threads.argtypes = []
     lib.lio_threads.restype = ctypes.c_int
+    u8 = ctypes.c_uint8
+    _u8p = ctypes.POINTER(u8)
+    _fp = ctypes.POINTER(ctypes.c_float)
+    lib.lio_e4m3_decode.argtypes = [u8]
+    lib.lio_e4m3_decode.restype = ctypes.c_double
+    lib.lio_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.lio_e4m3_encode.restype = u8
+    lib.lio_wht128.argtypes = [_fp]
+    lib.lio_wht128.restype = None
+    lib.lio_pow2_exponent.argtypes = [ctypes.c_float]
+    lib.lio_pow2_exponent.restype = ctypes.c_int
+    lib.lio_quantize_rows.argtypes = [_fp, _i64, _i64, _u8p, _fp]
+    lib.lio_quantize_rows.restype = None
+    lib.lio_score_fp8.argtypes = [_u8p, _fp, _dp, _u8p, _fp, _ip, _i64, _i64, _i64, _dp]
+    lib.lio_score_fp8.restype = None
     return lib
 
 
@@ -177,6 +192,89 @@ def topk(s: np.ndarray, K: int, pos: Optional[np.ndarray] = None) -> np.ndarray:
         if got != K:
             raise MemoryError("oracle top-k allocation failed")
     return out
+
+
+# ----------------------------------------------------------------------------
+# Segmented FP8 (reading of §A.2 / §B.2; see li_oracle.c)
+# ----------------------------------------------------------------------------
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_fp = ctypes.POINTER(ctypes.c_float)
+SEGMENT = 128
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (fp64) of OCP E4M3 codes."""
+    c = np.asarray(codes, dtype=np.uint8)
+    L = _load()
+    flat = np.array([L.lio_e4m3_decode(int(x)) for x in c.ravel()], dtype=np.float64)
+    return flat.reshape(c.shape)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 codes of fp32 values (ties to even, saturating at 448)."""
+    x = np.asarray(v, dtype=np.float32)
+    L = _load()
+    flat = np.array([L.lio_e4m3_encode(float(a)) for a in x.ravel()], dtype=np.uint8)
+    return flat.reshape(x.shape)
+
+
+def wht128(x) -> np.ndarray:
+    """Orthonormal Walsh-Hadamard transform of one 128-vector, in fp32."""
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    assert y.shape == (SEGMENT,)
+    _load().lio_wht128(_ptr(y, _fp))
+    return y
+
+
+def pow2_exponent(amax: float) -> int:
+    """Smallest e with amax * 2^-e <= 448 (0 for amax = 0), clamped to [-120, 120]."""
+    return int(_load().lio_pow2_exponent(float(np.float32(amax))))
+
+
+def quantize_rows(x) -> tuple:
+    """Rows [..., r] (fp32, r a multiple of 128) -> (codes [..., r] uint8,
+    scales [..., r/128] fp32 powers of two)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    r = x.shape[-1]
+    assert r % SEGMENT == 0
+    lead = x.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    codes = np.empty(lead + (r,), dtype=np.uint8)
+    scales = np.empty(lead + (r // SEGMENT,), dtype=np.float32)
+    if rows:
+        _load().lio_quantize_rows(_ptr(x, _fp), rows, r, _ptr(codes, _u8p), _ptr(scales, _fp))
+    return codes, scales
+
+
+def score_fp8(qc, qs, w, cc, cs, n: Optional[int] = None, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Scores from FP8 operands: qc [H][r] codes, qs [H][r/128], w [H],
+    cc [*][r] codes, cs [*][r/128]; rows 0..n-1 or the given ``rows``."""
+    qc = np.ascontiguousarray(qc, dtype=np.uint8)
+    qs = np.ascontiguousarray(qs, dtype=np.float32)
+    w = _f64(w)
+    cc = np.ascontiguousarray(cc, dtype=np.uint8)
+    cs = np.ascontiguousarray(cs, dtype=np.float32)
+    H, r = qc.shape
+    assert cc.shape[1] == r and qs.shape == (H, r // SEGMENT) and cs.shape[1] == r // SEGMENT
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < cc.shape[0])
+        m = rows.size
+        rp = _ptr(rows, _ip)
+    else:
+        m = cc.shape[0] if n is None else int(n)
+        rp = None
+    out = np.empty(m, dtype=np.float64)
+    if m:
+        _load().lio_score_fp8(_ptr(qc, _u8p), _ptr(qs, _fp), _ptr(w, _dp), _ptr(cc, _u8p), _ptr(cs, _fp), rp, m,
+                              H, r, _ptr(out, _dp))
+    return out
+
+
+def absorb_fp8(q: np.ndarray, W: np.ndarray) -> tuple:
+    """Absorbed query in FP8: qt = q W (fp64, then rounded once to fp32),
+    rotated and quantized per 128-element segment."""
+    return quantize_rows(absorb(q, W).astype(np.float32))
 
 
 # ----------------------------------------------------------------------------

@@ -146,6 +146,133 @@ int64_t lio_topk(const double *s, const int32_t *pos, int64_t m, int64_t K, int3
     return K;
 }
 
+/*
+ * Segmented FP8 storage and scoring (§B.2: the indexer runs in segmented
+ * FP8; §A.2: queries are absorbed before the Hadamard rotation, i.e. the
+ * rotation is applied to both sides ahead of quantization).  The pages give
+ * neither formats nor segment sizes; the reading implemented here:
+ *   - each 128-element segment of a row is rotated by the orthonormal
+ *     Walsh-Hadamard transform (fp32 butterflies, strides 1, 2, ..., 64,
+ *     then a multiply by the fp32 value of 1/sqrt(128));
+ *   - the segment gets a power-of-two scale 2^e, e the smallest integer
+ *     with amax * 2^-e <= 448 (clamped to [-120, 120]);
+ *   - every element becomes an OCP FP8 E4M3 code of x * 2^-e, rounded to
+ *     nearest-even and saturated at 448.
+ * Rotation is orthonormal, so the score of the rotated, unquantized rows
+ * equals the plain score; quantization is the only approximation.
+ */
+
+/* Value of an OCP E4M3 code: 1 sign, 4 exponent (bias 7), 3 mantissa bits. */
+double lio_e4m3_decode(uint8_t c)
+{
+    const int ex = (c >> 3) & 15, m = c & 7;
+    const double v = ex == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), ex - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 code (ties to even mantissa); magnitudes of 448 and above
+ * become 448.  v must not be NaN. */
+uint8_t lio_e4m3_encode(float v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const float a = fabsf(v);
+    if (!(a > 0.0f)) return sign;
+    if (a >= 448.0f) return sign | 0x7E;
+    int E;
+    frexpf(a, &E);           /* a = f 2^E, f in [0.5, 1) */
+    const int e = E - 1;     /* floor(log2 a) */
+    if (e < -6) {            /* below the smallest normal: steps of 2^-9 */
+        const float n = rintf(ldexpf(a, 9));
+        return sign | (uint8_t)n;      /* n = 8 is the smallest normal, code 8 */
+    }
+    int m = (int)rintf(ldexpf(a, 3 - e)); /* 8 .. 16 */
+    int ee = e;
+    if (m == 16) {
+        m = 8;
+        ee += 1;
+    }
+    return sign | (uint8_t)(((ee + 7) << 3) | (m - 8));
+}
+
+/* In-place orthonormal Walsh-Hadamard transform of 128 floats (fp32). */
+void lio_wht128(float *x)
+{
+    for (int h = 1; h < 128; h <<= 1)
+        for (int i = 0; i < 128; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                const float a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+    const float k = 0.08838834764831845f; /* 1/sqrt(128) */
+    for (int j = 0; j < 128; ++j)
+        x[j] = x[j] * k;
+}
+
+/* Smallest e with amax * 2^-e <= 448 (0 for amax == 0), clamped. */
+int lio_pow2_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int E;
+    const float f = frexpf(amax, &E); /* amax = (2f) 2^(E-1), 2f in [1, 2) */
+    int e = (2.0f * f <= 1.75f) ? E - 9 : E - 8;
+    if (e < -120) e = -120;
+    if (e > 120) e = 120;
+    return e;
+}
+
+/* Rows [rows][r] (r a multiple of 128) -> codes [rows][r] and one scale
+ * per (row, segment), [rows][r/128]. */
+void lio_quantize_rows(const float *x, int64_t rows, int64_t r, uint8_t *codes, float *scales)
+{
+    const int64_t nseg = r / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t g = 0; g < nseg; ++g) {
+            float y[128];
+            for (int t = 0; t < 128; ++t)
+                y[t] = x[i * r + g * 128 + t];
+            lio_wht128(y);
+            float amax = 0.0f;
+            for (int t = 0; t < 128; ++t)
+                amax = fmaxf(amax, fabsf(y[t]));
+            const int e = lio_pow2_exponent(amax);
+            scales[i * nseg + g] = ldexpf(1.0f, e);
+            for (int t = 0; t < 128; ++t)
+                codes[i * r + g * 128 + t] = lio_e4m3_encode(ldexpf(y[t], -e));
+        }
+    }
+}
+
+/*
+ * Score from FP8 rows (§3.1 score on the rotated, quantized operands):
+ *   s[i] = sum_h w[h] max(0, sum_g qs[h][g] cs[row_i][g]
+ *                                 sum_{t in segment g} dec(qc[h][t]) dec(cc[row_i][t]))
+ * qc: [H][r] codes, qs: [H][r/128]; cc: [*][r] codes, cs: [*][r/128];
+ * row_i = rows[i] when rows != NULL, else i.
+ */
+void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const uint8_t *cc, const float *cs,
+                   const int32_t *rows, int64_t m, int64_t H, int64_t r, double *s)
+{
+    const int64_t nseg = r / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const int64_t row = rows ? (int64_t)rows[i] : i;
+        double total = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double dot = 0.0;
+            for (int64_t g = 0; g < nseg; ++g) {
+                double seg = 0.0;
+                for (int t = 0; t < 128; ++t)
+                    seg += lio_e4m3_decode(qc[h * r + g * 128 + t]) * lio_e4m3_decode(cc[row * r + g * 128 + t]);
+                dot += (double)qs[h * nseg + g] * (double)cs[row * nseg + g] * seg;
+            }
+            total += w[h] * (dot > 0.0 ? dot : 0.0);
+        }
+        s[i] = total;
+    }
+}
+
 /* Number of threads the OpenMP loops above run with in this process. */
 int lio_threads(void)
 {

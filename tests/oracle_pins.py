@@ -329,4 +329,168 @@ def pin_storage_accounting():
     assert round(100.0 * (1 - grouped / dsa), 1) == g["reduction_pct_1dp"]
 
 
+# ----------------------------------------------------------------------------
+# Segmented FP8 (OCP E4M3 codes, Walsh-Hadamard rotation, power-of-two scales)
+# ----------------------------------------------------------------------------
+def _finite_codes():
+    return np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _e4m3_value(c: int) -> float:
+    """Value of a code straight from the format definition (independent of the oracle)."""
+    s = -1.0 if c & 0x80 else 1.0
+    E, m = (c >> 3) & 15, c & 7
+    return s * (m / 8.0 * 2.0 ** -6 if E == 0 else (1.0 + m / 8.0) * 2.0 ** (E - 7))
+
+
+def pin_e4m3_code_table():
+    g = _golden("worked_fp8.json")
+    for c, v in g["code_values"]:
+        got = float(oracle.e4m3_decode([c])[0])
+        assert got == v and np.signbit(got) == np.signbit(v), (c, got, v)
+    codes = _finite_codes()
+    vals = oracle.e4m3_decode(codes)
+    assert all(vals[i] == _e4m3_value(int(c)) for i, c in enumerate(codes))
+
+
+def pin_e4m3_encode_worked_cases():
+    g = _golden("worked_fp8.json")
+    for v, c, why in g["encode_cases"]:
+        got = int(oracle.e4m3_encode([v])[0])
+        assert got == c, (v, got, c, why)
+
+
+def pin_e4m3_roundtrip():
+    codes = _finite_codes()
+    vals = oracle.e4m3_decode(codes).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def pin_e4m3_encode_brute_force():
+    """Nearest code by exhaustive search, ties to the even mantissa, saturation at 448."""
+    codes = _finite_codes()
+    table = np.array([_e4m3_value(int(c)) for c in codes])
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(400) * 10.0 ** rng.uniform(-4, 3, 400),
+                        (rng.integers(-3000, 3000, 300) / 8.0) * 2.0 ** rng.integers(-12, 6, 300)]).astype(np.float32)
+    got = oracle.e4m3_encode(x)
+    for v, c in zip(x.astype(np.float64), got):
+        if abs(v) >= 448.0:
+            want = 0xFE if v < 0 else 0x7E
+        else:
+            d = np.abs(table - v)
+            best = np.flatnonzero(d == d.min())
+            cand = [int(codes[i]) for i in best]
+            if len(cand) > 1:  # a tie: keep codes of the sign of v, then the even mantissa
+                same = [k for k in cand if bool(k & 0x80) == bool(np.signbit(v))] or cand
+                cand = [k for k in same if (k & 7) % 2 == 0] or same
+            want = cand[0]
+        assert _e4m3_value(int(c)) == _e4m3_value(want), (float(v), int(c), want)
+
+
+def pin_wht_is_the_normalized_hadamard_matrix():
+    """Sylvester Hadamard matrix / sqrt(128), to fp32 accuracy; orthonormal and self-inverse."""
+    Hm = np.array([[1.0]])
+    while Hm.shape[0] < 128:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    Hm /= np.sqrt(128.0)
+    rng = np.random.default_rng(8)
+    for _ in range(5):
+        x = rng.standard_normal(128).astype(np.float32)
+        y = oracle.wht128(x)
+        ref = Hm @ x.astype(np.float64)
+        assert np.max(np.abs(y - ref)) <= 1e-5 * (1 + np.max(np.abs(ref))), np.max(np.abs(y - ref))
+        back = oracle.wht128(y)
+        assert np.max(np.abs(back - x)) <= 1e-5 * (1 + np.max(np.abs(x)))
+        assert abs(np.linalg.norm(y.astype(np.float64)) - np.linalg.norm(x.astype(np.float64))) <= 1e-5 * np.linalg.norm(x)
+
+
+def pin_pow2_exponent():
+    g = _golden("worked_fp8.json")
+    for a, e in g["pow2_cases"]:
+        assert oracle.pow2_exponent(a) == e, (a, oracle.pow2_exponent(a), e)
+    rng = np.random.default_rng(9)
+    for a in (10.0 ** rng.uniform(-20, 20, 300)).astype(np.float32):
+        e = oracle.pow2_exponent(a)
+        assert float(a) * 2.0 ** -e <= 448.0 < float(a) * 2.0 ** -(e - 1), (a, e)
+
+
+def pin_quantize_worked_examples():
+    g = _golden("worked_fp8.json")
+    row = np.zeros((1, 128), np.float32)
+    row[0, 0] = 1.0
+    c, s = oracle.quantize_rows(row)
+    ex = g["quantize_e0"]
+    assert s[0, 0] == ex["scale"] == 2.0 ** ex["exponent"] and np.all(c == ex["code"]), (s, c[0, :4])
+    row[0, 1] = 1.0
+    c, s = oracle.quantize_rows(row)
+    ex = g["quantize_e0_e1"]
+    assert s[0, 0] == 2.0 ** ex["exponent"]
+    assert np.all(c[0, 0::2] == ex["code_even"]) and np.all(c[0, 1::2] == ex["code_odd"])
+    # two segments are quantized independently
+    two = np.zeros((1, 256), np.float32)
+    two[0, 0], two[0, 128] = 1.0, 4.0
+    c2, s2 = oracle.quantize_rows(two)
+    assert s2[0, 0] == 2.0 ** -12 and s2[0, 1] == 2.0 ** -10 and np.all(c2 == 123)
+
+
+def pin_quantization_error_bound():
+    """Each dequantized element is within half a step of its rotated value."""
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((6, 256)) * rng.uniform(0.01, 100, (6, 1))).astype(np.float32)
+    c, s = oracle.quantize_rows(x)
+    for i in range(6):
+        for gseg in range(2):
+            y = oracle.wht128(x[i, gseg * 128:(gseg + 1) * 128]).astype(np.float64)
+            d = oracle.e4m3_decode(c[i, gseg * 128:(gseg + 1) * 128]) * float(s[i, gseg])
+            step = np.maximum(np.abs(y) * 2.0 ** -3, 2.0 ** -9 * float(s[i, gseg]))
+            assert np.all(np.abs(d - y) <= step / 2 * (1 + 1e-12)), np.max(np.abs(d - y) / step)
+            assert np.max(np.abs(d)) <= 448.0 * float(s[i, gseg])
+
+
+def pin_fp8_score_worked_case():
+    g = _golden("worked_fp8.json")["score_case"]
+    e0 = np.zeros((1, 128), np.float32)
+    e0[0, 0] = 1.0
+    qc, qs = oracle.quantize_rows(e0)
+    cc_pos, cs_pos = oracle.quantize_rows(e0)
+    cc_neg, cs_neg = oracle.quantize_rows(-e0)
+    cc = np.concatenate([cc_pos, cc_neg])
+    cs = np.concatenate([cs_pos, cs_neg])
+    s = oracle.score_fp8(qc, qs, np.array(g["w"]), cc, cs)
+    assert s[0] == g["score_pos"] and s[1] == g["score_neg"], s
+
+
+def pin_fp8_score_is_plain_score_of_dequantized_rows():
+    """Reduces to the (pinned) plain scorer on the dequantized, scaled rows."""
+    rng = np.random.default_rng(11)
+    H, r, n = 5, 256, 40
+    q = rng.standard_normal((H, r)).astype(np.float32)
+    C = rng.standard_normal((n, r)).astype(np.float32)
+    w = rng.uniform(-1, 1, H)
+    qc, qs = oracle.quantize_rows(q)
+    cc, cs = oracle.quantize_rows(C)
+    qd = oracle.e4m3_decode(qc) * np.repeat(qs.astype(np.float64), 128, axis=1)
+    cd = oracle.e4m3_decode(cc) * np.repeat(cs.astype(np.float64), 128, axis=1)
+    want = oracle.score(qd, w, cd)
+    got = oracle.score_fp8(qc, qs, w, cc, cs)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.max(np.abs(want))), np.max(np.abs(got - want))
+    rows = np.array([7, 3, 39, 0], dtype=np.int32)
+    assert np.array_equal(oracle.score_fp8(qc, qs, w, cc, cs, rows=rows), got[rows])
+
+
+def pin_rotation_keeps_the_score():
+    """The orthonormal rotation alone changes no score beyond fp32 rounding."""
+    rng = np.random.default_rng(12)
+    H, r, n = 4, 256, 30
+    q = rng.standard_normal((H, r)).astype(np.float32)
+    C = rng.standard_normal((n, r)).astype(np.float32)
+    w = rng.uniform(0, 1, H)
+    rot = lambda a: np.concatenate([oracle.wht128(a[g * 128:(g + 1) * 128]) for g in range(2)])
+    qr = np.stack([rot(x) for x in q])
+    cr = np.stack([rot(x) for x in C])
+    a, b = oracle.score(q, w, C), oracle.score(qr, w, cr)
+    assert np.max(np.abs(a - b)) <= 1e-4 * (1 + np.max(np.abs(a)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -36,6 +36,16 @@ C_MUTANTS = {
                        "if (x->s > y->s) return 1;\n    if (x->s < y->s) return -1;"),
     "topk_tiebreak_reversed": ("return (x->p > y->p) - (x->p < y->p);", "return (x->p < y->p) - (x->p > y->p);"),
     "topk_drops_position_map": ("e[i].p = pos ? pos[i] : (int32_t)i;", "e[i].p = (int32_t)i;"),
+    "e4m3_truncates": ("int m = (int)rintf(ldexpf(a, 3 - e));", "int m = (int)truncf(ldexpf(a, 3 - e));"),
+    "e4m3_no_saturation": ("if (a >= 448.0f) return sign | 0x7E;", "if (a >= 480.0f) return sign | 0x7E;"),
+    "e4m3_subnormal_step": ("const float n = rintf(ldexpf(a, 9));", "const float n = rintf(ldexpf(a, 8));"),
+    "wht_unnormalized": ("const float k = 0.08838834764831845f;", "const float k = 1.0f;"),
+    "wht_wrong_sign": ("x[j + h] = a - b;", "x[j + h] = b - a;"),
+    "pow2_off_by_one": ("int e = (2.0f * f <= 1.75f) ? E - 9 : E - 8;", "int e = (2.0f * f <= 1.75f) ? E - 8 : E - 8;"),
+    "fp8_score_drops_scales": ("dot += (double)qs[h * nseg + g] * (double)cs[row * nseg + g] * seg;",
+                               "dot += seg;"),
+    "fp8_score_relu_after_sum": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;\n    }\n}\n\n/* Number",
+                                 "total += w[h] * dot;\n        }\n        s[i] = total > 0.0 ? total : 0.0;\n    }\n}\n\n/* Number"),
 }
 
 
@@ -62,7 +72,8 @@ def test_pins_catch_c_mutant(name, mutant_dir):
     msrc = mutant_dir / f"{name}.c"
     msrc.write_text(src.replace(old, new, 1))
     so = mutant_dir / f"{name}.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(msrc), "-o", str(so), "-lm"])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", str(msrc), "-o",
+                           str(so), "-lm"])
     oracle.use_library(str(so))
     try:
         failed = _run_pins()
