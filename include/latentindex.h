@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LI_ABI_VERSION 1
+#define LI_ABI_VERSION 2
 #define LI_API __attribute__((visibility("default")))
 #define LI_PAGE_SIZE 64      /* rows per cache page                        */
 #define LI_MAX_HEADS 64      /* indexer heads per query                    */
@@ -58,7 +58,17 @@ typedef enum {
     LI_ERR_HIP = 5          /* a HIP launch failed                           */
 } li_status;
 
-typedef enum { LI_BF16 = 0, LI_FP32 = 1 } li_dtype;
+/*
+ * LI_FP8: segmented FP8 (§B.2: the indexer runs in segmented FP8; §A.2: the
+ * decoder is absorbed before the Hadamard rotation).  The pages fix no
+ * format; the one implemented: each 128-element segment of a row is rotated
+ * by the orthonormal Walsh-Hadamard transform (fp32, butterfly strides 1..64,
+ * then x fp32(1/sqrt(128))), given the power-of-two scale 2^e with e the
+ * smallest integer such that amax 2^-e <= 448 (clamped to [-120, 120]), and
+ * stored as OCP FP8 E4M3 codes of x 2^-e (round to nearest even, saturating
+ * at 448).  r must be 128 or 256.
+ */
+typedef enum { LI_BF16 = 0, LI_FP32 = 1, LI_FP8 = 2 } li_dtype;
 
 /*
  * Shared latent cache of one layer group (§3.1: one cache per group, rows
@@ -68,8 +78,12 @@ typedef enum { LI_BF16 = 0, LI_FP32 = 1 } li_dtype;
  *               slot j%64.
  *   block_table [batch][max_pages] int32 physical page ids.
  *   seq_lens    [batch] int32 rows present per sequence (after appends).
+ *   scales      LI_FP8 only: [num_pages][page_size][r/128] fp32 segment
+ *               scales (powers of two) beside the E4M3 codes in pool;
+ *               NULL for the other dtypes.
  * page_size must be LI_PAGE_SIZE.  r in {64, 128, 256} for LI_BF16,
- * 1..256 for LI_FP32.  A contiguous cache is the identity block table.
+ * 1..256 for LI_FP32, {128, 256} for LI_FP8.  A contiguous cache is the
+ * identity block table.
  */
 typedef struct {
     void *pool;
@@ -81,6 +95,7 @@ typedef struct {
     int32_t num_pages;
     int32_t r;
     li_dtype dtype;
+    float *scales;
 } li_cache;
 
 /*
@@ -100,9 +115,11 @@ typedef struct {
 /*
  * append_latent — the anchor writes T new latent rows into the group cache
  * (§3.1: the shared representation is cached once per group; followers only
- * read it).  rows [T][r] of the cache dtype; row t goes to sequence seq[t],
- * logical position pos[t].  Rows are copied bit-exactly.  Updating
- * seq_lens is the caller's job.  Rows that target the same slot race.
+ * read it).  rows [T][r] of the cache dtype (bf16 for LI_FP8 caches); row t
+ * goes to sequence seq[t], logical position pos[t].  Rows are copied
+ * bit-exactly (LI_FP8: rotated and quantized per segment, codes and scale
+ * written to the slot).  Updating seq_lens is the caller's job.  Rows that
+ * target the same slot race.
  */
 LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const int32_t *seq,
                            const int32_t *pos, int32_t T, hipStream_t stream);
@@ -115,13 +132,23 @@ LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const
  * LI_BF16: bf16 inputs, fp32 accumulation, one round-to-nearest-even to bf16.
  * LI_FP32: fp32 throughout.  H <= 64; r in {64,128,256} and d in
  * {32,64,128,256} for LI_BF16; r in 1..256 and d in 1..1024 for LI_FP32.
+ * LI_FP8: bf16 inputs, fp32 accumulation, then each (query, head) segment is
+ * rotated and quantized as the cache is (LI_FP8 above); q_tilde is then one
+ * buffer of li_fp8_query_bytes(Q, H, r) bytes holding the codes [Q][H][r]
+ * followed, at byte offset li_fp8_query_scale_offset(Q, H, r), by the
+ * scales [Q][H][r/128] fp32.  r in {128, 256}, d in {32,64,128,256}.
  */
 LI_API li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32_t Q, int32_t H,
                           int32_t d, int32_t r, li_dtype dtype, hipStream_t stream);
 
+/* Size and scale offset of an LI_FP8 query buffer (0 for invalid sizes). */
+LI_API size_t li_fp8_query_bytes(int32_t Q, int32_t H, int32_t r);
+LI_API size_t li_fp8_query_scale_offset(int32_t Q, int32_t H, int32_t r);
+
 /*
  * score_topk — full-prefix scoring and per-query top-k (§3.1, §4.1).
- *   q_tilde [Q][H][r] absorbed queries (cache dtype); w [Q][H] fp32 head
+ *   q_tilde [Q][H][r] absorbed queries (cache dtype; for an LI_FP8 cache the
+ *           FP8 query buffer of li_absorb_query); w [Q][H] fp32 head
  *   weights (any sign).  scores[i][j] = sum_h w[i][h] max(0, q_tilde[i][h] . c_j)
  *   for j < n_i, accumulated in fp32.
  *   idx     [Q][k] out: the set of the min(k, n_i) highest-scoring positions
@@ -155,6 +182,7 @@ LI_API li_status li_score_topk(const li_cache *cache, const li_queries *queries,
  *              best candidates (unordered, -1 padded); count [Q] out.
  *   cand_scores [Q][M] fp32 out (optional): the follower's candidate scores.
  *   ws         at least li_workspace_bytes(LI_OP_HS_SELECT, ...).
+ * q_tilde as for li_score_topk (the FP8 query buffer for an LI_FP8 cache).
  */
 LI_API li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
                        const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w,

@@ -19,11 +19,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblatentindex.so")
 
 LI_OK, LI_ERR_NULL, LI_ERR_SHAPE, LI_ERR_UNSUPPORTED, LI_ERR_WORKSPACE, LI_ERR_HIP = range(6)
-LI_BF16, LI_FP32 = 0, 1
+LI_BF16, LI_FP32, LI_FP8 = 0, 1, 2
 LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
 EXPORTED = ["li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select", "li_workspace_bytes",
-            "li_timing_enable", "li_timing_read", "li_status_str", "li_last_error", "li_abi_version"]
+            "li_fp8_query_bytes", "li_fp8_query_scale_offset", "li_timing_enable", "li_timing_read", "li_status_str",
+            "li_last_error", "li_abi_version"]
 (LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
  LI_KERNEL_APPEND) = range(6)
 
@@ -37,7 +38,8 @@ class LIError(RuntimeError):
 class _Cache(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("r", ctypes.c_int32), ("dtype", ctypes.c_int)]
+                ("num_pages", ctypes.c_int32), ("r", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("scales", ctypes.c_void_p)]
 
 
 class _Queries(ctypes.Structure):
@@ -63,6 +65,9 @@ def lib():
         L.li_hs_select.argtypes = [cp, qp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.li_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32]
         L.li_workspace_bytes.restype = sz
+        for f in ("li_fp8_query_bytes", "li_fp8_query_scale_offset"):
+            getattr(L, f).argtypes = [i32, i32, i32]
+            getattr(L, f).restype = sz
         L.li_status_str.argtypes = [ctypes.c_int]
         L.li_status_str.restype = ctypes.c_char_p
         L.li_last_error.argtypes = []
@@ -125,23 +130,35 @@ def _li_dtype(dt) -> int:
 class LatentCache:
     """Paged shared latent cache of one layer group (caller-owned tensors).
 
-    pool [num_pages][64][r] (bf16 or fp32), block_table [batch][max_pages]
-    int32, seq_lens [batch] int32.
+    pool [num_pages][64][r] (bf16 or fp32; uint8 E4M3 codes for a segmented
+    FP8 cache, which then needs scales [num_pages][64][r/128] float32),
+    block_table [batch][max_pages] int32, seq_lens [batch] int32.
     """
     pool: torch.Tensor
     block_table: torch.Tensor
     seq_lens: torch.Tensor
+    scales: Optional[torch.Tensor] = None
 
     def __post_init__(self):
         if self.pool.dim() != 3 or self.pool.shape[1] != PAGE_SIZE:
             raise ValueError("pool must be [num_pages][64][r]")
         _need(self.pool, "pool", self.pool.dtype)
-        _li_dtype(self.pool.dtype)
         dev = self.pool.device
+        if self.pool.dtype == torch.uint8:
+            if self.scales is None:
+                raise ValueError("an FP8 cache needs scales [num_pages][64][r/128]")
+            _need(self.scales, "scales", torch.float32, dev,
+                  (self.pool.shape[0], PAGE_SIZE, self.pool.shape[2] // 128))
+        else:
+            _li_dtype(self.pool.dtype)
         _need(self.block_table, "block_table", torch.int32, dev)
         _need(self.seq_lens, "seq_lens", torch.int32, dev)
         if self.block_table.dim() != 2 or self.seq_lens.shape != (self.block_table.shape[0],):
             raise ValueError("block_table must be [batch][max_pages] and seq_lens [batch]")
+
+    @property
+    def fp8(self) -> bool:
+        return self.pool.dtype == torch.uint8
 
     @property
     def device(self):
@@ -158,7 +175,32 @@ class LatentCache:
     def desc(self) -> _Cache:
         return _Cache(self.pool.data_ptr(), self.block_table.data_ptr(), self.seq_lens.data_ptr(),
                       int(self.block_table.shape[0]), int(self.block_table.shape[1]), PAGE_SIZE,
-                      int(self.pool.shape[0]), self.r, _li_dtype(self.pool.dtype))
+                      int(self.pool.shape[0]), self.r, LI_FP8 if self.fp8 else _li_dtype(self.pool.dtype),
+                      self.scales.data_ptr() if self.fp8 else None)
+
+
+class Fp8Query:
+    """Absorbed queries in segmented FP8: one uint8 buffer holding the codes
+    [Q][H][r] and, at li_fp8_query_scale_offset, the scales [Q][H][r/128]."""
+
+    def __init__(self, buf: torch.Tensor, Q: int, H: int, r: int):
+        self.buf, self.Q, self.H, self.r = buf, Q, H, r
+
+    @staticmethod
+    def nbytes(Q: int, H: int, r: int) -> int:
+        return int(lib().li_fp8_query_bytes(Q, H, r))
+
+    @staticmethod
+    def empty(Q: int, H: int, r: int, device) -> "Fp8Query":
+        return Fp8Query(torch.empty(max(Fp8Query.nbytes(Q, H, r), 1), dtype=torch.uint8, device=device), Q, H, r)
+
+    def codes(self) -> torch.Tensor:
+        return self.buf[:self.Q * self.H * self.r].view(self.Q, self.H, self.r)
+
+    def scales(self) -> torch.Tensor:
+        off = int(lib().li_fp8_query_scale_offset(self.Q, self.H, self.r))
+        n = self.Q * self.H * (self.r // 128)
+        return self.buf[off:off + 4 * n].view(torch.float32).view(self.Q, self.H, self.r // 128)
 
 
 def _queries(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int) -> _Queries:
@@ -194,8 +236,9 @@ def _workspace(device, nbytes: int, ws: Optional[torch.Tensor]) -> torch.Tensor:
 
 
 def append_latent(cache: LatentCache, rows: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor) -> None:
-    """li_append_latent: copy rows [T][r] into the pool at (seq[t], pos[t])."""
-    _need(rows, "rows", cache.dtype, cache.device)
+    """li_append_latent: copy rows [T][r] into the pool at (seq[t], pos[t])
+    (bf16 rows, rotated and quantized, for an FP8 cache)."""
+    _need(rows, "rows", torch.bfloat16 if cache.fp8 else cache.dtype, cache.device)
     _need(seq, "seq", torch.int32, cache.device)
     _need(pos, "pos", torch.int32, cache.device)
     T = int(rows.shape[0])
@@ -206,8 +249,9 @@ def append_latent(cache: LatentCache, rows: torch.Tensor, seq: torch.Tensor, pos
            "li_append_latent")
 
 
-def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """li_absorb_query: q [Q][H][d] x W_dec [d][r] -> q_tilde [Q][H][r]."""
+def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out=None, fp8: bool = False):
+    """li_absorb_query: q [Q][H][d] x W_dec [d][r] -> q_tilde [Q][H][r]
+    (an Fp8Query with fp8=True: bf16 inputs, rotated and quantized output)."""
     dev = q.device
     _need(q, "q", q.dtype, dev)
     dt = _li_dtype(q.dtype)
@@ -216,11 +260,37 @@ def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out: Optional[torch.Tenso
         raise ValueError("q must be [Q][H][d] and w_dec [d][r]")
     Q, H, d = (int(x) for x in q.shape)
     r = int(w_dec.shape[1])
+    if fp8:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("FP8 absorption takes bf16 q and w_dec")
+        if out is None:
+            out = Fp8Query.empty(Q, H, r, dev)
+        if not isinstance(out, Fp8Query) or (out.Q, out.H, out.r) != (Q, H, r):
+            raise ValueError("out must be an Fp8Query of the same shape")
+        _need(out.buf, "out", torch.uint8, dev)
+        if out.buf.numel() < Fp8Query.nbytes(Q, H, r):
+            raise ValueError("FP8 query buffer too small")
+        _check(lib().li_absorb_query(_ptr(q), _ptr(w_dec), _ptr(out.buf), Q, H, d, r, LI_FP8, _stream(dev)),
+               "li_absorb_query")
+        return out
     if out is None:
         out = torch.empty((Q, H, r), dtype=q.dtype, device=dev)
     _need(out, "out", q.dtype, dev, (Q, H, r))
     _check(lib().li_absorb_query(_ptr(q), _ptr(w_dec), _ptr(out), Q, H, d, r, dt, _stream(dev)), "li_absorb_query")
     return out
+
+
+def _query_operand(cache: LatentCache, q_tilde, Q: int):
+    """(H, device buffer) of the absorbed queries for this cache."""
+    if cache.fp8:
+        if not isinstance(q_tilde, Fp8Query) or q_tilde.Q != Q or q_tilde.r != cache.r:
+            raise ValueError("an FP8 cache is scored with the Fp8Query of absorb_query(..., fp8=True)")
+        _need(q_tilde.buf, "q_tilde", torch.uint8, cache.device)
+        return q_tilde.H, q_tilde.buf
+    _need(q_tilde, "q_tilde", cache.dtype, cache.device)
+    if q_tilde.dim() != 3 or q_tilde.shape[0] != Q or q_tilde.shape[2] != cache.r:
+        raise ValueError("q_tilde must be [Q][H][r]")
+    return int(q_tilde.shape[1]), q_tilde
 
 
 class TopK:
@@ -241,10 +311,7 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
     dev = cache.device
     qs = _queries(cache, seq, pos, max_valid)
     Q = qs.Q
-    _need(q_tilde, "q_tilde", cache.dtype, dev)
-    if q_tilde.dim() != 3 or q_tilde.shape[0] != Q or q_tilde.shape[2] != cache.r:
-        raise ValueError("q_tilde must be [Q][H][r]")
-    H = int(q_tilde.shape[1])
+    H, qbuf = _query_operand(cache, q_tilde, Q)
     _need(w, "w", torch.float32, dev, (Q, H))
     if out is None:
         out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
@@ -263,7 +330,7 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
     nb = workspace_bytes(op, Q, max_valid, H, cache.r, k, 0)
     ws = _workspace(dev, nb, ws)
     c = cache.desc()
-    _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(q_tilde), _ptr(w), H, k, _ptr(out.idx),
+    _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(qbuf), _ptr(w), H, k, _ptr(out.idx),
                                _ptr(out.count), k_inner, _ptr(out.idx_inner), _ptr(out.count_inner),
                                _ptr(out.scores), ld, _ptr(ws), ws.numel(), _stream(dev)), "li_score_topk")
     return out
@@ -281,10 +348,7 @@ def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_vali
         raise ValueError("cand must be [Q][M]")
     M = int(cand.shape[1])
     _need(cand_count, "cand_count", torch.int32, dev, (Q,))
-    _need(q_tilde, "q_tilde", cache.dtype, dev)
-    if q_tilde.dim() != 3 or q_tilde.shape[0] != Q or q_tilde.shape[2] != cache.r:
-        raise ValueError("q_tilde must be [Q][H][r]")
-    H = int(q_tilde.shape[1])
+    H, qbuf = _query_operand(cache, q_tilde, Q)
     _need(w, "w", torch.float32, dev, (Q, H))
     if out is None:
         out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
@@ -297,7 +361,7 @@ def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_vali
     nb = workspace_bytes(LI_OP_HS_SELECT, Q, 0, H, cache.r, k, M)
     ws = _workspace(dev, nb, ws)
     c = cache.desc()
-    _check(lib().li_hs_select(ctypes.byref(c), ctypes.byref(qs), _ptr(cand), _ptr(cand_count), M, _ptr(q_tilde),
+    _check(lib().li_hs_select(ctypes.byref(c), ctypes.byref(qs), _ptr(cand), _ptr(cand_count), M, _ptr(qbuf),
                               _ptr(w), H, k, _ptr(out.idx), _ptr(out.count), _ptr(out.scores), _ptr(ws),
                               ws.numel(), _stream(dev)), "li_hs_select")
     return out

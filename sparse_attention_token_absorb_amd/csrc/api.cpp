@@ -48,6 +48,7 @@ bool r_supported(int32_t r, li_dtype dt)
 {
     if (dt == LI_BF16) return r == 64 || r == 128 || r == 256;
     if (dt == LI_FP32) return r >= 1 && r <= 256;
+    if (dt == LI_FP8) return r == 128 || r == 256;
     return false;
 }
 
@@ -59,8 +60,10 @@ li_status check_cache(const li_cache *c)
     if (c->batch <= 0 || c->max_pages <= 0 || c->num_pages <= 0)
         return fail(LI_ERR_SHAPE, "batch %d, max_pages %d, num_pages %d must be positive", c->batch, c->max_pages,
                     c->num_pages);
-    if (c->dtype != LI_BF16 && c->dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)c->dtype);
+    if (c->dtype != LI_BF16 && c->dtype != LI_FP32 && c->dtype != LI_FP8)
+        return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)c->dtype);
     if (!r_supported(c->r, c->dtype)) return fail(LI_ERR_UNSUPPORTED, "latent width r=%d for dtype %d", c->r, (int)c->dtype);
+    if (c->dtype == LI_FP8 && !c->scales) return fail(LI_ERR_NULL, "FP8 cache without scales");
     return LI_OK;
 }
 
@@ -143,8 +146,12 @@ li_status li_append_latent(const li_cache *cache, const void *rows, const int32_
     hipError_t e;
     {
         li::TimedScope ts(LI_KERNEL_APPEND, stream);
-        e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos, T,
-                              stream);
+        if (cache->dtype == LI_FP8)
+            e = li::launch_append_fp8(cache->pool, cache->scales, cache->block_table, cache->max_pages, cache->r, rows,
+                                      seq, pos, T, stream);
+        else
+            e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos,
+                                  T, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "append_latent launch");
     return ok();
@@ -155,9 +162,9 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
 {
     if (Q < 0) return fail(LI_ERR_SHAPE, "Q=%d", Q);
     if (H <= 0 || H > LI_MAX_HEADS) return fail(LI_ERR_SHAPE, "H=%d outside [1, %d]", H, LI_MAX_HEADS);
-    if (dtype != LI_BF16 && dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (dtype != LI_BF16 && dtype != LI_FP32 && dtype != LI_FP8) return fail(LI_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
     if (!r_supported(r, dtype)) return fail(LI_ERR_UNSUPPORTED, "r=%d for dtype %d", r, (int)dtype);
-    if (dtype == LI_BF16 && d != 32 && d != 64 && d != 128 && d != 256)
+    if (dtype != LI_FP32 && d != 32 && d != 64 && d != 128 && d != 256)
         return fail(LI_ERR_UNSUPPORTED, "bf16 absorption needs d in {32,64,128,256}, got %d", d);
     if (dtype == LI_FP32 && (d <= 0 || d > 1024)) return fail(LI_ERR_SHAPE, "d=%d outside [1, 1024]", d);
     if (Q == 0) return ok();
@@ -165,7 +172,10 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
     hipError_t e;
     {
         li::TimedScope ts(LI_KERNEL_ABSORB, stream);
-        e = li::launch_absorb(q, w_dec, q_tilde, (int64_t)Q * H, d, r, dtype == LI_BF16, stream);
+        if (dtype == LI_FP8)
+            e = li::launch_absorb_fp8(q, w_dec, q_tilde, (int64_t)Q * H, d, r, stream);
+        else
+            e = li::launch_absorb(q, w_dec, q_tilde, (int64_t)Q * H, d, r, dtype == LI_BF16, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "absorb_query launch");
     return ok();
@@ -226,6 +236,7 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     // read once more by selection anyway); prefill scoring is MFMA-bound and
     // leaves the count to the selection pass.
     const bool fused_hist = scored && !(many && cache->dtype == LI_BF16);
+    const bool fp8 = cache->dtype == LI_FP8;
     hipError_t e = hipSuccess;
     if (scored) {
         if (fused_hist) {
@@ -239,7 +250,11 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         a.max_rows = queries->max_valid;
         a.hist = fused_hist ? sw.hist : nullptr;
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
-        e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
+        if (fp8)
+            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r,
+                                     queries->max_valid, stream);
+        else
+            e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
         if (e != hipSuccess) return hip_fail(e, "score launch");
     }
     {
@@ -303,7 +318,10 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.hist = sw.hist;
     {
         li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
-        e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
+        if (cache->dtype == LI_FP8)
+            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, M, stream);
+        else
+            e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "hs score launch");
     {
@@ -312,6 +330,18 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     }
     if (e != hipSuccess) return hip_fail(e, "hs select launch");
     return ok();
+}
+
+size_t li_fp8_query_scale_offset(int32_t Q, int32_t H, int32_t r)
+{
+    if (Q < 0 || H <= 0 || H > LI_MAX_HEADS || !r_supported(r, LI_FP8)) return 0;
+    return (size_t)li::fp8_query_scale_offset(Q, H, r);
+}
+
+size_t li_fp8_query_bytes(int32_t Q, int32_t H, int32_t r)
+{
+    if (Q < 0 || H <= 0 || H > LI_MAX_HEADS || !r_supported(r, LI_FP8)) return 0;
+    return (size_t)li::fp8_query_scale_offset(Q, H, r) + (size_t)Q * H * (r / 128) * 4;
 }
 
 li_status li_timing_enable(int on)

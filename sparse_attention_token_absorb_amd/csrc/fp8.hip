@@ -1,0 +1,517 @@
+// Segmented FP8 latent cache, FP8 queries and FP8 MFMA scoring (gfx950).
+//
+// LatentIndex (paperlayer.ai summary of arXiv:2610.04635), §B.2: the
+// indexer runs in segmented FP8; §A.2: the decoder is absorbed into the
+// query before the Hadamard rotation, so both operands are rotated ahead of
+// quantization and their dot products are unchanged by it.  The pages fix no
+// format; the one used here:
+//   - each 128-element segment of a latent row or of an absorbed query head
+//     is rotated by the orthonormal Walsh-Hadamard transform (fp32
+//     butterflies with strides 1, 2, ..., 64, then a multiply by the fp32
+//     value of 1/sqrt(128));
+//   - the segment gets a power-of-two scale 2^e, e the smallest integer with
+//     amax * 2^-e <= 448 (clamped to [-120, 120]);
+//   - every element is stored as the OCP FP8 E4M3 code of x * 2^-e (round to
+//     nearest even, saturating at 448).
+// Power-of-two scales make the scaling exact and map onto the E8M0 block
+// scales of v_mfma_scale_f32_32x32x64_f8f6f4, which applies them to each
+// lane's block of 32 codes inside the MFMA: the score is
+//   sum_h w_h max(0, sum_seg sq[h][seg] sc[j][seg] sum_{t in seg} q8[h][t] c8[j][t])
+// with exact products and fp32 accumulation.
+//
+// Layouts.  Latent: codes [page][64][r] bytes beside scales [page][64][r/128]
+// fp32 (powers of two).  Query: one buffer, codes [Q][H][r] bytes then, at
+// byte offset li_fp8_query_scale_offset(Q, H, r), scales [Q][H][r/128] fp32.
+#include "li_device.hpp"
+#include "li_internal.hpp"
+
+#include <algorithm>
+
+namespace li {
+namespace {
+
+constexpr int kSeg = 128;               // elements per quantization segment
+constexpr int kGatherTilesF8 = 16;      // max tiles per wave in gather mode
+
+// 2^k as an fp32 (k in [-126, 127]).
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// Nearest E4M3 code (ties to the even mantissa), saturating at 448.  The
+// steps follow the format definition: magnitudes below 2^-6 go in steps of
+// 2^-9 (code = step count; 8 steps is the smallest normal, code 8); above,
+// three mantissa bits under the binade's exponent.
+__device__ __forceinline__ uint32_t e4m3_encode(float v)
+{
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (!(a > 0.0f)) return sign;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127; // floor(log2 a); fp32 subnormals land below -6
+    if (e < -6) return sign | (uint32_t)rintf(a * 512.0f);
+    int m = (int)rintf(a * exp2i(3 - e)); // 8 .. 16
+    int ee = e;
+    if (m == 16) {
+        m = 8;
+        ee += 1;
+    }
+    return sign | (uint32_t)(((ee + 7) << 3) | (m - 8));
+}
+
+// Smallest e with amax * 2^-e <= 448 (0 for amax == 0), clamped to [-120, 120].
+__device__ __forceinline__ int pow2_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int E;
+    const float f = frexpf(amax, &E); // amax = (2f) 2^(E-1), 2f in [1, 2)
+    int e = (2.0f * f <= 1.75f) ? E - 9 : E - 8;
+    return e < -120 ? -120 : (e > 120 ? 120 : e);
+}
+
+// Rotate and quantize one 128-element segment held by the 32 lanes of a
+// half-wave, four consecutive elements per lane (lane l32 holds elements
+// 4*l32 .. 4*l32+3).  Returns the four codes packed little-endian; e receives
+// the segment's scale exponent.  The butterflies run in the order of the
+// definition (strides 1, 2 inside the lane, then 4 .. 64 across lanes), each
+// output being lower + upper or lower - upper, so the fp32 results are the
+// definition's to the bit.
+__device__ __forceinline__ uint32_t rotate_quantize(float (&x)[4], int l32, int &e)
+{
+    {
+        const float a0 = x[0], b0 = x[1], a1 = x[2], b1 = x[3];
+        x[0] = a0 + b0;
+        x[1] = a0 - b0;
+        x[2] = a1 + b1;
+        x[3] = a1 - b1;
+    }
+    {
+        const float a0 = x[0], b0 = x[2], a1 = x[1], b1 = x[3];
+        x[0] = a0 + b0;
+        x[2] = a0 - b0;
+        x[1] = a1 + b1;
+        x[3] = a1 - b1;
+    }
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+        const bool upper = (l32 & d) != 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float p = __shfl_xor(x[t], d);
+            x[t] = upper ? p - x[t] : x[t] + p;
+        }
+    }
+    const float k = 0.08838834764831845f; // 1/sqrt(128)
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[t] = x[t] * k;
+        amax = fmaxf(amax, fabsf(x[t]));
+    }
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+    e = pow2_exponent(amax);
+    const float inv = exp2i(-e);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) packed |= e4m3_encode(x[t] * inv) << (8 * t);
+    return packed;
+}
+
+// ---------------------------------------------------------------------------
+// Append: bf16 rows [T][R] -> rotated, quantized codes and segment scales at
+// their page slots.  One half-wave per (row, segment).
+// ---------------------------------------------------------------------------
+template <int R>
+__global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales, const int32_t *bt, int max_pages,
+                                                    const u16 *rows, const int32_t *seq, const int32_t *pos, int T)
+{
+    constexpr int NSEG = R / kSeg;
+    const int half = (int)((blockIdx.x * 256 + threadIdx.x) >> 5); // (row, segment) index
+    const int l32 = threadIdx.x & 31;
+    const int t = half / NSEG, g = half % NSEG;
+    const bool live = t < T;
+    const int tc = live ? t : T - 1; // lanes past the end mirror the last row and store nothing
+    const uint2 raw = *(const uint2 *)(rows + (int64_t)tc * R + g * kSeg + 4 * l32);
+    float x[4] = {bf16_to_f32((u16)(raw.x & 0xFFFF)), bf16_to_f32((u16)(raw.x >> 16)),
+                  bf16_to_f32((u16)(raw.y & 0xFFFF)), bf16_to_f32((u16)(raw.y >> 16))};
+    int e;
+    const uint32_t codes = rotate_quantize(x, l32, e);
+    if (!live) return;
+    const int p = pos[t];
+    const int64_t slot = (int64_t)bt[(int64_t)seq[t] * max_pages + (p >> 6)] * kPage + (p & 63);
+    *(uint32_t *)(pool + slot * R + g * kSeg + 4 * l32) = codes;
+    if (l32 == 0) scales[slot * NSEG + g] = exp2i(e);
+}
+
+// ---------------------------------------------------------------------------
+// Absorption into an FP8 query: qt = q W_dec (bf16 MFMA, fp32 accumulation)
+// for 128 (query, head) rows and one 128-column segment per workgroup; the
+// fp32 result goes through LDS and each (row, segment) is rotated and
+// quantized by a half-wave.
+// ---------------------------------------------------------------------------
+template <int R, int D>
+__global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, uint8_t *codes, float *qscales,
+                                                    int64_t QH)
+{
+    constexpr int NSEG = R / kSeg;
+    constexpr int LD = D + 8;          // halves per transposed W row
+    constexpr int KS = D / 16;
+    constexpr int ITEMS = (D / 2) * (kSeg / 8);
+    constexpr int NIT = (ITEMS + 255) / 256;
+    constexpr int OLD = kSeg + 4;      // floats per staged result row
+    __shared__ __attribute__((aligned(16))) u16 wt[kSeg * LD];
+    __shared__ float s_out[4][32 * OLD];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int g = blockIdx.y;          // segment
+    const int c0 = g * kSeg;
+    const int64_t m0 = (int64_t)blockIdx.x * 128 + wv * 32;
+
+    bf16x8 a[KS];
+    {
+        const int64_t m = m0 + (lane & 31);
+        const int64_t mc = m < QH ? m : QH - 1;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[s] = *(const bf16x8 *)(q + mc * D + s * 16 + (lane >> 5) * 8);
+        if (m >= QH) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 z = {};
+                a[s] = z;
+            }
+        }
+    }
+    bf16x8 r0[NIT], r1[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        int it = tid + k * 256;
+        it = it < ITEMS ? it : ITEMS - 1;
+        const int e = (it / (kSeg / 8)) * 2;
+        const int t0 = c0 + (it % (kSeg / 8)) * 8;
+        r0[k] = *(const bf16x8 *)(W + (int64_t)e * R + t0);
+        r1[k] = *(const bf16x8 *)(W + (int64_t)(e + 1) * R + t0);
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = tid + k * 256;
+        if (it < ITEMS) {
+            const int e = (it / (kSeg / 8)) * 2;
+            const int tl = (it % (kSeg / 8)) * 8;
+            const u16 *h0 = (const u16 *)&r0[k];
+            const u16 *h1 = (const u16 *)&r1[k];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *(uint32_t *)(wt + (tl + i) * LD + e) = (uint32_t)h0[i] | ((uint32_t)h1[i] << 16);
+        }
+    }
+    __syncthreads();
+    // this wave's 32 rows x 128 columns, staged as fp32 rows
+    float *so = s_out[wv];
+#pragma unroll 1
+    for (int nt = 0; nt < kSeg / 32; ++nt) {
+        f32x16 acc = {};
+        const int n = nt * 32 + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 b = *(const bf16x8 *)(wt + n * LD + s * 16 + (lane >> 5) * 8);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) so[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * OLD + n] = acc[r];
+    }
+    wait_lds();
+    // two (row, segment) items per pass, one per half-wave
+    const int l32 = lane & 31;
+#pragma unroll 1
+    for (int rr = 0; rr < 32; rr += 2) {
+        const int row = rr + (lane >> 5);
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = so[row * OLD + 4 * l32 + t];
+        int e;
+        const uint32_t cw = rotate_quantize(x, l32, e);
+        const int64_t m = m0 + row;
+        if (m < QH) {
+            *(uint32_t *)(codes + m * R + c0 + 4 * l32) = cw;
+            if (l32 == 0) qscales[m * NSEG + g] = exp2i(e);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode scoring from the FP8 cache.  Workgroup = 4 waves of one query; wave
+// w streams tiles row0 + (w + 4 i) * 32 through a private ring of NB slots,
+// each the tile's codes (32 rows x R bytes, 16-byte pieces XOR-swizzled by
+// row) plus its rows' segment scales.  The query's codes are MFMA A
+// fragments for the whole stream; the tile is the B operand; both scales
+// enter as E8M0 exponents of v_mfma_scale_f32_32x32x64_f8f6f4.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int R, int HB, bool GATHER, int NB>
+__global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *pool_scales, int64_t qscale_off,
+                                                   int tiles_per_wave)
+{
+    constexpr int NSEG = R / kSeg;
+    constexpr int CODE_BYTES = kTile * R;      // one tile's codes
+    constexpr int SLOT = CODE_BYTES + 256;     // + 32 rows x NSEG scales
+    constexpr int NIC = CODE_BYTES / 1024;     // 1-KiB DMA instructions per tile
+    constexpr int NIT = NIC + 1;               // + the scales
+    constexpr int CH = R / 16;                 // 16-byte pieces per row
+    constexpr int KS = R / 64;                 // MFMA k-steps
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * SLOT];
+    __shared__ int32_t s_row[GATHER ? 4 * kGatherTilesF8 * kTile : 1];
+    __shared__ uint32_t s_hist[kHistBins];
+
+    const int q = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
+    const int64_t first = row0 + (int64_t)wv * kTile;
+    auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
+    const int nt_max =
+        first < a.max_rows ? (int)min64(tiles_per_wave, (a.max_rows - first + 4 * kTile - 1) / (4 * kTile)) : 0;
+
+    // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
+    // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
+    i32x8 qa[HB][KS];
+    int sa[HB][NSEG];
+    float wr[HB][16];
+    {
+        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
+        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const int hc = h < a.H ? h : a.H - 1;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
+                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
+                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (h >= a.H) {
+                    i32x8 z = {};
+                    v = z;
+                }
+                qa[hb][s] = v;
+            }
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g)
+                sa[hb][g] = h < a.H ? (int)((__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu) : 127;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                wr[hb][r] = hh < a.H ? a.w[(int64_t)q * a.H + hh] : 0.0f;
+            }
+        }
+    }
+    const int b = ((const_i32_t *)a.qseq)[q];
+    int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
+                   : valid_rows(((const_i32_t *)a.qpos)[q], ((const_i32_t *)a.seq_lens)[b]);
+    n = (int)min64(n, a.max_rows);
+    const uint8_t *pool = (const uint8_t *)a.pool;
+    const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
+    lds_u8 *const ring = (lds_u8 *)ring_raw + wv * NB * SLOT;
+    auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
+
+    if constexpr (GATHER) {
+        // physical slots of every tile row of this wave, two batched rounds
+        const int64_t max_pos = (int64_t)a.max_pages * kPage - 1;
+        int pos[kGatherTilesF8], page[kGatherTilesF8];
+#pragma unroll
+        for (int i = 0; i < kGatherTilesF8; ++i) {
+            pos[i] = 0;
+            if (i < nt_max) {
+                int64_t j = tile_row0(i) + (lane & 31);
+                j = j < a.cand_ld ? j : a.cand_ld - 1;
+                pos[i] = a.cand[(int64_t)q * a.cand_ld + j];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kGatherTilesF8; ++i) {
+            pos[i] = pos[i] < 0 ? 0 : (pos[i] > max_pos ? (int)max_pos : pos[i]);
+            page[i] = 0;
+            if (i < nt_max) page[i] = a.bt[(int64_t)b * a.max_pages + (pos[i] >> 6)];
+        }
+#pragma unroll
+        for (int i = 0; i < kGatherTilesF8; ++i)
+            if (i < nt_max && lane < 32)
+                s_row[(wv * kGatherTilesF8 + i) * kTile + lane] = clamp_page(page[i]) * kPage + (pos[i] & 63);
+        wait_lds();
+    }
+    // tile i -> slot (i % NB): the codes, then the scales of its 32 rows
+    auto issue = [&](int i) {
+        lds_u8 *slot = ring + (i % NB) * SLOT;
+        const __attribute__((address_space(3))) int32_t *rows =
+            (const __attribute__((address_space(3))) int32_t *)s_row + (wv * kGatherTilesF8 + i) * kTile;
+        int64_t base = 0;
+        if constexpr (!GATHER) {
+            const int64_t t0 = tile_row0(i);
+            base = (int64_t)clamp_page(bt[t0 >> 6]) * kPage + (t0 & 63);
+        }
+        auto slot_of = [&](int nr) -> int64_t {
+            if constexpr (GATHER) return (int64_t)rows[nr];
+            else return base + nr;
+        };
+#pragma unroll
+        for (int ii = 0; ii < NIC; ++ii) {
+            const int p = ii * 64 + lane;
+            const int nr = p / CH, cs = p % CH;
+            const int c = cs ^ (nr % CH);
+            dma16(pool + slot_of(nr) * R + c * 16, slot + ii * 1024);
+        }
+        // scales: lane l carries (row l / NSEG, segment l % NSEG); lanes past
+        // the tile's 32 rows repeat its last row
+        int sl = lane / NSEG;
+        sl = sl < kTile ? sl : kTile - 1;
+        dma4(pool_scales + slot_of(sl) * NSEG + (lane % NSEG), slot + CODE_BYTES);
+    };
+    const int npro = min(NB - 1, nt_max);
+    for (int i = 0; i < npro; ++i) issue(i);
+
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (row0 >= n) {
+        wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
+        return;
+    }
+    if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
+    int nt = 0;
+    if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
+    if (a.hist) wg_barrier(); // histogram cleared before any wave counts into it
+
+    float *out = a.out + (int64_t)q * a.out_ld;
+    const int nr = lane & 31, gk = lane >> 5;
+    for (int i = 0; i < nt; ++i) {
+        if (i + NB - 1 < nt) {
+            wait_lds(); // this wave's reads of that slot (tile i-1) are complete
+            issue(i + NB - 1);
+        }
+        wait_after<NIT, NB - 1>(min(NB - 1, nt - 1 - i));
+        const lds_u8 *slot = ring + (i % NB) * SLOT;
+        int sb[NSEG];
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g)
+            sb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + CODE_BYTES +
+                                                                                  (nr * NSEG + g) * 4) >> 23) & 0xFFu);
+        f32x16 acc[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            f32x16 z = {};
+            acc[hb] = z;
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int c = 4 * s + 2 * gk;
+            const u32x4 lo = *(const lds_u32x4 *)(slot + (nr * CH + (c ^ (nr % CH))) * 16);
+            const u32x4 hi = *(const lds_u32x4 *)(slot + (nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+            const i32x8 bv = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const int g = (s * 64) / kSeg;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[hb][s], bv, acc[hb], 0, 0, 0, sa[hb][g], 0,
+                                                                          sb[g]);
+        }
+        const float p = epilogue<HB>(acc, wr);
+        const int64_t j = tile_row0(i) + lane;
+        if (lane < 32 && j < n) {
+            out[j] = p;
+            if (a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+        }
+    }
+    wait_vmcnt<0>(); // tiles issued ahead of the row count and never used
+    if (a.hist) {
+        __syncthreads();
+        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
+    }
+}
+
+template <int R, int HB>
+hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
+                               hipStream_t s)
+{
+    constexpr int NB = R == 256 ? 4 : 7;
+    const int64_t tiles = (max_rows + kTile - 1) / kTile;
+    const int64_t per_q = (256 + a.Q - 1) / a.Q;
+    int64_t tpw = (tiles + 4 * per_q - 1) / (4 * per_q);
+    if (tpw < 1) tpw = 1;
+    if (a.cand && tpw > kGatherTilesF8) tpw = kGatherTilesF8;
+    const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    if (a.cand)
+        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, pool_scales,
+                           qscale_off, (int)tpw);
+    else
+        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, pool_scales,
+                           qscale_off, (int)tpw);
+    return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
+                              hipStream_t s)
+{
+    if (a.H <= 32) return launch_score_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s);
+    return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
+}
+
+} // namespace
+
+int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r) { return (Q * H * r + 255) / 256 * 256; }
+
+hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
+                             const int32_t *seq, const int32_t *pos, int T, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    const int64_t halves = (int64_t)T * (r / kSeg);
+    const unsigned blocks = (unsigned)((halves * 32 + 255) / 256);
+    if (r == 256)
+        hipLaunchKernelGGL((k_append_fp8<256>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
+                           (const u16 *)rows, seq, pos, T);
+    else if (r == 128)
+        hipLaunchKernelGGL((k_append_fp8<128>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
+                           (const u16 *)rows, seq, pos, T);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH, int d, int r, hipStream_t s)
+{
+    if (QH <= 0) return hipSuccess;
+    uint8_t *codes = (uint8_t *)qt;
+    float *scales = (float *)((uint8_t *)qt + fp8_query_scale_offset(QH, 1, r));
+    const dim3 grid((unsigned)((QH + 127) / 128), (unsigned)(r / kSeg));
+    const u16 *qq = (const u16 *)q, *ww = (const u16 *)W;
+#define LI_ABSORB_FP8(RR, DD)                                                                                        \
+    hipLaunchKernelGGL((k_absorb_fp8<RR, DD>), grid, dim3(256), 0, s, qq, ww, codes, scales, QH)
+    if (r == 256) {
+        switch (d) {
+        case 32: LI_ABSORB_FP8(256, 32); break;
+        case 64: LI_ABSORB_FP8(256, 64); break;
+        case 128: LI_ABSORB_FP8(256, 128); break;
+        case 256: LI_ABSORB_FP8(256, 256); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else if (r == 128) {
+        switch (d) {
+        case 32: LI_ABSORB_FP8(128, 32); break;
+        case 64: LI_ABSORB_FP8(128, 64); break;
+        case 128: LI_ABSORB_FP8(128, 128); break;
+        case 256: LI_ABSORB_FP8(128, 256); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef LI_ABSORB_FP8
+    return hipGetLastError();
+}
+
+hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
+                            int64_t max_rows, hipStream_t s)
+{
+    if (a.Q <= 0 || max_rows <= 0) return hipSuccess;
+    if (r == 256) return launch_score_fp8_r<256>(a, pool_scales, qscale_off, max_rows, s);
+    if (r == 128) return launch_score_fp8_r<128>(a, pool_scales, qscale_off, max_rows, s);
+    return hipErrorInvalidValue;
+}
+
+} // namespace li

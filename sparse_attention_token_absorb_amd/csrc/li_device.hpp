@@ -1,0 +1,134 @@
+// Device helpers shared by the scoring kernels (gfx950): LDS-typed
+// pointers, LDS DMA, barriers and waits, and the fused score epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "li_common.hpp"
+#include "li_internal.hpp"
+
+namespace li {
+namespace {
+
+// LDS-typed pointers keep every access a ds_* instruction (a generic pointer
+// would become a flat access that also waits on global memory).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef const __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_uniform + lane * 16 (global_load_lds_dwordx4, LDS base in M0).
+// Written as inline asm on purpose: the compiler then does not know that
+// LDS is being written, and does not drain every such load (vmcnt(0))
+// before each later LDS read.  The kernels wait for these loads themselves
+// (wait_after / wait_vmcnt, counting loads only: vector loads complete in
+// issue order) and publish them to other waves with a barrier.  The
+// instruction has no VGPR result, so no register is left in flight.  M0 is
+// saved and restored around it (with the wait state a write of M0 needs
+// before an LDS-direct load), so the compiler's own use of M0 is untouched.
+__device__ __forceinline__ void dma16(const void *g, lds_u8 *lds_uniform)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[addr], off\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [addr] "v"(g), [lds] "s"(lds)
+                 : "memory");
+}
+
+// Workgroup barrier without the global-memory fences of __syncthreads():
+// outstanding DMA loads stay in flight across it.  This wave's LDS reads are
+// complete before it arrives.
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+
+// Wait until at most `after` * PER vector-memory operations are in flight
+// (the count must be an immediate, hence the switch).
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_after(int after)
+{
+    static_assert(PER * MAXA < 64, "vmcnt range");
+    switch (after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<(MAXA >= 2 ? 2 : 1) * PER>(); break;
+    case 3: wait_vmcnt<(MAXA >= 3 ? 3 : 1) * PER>(); break;
+    case 4: wait_vmcnt<(MAXA >= 4 ? 4 : 1) * PER>(); break;
+    case 5: wait_vmcnt<(MAXA >= 5 ? 5 : 1) * PER>(); break;
+    case 6: wait_vmcnt<(MAXA >= 6 ? 6 : 1) * PER>(); break;
+    default: wait_vmcnt<(MAXA >= 7 ? 7 : 1) * PER>(); break;
+    }
+}
+
+// Absorbed-query fragments (MFMA A operand) and per-lane head weights.
+// 4 bytes per lane from global memory straight into LDS at
+// lds_uniform + lane * 4 (global_load_lds_dword), issued like dma16.
+__device__ __forceinline__ void dma4(const void *g, lds_u8 *lds_uniform)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dword %[addr], off\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [addr] "v"(g), [lds] "s"(lds)
+                 : "memory");
+}
+
+// max(x, 0) in one integer max on the bit pattern (negative floats, -0.0
+// included, have the sign bit set and become +0.0).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// ReLU, head weights and head sum: the score of tile row (lane % 32).
+template <int HB>
+__device__ __forceinline__ float epilogue(const f32x16 (&acc)[HB], const float (&w)[HB][16])
+{
+    float ps[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        ps[hb] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ps[hb] = fmaf(w[hb][r], relu(acc[hb][r]), ps[hb]);
+    }
+    float p = ps[0];
+#pragma unroll
+    for (int hb = 1; hb < HB; ++hb) p += ps[hb];
+    return p + __shfl_xor(p, 32);
+}
+
+__device__ __forceinline__ void hist_zero(uint32_t *h, int nthreads, int tid)
+{
+    for (int i = tid; i < kHistBins; i += nthreads) h[i] = 0;
+}
+
+__device__ __forceinline__ void hist_flush(const uint32_t *h, int32_t *g, int nthreads, int tid)
+{
+    for (int i = tid; i < kHistBins; i += nthreads)
+        if (h[i]) atomicAdd(&g[i], (int)h[i]);
+}
+
+} // namespace
+} // namespace li

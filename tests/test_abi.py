@@ -45,7 +45,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings(L):
-    assert L.li_abi_version() == 1
+    assert L.li_abi_version() == 2
     assert L.li_status_str(0) == b"LI_OK"
     assert L.li_status_str(4) == b"LI_ERR_WORKSPACE"
     assert L.li_status_str(99) == b"LI_ERR_UNKNOWN"
@@ -53,7 +53,7 @@ def test_version_and_status_strings(L):
 
 def cache(**kw):
     d = dict(pool=FAKE.value, block_table=FAKE.value, seq_lens=FAKE.value, batch=1, max_pages=4, page_size=64,
-             num_pages=4, r=256, dtype=B.LI_BF16)
+             num_pages=4, r=256, dtype=B.LI_BF16, scales=None)
     d.update(kw)
     return B._Cache(**d)
 
@@ -149,3 +149,24 @@ def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         B.absorb_query(torch.zeros(1, 4, 32), torch.zeros(32, 64))
+
+
+def test_fp8_validation_and_sizes(L):
+    c = cache(dtype=B.LI_FP8)  # no scales
+    assert L.li_append_latent(ctypes.byref(c), FAKE, FAKE, FAKE, 3, None) == B.LI_ERR_NULL
+    c = cache(dtype=B.LI_FP8, scales=FAKE.value, r=64)
+    assert L.li_append_latent(ctypes.byref(c), FAKE, FAKE, FAKE, 3, None) == B.LI_ERR_UNSUPPORTED
+    c = cache(dtype=B.LI_FP8, scales=FAKE.value, r=256)
+    assert L.li_append_latent(ctypes.byref(c), None, None, None, 0, None) == B.LI_OK
+    assert score_topk(L, c=c, k=0) == B.LI_ERR_SHAPE
+    a = lambda **kw: L.li_absorb_query(FAKE, FAKE, FAKE, kw.get("Q", 1), 64, kw.get("d", 128), kw.get("r", 256),
+                                      B.LI_FP8, None)
+    assert a(r=64) == B.LI_ERR_UNSUPPORTED
+    assert a(d=48) == B.LI_ERR_UNSUPPORTED
+    assert a(Q=0) == B.LI_OK
+    # codes [Q][H][r], then (256-byte aligned) scales [Q][H][r/128] fp32
+    assert L.li_fp8_query_scale_offset(3, 64, 256) == 3 * 64 * 256
+    assert L.li_fp8_query_bytes(3, 64, 256) == 3 * 64 * 256 + 3 * 64 * 2 * 4
+    assert L.li_fp8_query_scale_offset(1, 3, 128) == 512
+    assert L.li_fp8_query_bytes(1, 3, 128) == 512 + 3 * 4
+    assert L.li_fp8_query_bytes(1, 64, 64) == 0 and L.li_fp8_query_bytes(1, 0, 256) == 0
