@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--counters", choices=("decode", "prefill"), default=None,
                     help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
@@ -320,6 +321,50 @@ def main() -> int:
         log(f"sweep {sweep}")
 
     # ------------------------------------------------------------------
+    # Segmented FP8 cache (same latent, rotated and quantized on append):
+    # full LatentIndex x4 layers and HS, decode scoring against HBM
+    # ------------------------------------------------------------------
+    fp8 = None
+    if not args.no_fp8:
+        f8pool = torch.zeros((g.num_pages, 64, r), dtype=torch.uint8, device=dev)
+        f8sc = torch.zeros((g.num_pages, 64, r // 128), dtype=torch.float32, device=dev)
+        f8cache = B.LatentCache(f8pool, i32(g.block_table), i32(g.lens), f8sc)
+        for b in range(Bn):
+            B.append_latent(f8cache, tdev(g.latent[b], bf), i32(np.full(N, b)), i32(np.arange(N)))
+        f8q = [B.absorb_query(q[l], W[l], fp8=True) for l in range(G)]
+
+        def f8_prep():
+            B.append_latent(f8cache, new_rows, new_seq, new_pos)
+            for l in range(G):
+                B.absorb_query(q[l], W[l], out=f8q[l], fp8=True)
+
+        def f8_full():
+            for l in range(G):
+                B.score_topk(f8cache, seq, pos, N, f8q[l], w[l], k, ws=ws, out=out_b[l])
+
+        def f8_hs():
+            B.score_topk(f8cache, seq, pos, N, f8q[0], w[0], M, k_inner=k, ws=ws, out=out_anchor)
+            for l in range(1, G):
+                B.hs_select(f8cache, seq, pos, N, out_anchor.idx, out_anchor.count, f8q[l], w[l], k, ws=ws_hs,
+                            out=out_f[l - 1])
+
+        f8_ms_prep = time_graph(capture(f8_prep), reps)
+        f8_ms_full = time_graph(capture(f8_full), reps)
+        f8_ms_hs = time_graph(capture(f8_hs), reps)
+        f8_score_ms, _ = kernel_time(f8_full, B.LI_KERNEL_SCORE_DECODE, reps)
+        f8_bytes_row = r + (r // 128) * 4
+        f8_bytes = Bn * N * f8_bytes_row + Bn * (H * r + H * (r // 128) * 4 + H * 4)
+        f8_gbs = f8_bytes / (f8_score_ms * 1e-3) / 1e9
+        fp8 = {"append_plus_absorb_x4_us": round(f8_ms_prep * 1e3, 2),
+               "full_latentindex_us_per_layer": round(f8_ms_full * 1e3 / G, 2),
+               "hs_us_per_group": round(f8_ms_hs * 1e3, 2),
+               "score_kernel_us": round(f8_score_ms * 1e3, 2), "bytes_per_launch": f8_bytes,
+               "score_GBs": round(f8_gbs, 1), "score_frac_hbm": round(f8_gbs / HBM_PEAK_GBS, 4),
+               "rows_per_s_full": round(G * Bn * N / (f8_ms_full * 1e-3), 1)}
+        log(f"fp8 {fp8}")
+        del f8pool, f8sc, f8cache, f8q
+
+    # ------------------------------------------------------------------
     # CPU baseline: the fp64 oracle on a bounded sample of the same workload
     # ------------------------------------------------------------------
     cpu = None
@@ -377,7 +422,7 @@ def main() -> int:
                                f"+ HS (M={M}) + per-layer baseline indexer x{G}",
                    "batch": Bn, "context": N, "heads": H, "d": d, "r": r, "k": k, "M": M, "group": G,
                    "parallelism": "single GPU"},
-        "modes": modes, "roofline": roofline, "sweep": sweep, "prefill": prefill, "cpu_baseline": cpu,
+        "modes": modes, "roofline": roofline, "sweep": sweep, "fp8": fp8, "prefill": prefill, "cpu_baseline": cpu,
     }
     s = json.dumps(line)
     print(s, flush=True)

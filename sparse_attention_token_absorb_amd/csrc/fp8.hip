@@ -67,53 +67,96 @@ __device__ __forceinline__ int pow2_exponent(float amax)
     return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
-// Rotate and quantize one 128-element segment held by the 32 lanes of a
-// half-wave, four consecutive elements per lane (lane l32 holds elements
-// 4*l32 .. 4*l32+3).  Returns the four codes packed little-endian; e receives
-// the segment's scale exponent.  The butterflies run in the order of the
-// definition (strides 1, 2 inside the lane, then 4 .. 64 across lanes), each
-// output being lower + upper or lower - upper, so the fp32 results are the
-// definition's to the bit.
-__device__ __forceinline__ uint32_t rotate_quantize(float (&x)[4], int l32, int &e)
+// v from lane (l ^ d) of the same 32-lane half (d < 32): ds_swizzle in
+// bit-mask mode (and 0x1F, or 0, xor d), no LDS access.
+template <int D>
+__device__ __forceinline__ float xor32(float v)
 {
-    {
-        const float a0 = x[0], b0 = x[1], a1 = x[2], b1 = x[3];
-        x[0] = a0 + b0;
-        x[1] = a0 - b0;
-        x[2] = a1 + b1;
-        x[3] = a1 - b1;
-    }
-    {
-        const float a0 = x[0], b0 = x[2], a1 = x[1], b1 = x[3];
-        x[0] = a0 + b0;
-        x[2] = a0 - b0;
-        x[1] = a1 + b1;
-        x[3] = a1 - b1;
-    }
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (D << 10) | 0x1F));
+}
+
+// Rotate and quantize NR 128-element segments, each held by the 32 lanes of
+// a half-wave, four consecutive elements per lane (lane l32 holds elements
+// 4*l32 .. 4*l32+3 of each).  Returns the four codes of each segment packed
+// little-endian; e[k] receives segment k's scale exponent.  The butterflies
+// run in the order of the definition (strides 1, 2 inside the lane, then
+// 4 .. 64 across lanes), each output being lower + upper or lower - upper,
+// so the fp32 results are the definition's to the bit.  The NR segments are
+// independent chains, interleaved to hide the cross-lane latency.
+template <int D, int NR>
+__device__ __forceinline__ void butterfly_stage(float (&x)[NR][4], bool upper)
+{
+    float p[NR][4];
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
-        const bool upper = (l32 & d) != 0;
+    for (int k = 0; k < NR; ++k)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float p = __shfl_xor(x[t], d);
-            x[t] = upper ? p - x[t] : x[t] + p;
+        for (int t = 0; t < 4; ++t) p[k][t] = xor32<D>(x[k][t]);
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[k][t] = upper ? p[k][t] - x[k][t] : x[k][t] + p[k][t];
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void amax_stage(float (&m)[NR])
+{
+    float p[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) p[k] = xor32<D>(m[k]);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) m[k] = fmaxf(m[k], p[k]);
+}
+
+template <int NR>
+__device__ __forceinline__ void rotate_quantize(float (&x)[NR][4], int l32, int (&e)[NR], uint32_t (&codes)[NR])
+{
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        {
+            const float a0 = x[k][0], b0 = x[k][1], a1 = x[k][2], b1 = x[k][3];
+            x[k][0] = a0 + b0;
+            x[k][1] = a0 - b0;
+            x[k][2] = a1 + b1;
+            x[k][3] = a1 - b1;
+        }
+        {
+            const float a0 = x[k][0], b0 = x[k][2], a1 = x[k][1], b1 = x[k][3];
+            x[k][0] = a0 + b0;
+            x[k][2] = a0 - b0;
+            x[k][1] = a1 + b1;
+            x[k][3] = a1 - b1;
         }
     }
-    const float k = 0.08838834764831845f; // 1/sqrt(128)
-    float amax = 0.0f;
+    butterfly_stage<1>(x, (l32 & 1) != 0);
+    butterfly_stage<2>(x, (l32 & 2) != 0);
+    butterfly_stage<4>(x, (l32 & 4) != 0);
+    butterfly_stage<8>(x, (l32 & 8) != 0);
+    butterfly_stage<16>(x, (l32 & 16) != 0);
+    const float kn = 0.08838834764831845f; // 1/sqrt(128)
+    float amax[NR];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        x[t] = x[t] * k;
-        amax = fmaxf(amax, fabsf(x[t]));
+    for (int k = 0; k < NR; ++k) {
+        amax[k] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[k][t] = x[k][t] * kn;
+            amax[k] = fmaxf(amax[k], fabsf(x[k][t]));
+        }
     }
+    amax_stage<1>(amax);
+    amax_stage<2>(amax);
+    amax_stage<4>(amax);
+    amax_stage<8>(amax);
+    amax_stage<16>(amax);
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-    e = pow2_exponent(amax);
-    const float inv = exp2i(-e);
-    uint32_t packed = 0;
+    for (int k = 0; k < NR; ++k) {
+        e[k] = pow2_exponent(amax[k]);
+        const float inv = exp2i(-e[k]);
+        uint32_t packed = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) packed |= e4m3_encode(x[t] * inv) << (8 * t);
-    return packed;
+        for (int t = 0; t < 4; ++t) packed |= e4m3_encode(x[k][t] * inv) << (8 * t);
+        codes[k] = packed;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -131,10 +174,13 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
     const bool live = t < T;
     const int tc = live ? t : T - 1; // lanes past the end mirror the last row and store nothing
     const uint2 raw = *(const uint2 *)(rows + (int64_t)tc * R + g * kSeg + 4 * l32);
-    float x[4] = {bf16_to_f32((u16)(raw.x & 0xFFFF)), bf16_to_f32((u16)(raw.x >> 16)),
-                  bf16_to_f32((u16)(raw.y & 0xFFFF)), bf16_to_f32((u16)(raw.y >> 16))};
-    int e;
-    const uint32_t codes = rotate_quantize(x, l32, e);
+    float x[1][4] = {{bf16_to_f32((u16)(raw.x & 0xFFFF)), bf16_to_f32((u16)(raw.x >> 16)),
+                      bf16_to_f32((u16)(raw.y & 0xFFFF)), bf16_to_f32((u16)(raw.y >> 16))}};
+    int ee[1];
+    uint32_t cw[1];
+    rotate_quantize<1>(x, l32, ee, cw);
+    const uint32_t codes = cw[0];
+    const int e = ee[0];
     if (!live) return;
     const int p = pos[t];
     const int64_t slot = (int64_t)bt[(int64_t)seq[t] * max_pages + (p >> 6)] * kPage + (p & 63);
@@ -144,27 +190,33 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
 
 // ---------------------------------------------------------------------------
 // Absorption into an FP8 query: qt = q W_dec (bf16 MFMA, fp32 accumulation)
-// for 128 (query, head) rows and one 128-column segment per workgroup; the
+// for MB (query, head) rows and one 128-column segment per workgroup; the
 // fp32 result goes through LDS and each (row, segment) is rotated and
-// quantized by a half-wave.
+// quantized by a half-wave.  MB = 128: each wave owns 32 rows and all four
+// 32-column tiles (many rows, W staged once per 128 rows).  MB = 32: the
+// four waves split the columns of 32 rows (few rows: 4x more workgroups).
 // ---------------------------------------------------------------------------
-template <int R, int D>
+template <int R, int D, int MB>
 __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, uint8_t *codes, float *qscales,
                                                     int64_t QH)
 {
+    static_assert(MB == 32 || MB == 128, "row block");
     constexpr int NSEG = R / kSeg;
     constexpr int LD = D + 8;          // halves per transposed W row
     constexpr int KS = D / 16;
     constexpr int ITEMS = (D / 2) * (kSeg / 8);
     constexpr int NIT = (ITEMS + 255) / 256;
     constexpr int OLD = kSeg + 4;      // floats per staged result row
+    constexpr int TPW = MB / 32;       // column tiles per wave
     __shared__ __attribute__((aligned(16))) u16 wt[kSeg * LD];
-    __shared__ float s_out[4][32 * OLD];
+    __shared__ float s_out[MB * OLD];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int g = blockIdx.y;          // segment
     const int c0 = g * kSeg;
-    const int64_t m0 = (int64_t)blockIdx.x * 128 + wv * 32;
+    const int rg = MB == 128 ? wv : 0; // this wave's 32-row group
+    const int64_t mb0 = (int64_t)blockIdx.x * MB;
+    const int64_t m0 = mb0 + rg * 32;
 
     bf16x8 a[KS];
     {
@@ -204,10 +256,10 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
         }
     }
     __syncthreads();
-    // this wave's 32 rows x 128 columns, staged as fp32 rows
-    float *so = s_out[wv];
-#pragma unroll 1
-    for (int nt = 0; nt < kSeg / 32; ++nt) {
+    // MFMA: this wave's 32 rows x TPW column tiles, staged as fp32 rows
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+        const int nt = MB == 128 ? ti : wv;
         f32x16 acc = {};
         const int n = nt * 32 + (lane & 31);
 #pragma unroll
@@ -216,23 +268,34 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) so[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * OLD + n] = acc[r];
+        for (int r = 0; r < 16; ++r)
+            s_out[(rg * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * OLD + n] = acc[r];
     }
-    wait_lds();
-    // two (row, segment) items per pass, one per half-wave
+    __syncthreads();
+    // quantization: the MB rows split over the 8 half-waves, NR rows each per pass
+    constexpr int ROWS_PER_HALF = MB / 8;
+    constexpr int NR = ROWS_PER_HALF < 8 ? ROWS_PER_HALF : 8;
     const int l32 = lane & 31;
+    const int half = wv * 2 + (lane >> 5);
 #pragma unroll 1
-    for (int rr = 0; rr < 32; rr += 2) {
-        const int row = rr + (lane >> 5);
-        float x[4];
+    for (int rr = 0; rr < ROWS_PER_HALF; rr += NR) {
+        float x[NR][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = so[row * OLD + 4 * l32 + t];
-        int e;
-        const uint32_t cw = rotate_quantize(x, l32, e);
-        const int64_t m = m0 + row;
-        if (m < QH) {
-            *(uint32_t *)(codes + m * R + c0 + 4 * l32) = cw;
-            if (l32 == 0) qscales[m * NSEG + g] = exp2i(e);
+        for (int k = 0; k < NR; ++k) {
+            const int row = (rr + k) * 8 + half;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[k][t] = s_out[row * OLD + 4 * l32 + t];
+        }
+        int e[NR];
+        uint32_t cw[NR];
+        rotate_quantize<NR>(x, l32, e, cw);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int64_t m = mb0 + (rr + k) * 8 + half;
+            if (m < QH) {
+                *(uint32_t *)(codes + m * R + c0 + 4 * l32) = cw[k];
+                if (l32 == 0) qscales[m * NSEG + g] = exp2i(e[k]);
+            }
         }
     }
 }
@@ -452,6 +515,31 @@ hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int6
     return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
 }
 
+template <int R, int D>
+void launch_absorb_fp8_rd(const u16 *q, const u16 *W, uint8_t *codes, float *scales, int64_t QH, hipStream_t s)
+{
+    if ((QH + 127) / 128 >= 256) // many rows: W staged once per 128 rows
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 128>), dim3((unsigned)((QH + 127) / 128), R / kSeg), dim3(256), 0, s,
+                           q, W, codes, scales, QH);
+    else
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 32>), dim3((unsigned)((QH + 31) / 32), R / kSeg), dim3(256), 0, s, q,
+                           W, codes, scales, QH);
+}
+
+template <int R>
+hipError_t launch_absorb_fp8_r(const u16 *q, const u16 *W, uint8_t *codes, float *scales, int64_t QH, int d,
+                               hipStream_t s)
+{
+    switch (d) {
+    case 32: launch_absorb_fp8_rd<R, 32>(q, W, codes, scales, QH, s); break;
+    case 64: launch_absorb_fp8_rd<R, 64>(q, W, codes, scales, QH, s); break;
+    case 128: launch_absorb_fp8_rd<R, 128>(q, W, codes, scales, QH, s); break;
+    case 256: launch_absorb_fp8_rd<R, 256>(q, W, codes, scales, QH, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 } // namespace
 
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r) { return (Q * H * r + 255) / 256 * 256; }
@@ -478,31 +566,10 @@ hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH,
     if (QH <= 0) return hipSuccess;
     uint8_t *codes = (uint8_t *)qt;
     float *scales = (float *)((uint8_t *)qt + fp8_query_scale_offset(QH, 1, r));
-    const dim3 grid((unsigned)((QH + 127) / 128), (unsigned)(r / kSeg));
     const u16 *qq = (const u16 *)q, *ww = (const u16 *)W;
-#define LI_ABSORB_FP8(RR, DD)                                                                                        \
-    hipLaunchKernelGGL((k_absorb_fp8<RR, DD>), grid, dim3(256), 0, s, qq, ww, codes, scales, QH)
-    if (r == 256) {
-        switch (d) {
-        case 32: LI_ABSORB_FP8(256, 32); break;
-        case 64: LI_ABSORB_FP8(256, 64); break;
-        case 128: LI_ABSORB_FP8(256, 128); break;
-        case 256: LI_ABSORB_FP8(256, 256); break;
-        default: return hipErrorInvalidValue;
-        }
-    } else if (r == 128) {
-        switch (d) {
-        case 32: LI_ABSORB_FP8(128, 32); break;
-        case 64: LI_ABSORB_FP8(128, 64); break;
-        case 128: LI_ABSORB_FP8(128, 128); break;
-        case 256: LI_ABSORB_FP8(128, 256); break;
-        default: return hipErrorInvalidValue;
-        }
-    } else {
-        return hipErrorInvalidValue;
-    }
-#undef LI_ABSORB_FP8
-    return hipGetLastError();
+    if (r == 256) return launch_absorb_fp8_r<256>(qq, ww, codes, scales, QH, d, s);
+    if (r == 128) return launch_absorb_fp8_r<128>(qq, ww, codes, scales, QH, d, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
