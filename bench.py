@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "indexer decode us/layer + latent rows scored/s, 8K-128K ctx; % HBM peak"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, TFLOP/s
 
 
 def log(msg: str) -> None:
@@ -413,6 +414,21 @@ def main() -> int:
                    "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "select_ms": round(sel_ms, 3),
                    "absorb_ms": round(ab_ms, 3), "valid_pairs": pl.pairs}
         log(f"prefill {prefill}")
+        if not args.no_fp8:
+            del pl
+            torch.cuda.empty_cache()
+            pf = setup_prefill(B, synth, dev, bf, i32, tdev, N // 2, fp8=True)
+            with torch.cuda.stream(stream):
+                pf.layer()
+            torch.cuda.synchronize()
+            f_sc, _ = kernel_time(pf.layer, B.LI_KERNEL_SCORE_PREFILL, preps)
+            f_sel, _ = kernel_time(pf.layer, B.LI_KERNEL_SELECT, preps)
+            f_ab, _ = kernel_time(pf.layer, B.LI_KERNEL_ABSORB, preps)
+            f_tf = flops / (f_sc * 1e-3) / 1e12
+            prefill["fp8"] = {"score_ms": round(f_sc, 3), "tflops": round(f_tf, 1), "peak_tflops": FP8_PEAK_TFLOPS,
+                              "frac_mfma": round(f_tf / FP8_PEAK_TFLOPS, 4), "select_ms": round(f_sel, 3),
+                              "absorb_ms": round(f_ab, 3)}
+            log(f"prefill fp8 {prefill['fp8']}")
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -468,15 +484,18 @@ class PrefillLayer:
     """Chunked prefill of one layer: 4096 queries at the last positions of a
     `n`-row cache (n = 65536 by default), absorb + score + per-row top-k."""
 
-    def __init__(self, B, synth, dev, bf, i32, tdev, n):
+    def __init__(self, B, synth, dev, bf, i32, tdev, n, fp8=False):
         import numpy as np
         import torch
-        self.n, self.Q = n, 4096
+        self.n, self.Q, self.fp8 = n, 4096, fp8
         p5 = synth.make_prefill("prefill", 5, N=n, Qn=self.Q, r=256, H=64, d=128, G=1, k=2048)
-        self.cache = make_cache_from(p5, B, tdev, i32, bf, dev)
+        self.cache = make_cache_from(p5, B, tdev, i32, bf, dev, fp8=fp8)
         self.seq, self.pos = i32(p5.qseq), i32(p5.qpos)
         self.q, self.W, self.w = tdev(p5.q[0], bf), tdev(p5.W[0], bf), torch.from_numpy(p5.w[0]).to(dev)
-        self.qt = torch.empty((p5.Q, p5.H, p5.r), dtype=bf, device=dev)
+        if fp8:
+            self.qt = B.absorb_query(self.q, self.W, fp8=True)
+        else:
+            self.qt = torch.empty((p5.Q, p5.H, p5.r), dtype=bf, device=dev)
         self.ws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, p5.Q, n, p5.H, p5.r, p5.k, 0),
                               dtype=torch.uint8, device=dev)
         self.out = B.TopK(torch.empty((p5.Q, p5.k), dtype=torch.int32, device=dev),
@@ -486,19 +505,24 @@ class PrefillLayer:
         self.B = B
 
     def layer(self):
-        self.B.absorb_query(self.q, self.W, out=self.qt)
+        self.B.absorb_query(self.q, self.W, out=self.qt, fp8=self.fp8)
         self.B.score_topk(self.cache, self.seq, self.pos, self.n, self.qt, self.w, self.k, ws=self.ws, out=self.out)
 
 
-def setup_prefill(B, synth, dev, bf, i32, tdev, n):
-    return PrefillLayer(B, synth, dev, bf, i32, tdev, n)
+def setup_prefill(B, synth, dev, bf, i32, tdev, n, fp8=False):
+    return PrefillLayer(B, synth, dev, bf, i32, tdev, n, fp8=fp8)
 
 
-def make_cache_from(g, B, tdev, i32, bf, dev):
+def make_cache_from(g, B, tdev, i32, bf, dev, fp8=False):
     import numpy as np
     import torch
-    pool = torch.zeros((g.num_pages, 64, g.r), dtype=bf, device=dev)
-    c = B.LatentCache(pool, i32(g.block_table), i32(g.lens))
+    if fp8:
+        pool = torch.zeros((g.num_pages, 64, g.r), dtype=torch.uint8, device=dev)
+        scales = torch.zeros((g.num_pages, 64, g.r // 128), dtype=torch.float32, device=dev)
+        c = B.LatentCache(pool, i32(g.block_table), i32(g.lens), scales)
+    else:
+        pool = torch.zeros((g.num_pages, 64, g.r), dtype=bf, device=dev)
+        c = B.LatentCache(pool, i32(g.block_table), i32(g.lens))
     for b in range(g.B):
         n = int(g.lens[b])
         B.append_latent(c, tdev(g.latent[b], bf), i32(np.full(n, b)), i32(np.arange(n)))

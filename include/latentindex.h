@@ -132,8 +132,10 @@ LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const
  * LI_BF16: bf16 inputs, fp32 accumulation, one round-to-nearest-even to bf16.
  * LI_FP32: fp32 throughout.  H <= 64; r in {64,128,256} and d in
  * {32,64,128,256} for LI_BF16; r in 1..256 and d in 1..1024 for LI_FP32.
- * LI_FP8: bf16 inputs, fp32 accumulation, then each (query, head) segment is
- * rotated and quantized as the cache is (LI_FP8 above); q_tilde is then one
+ * LI_FP8: bf16 inputs, the products summed in fp64 (exact for bf16 data of
+ * ordinary range) and rounded once to fp32, so the result does not depend on
+ * the summation order; then each (query, head) segment is rotated and
+ * quantized as the cache is (LI_FP8 above); q_tilde is then one
  * buffer of li_fp8_query_bytes(Q, H, r) bytes holding the codes [Q][H][r]
  * followed, at byte offset li_fp8_query_scale_offset(Q, H, r), by the
  * scales [Q][H][r/128] fp32.  r in {128, 256}, d in {32,64,128,256}.

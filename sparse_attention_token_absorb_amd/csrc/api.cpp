@@ -235,8 +235,8 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     // Decode scoring counts the first radix digit as it writes (the row is
     // read once more by selection anyway); prefill scoring is MFMA-bound and
     // leaves the count to the selection pass.
-    const bool fused_hist = scored && !(many && cache->dtype == LI_BF16);
     const bool fp8 = cache->dtype == LI_FP8;
+    const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8));
     hipError_t e = hipSuccess;
     if (scored) {
         if (fused_hist) {
@@ -251,7 +251,7 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         a.hist = fused_hist ? sw.hist : nullptr;
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
         if (fp8)
-            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r,
+            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, many,
                                      queries->max_valid, stream);
         else
             e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
@@ -319,7 +319,8 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     {
         li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
         if (cache->dtype == LI_FP8)
-            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, M, stream);
+            e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, false, M,
+                                     stream);
         else
             e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, M, stream);
     }

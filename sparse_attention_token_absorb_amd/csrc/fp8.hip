@@ -189,89 +189,96 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
 }
 
 // ---------------------------------------------------------------------------
-// Absorption into an FP8 query: qt = q W_dec (bf16 MFMA, fp32 accumulation)
-// for MB (query, head) rows and one 128-column segment per workgroup; the
-// fp32 result goes through LDS and each (row, segment) is rotated and
-// quantized by a half-wave.  MB = 128: each wave owns 32 rows and all four
-// 32-column tiles (many rows, W staged once per 128 rows).  MB = 32: the
-// four waves split the columns of 32 rows (few rows: 4x more workgroups).
+// Absorption into an FP8 query: qt = q W_dec with every bf16 x bf16 product
+// (exact in fp32) summed in fp64 and rounded once to fp32.  For bf16 inputs
+// of ordinary range the fp64 sum is exact, so qt is the correctly rounded
+// product whatever the summation order, and the FP8 codes do not depend on
+// the tiling.  Workgroup = MB (query, head) rows x one 128-column segment:
+// chunks of q (transposed) and W are staged in LDS as fp32, each thread
+// holds an RT x CT tile of fp64 accumulators; the fp32 results go back
+// through the same LDS and each (row, segment) is rotated and quantized by a
+// half-wave.
 // ---------------------------------------------------------------------------
 template <int R, int D, int MB>
 __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, uint8_t *codes, float *qscales,
                                                     int64_t QH)
 {
-    static_assert(MB == 32 || MB == 128, "row block");
+    static_assert(MB == 8 || MB == 32 || MB == 128, "row block");
     constexpr int NSEG = R / kSeg;
-    constexpr int LD = D + 8;          // halves per transposed W row
-    constexpr int KS = D / 16;
-    constexpr int ITEMS = (D / 2) * (kSeg / 8);
-    constexpr int NIT = (ITEMS + 255) / 256;
-    constexpr int OLD = kSeg + 4;      // floats per staged result row
-    constexpr int TPW = MB / 32;       // column tiles per wave
-    __shared__ __attribute__((aligned(16))) u16 wt[kSeg * LD];
-    __shared__ float s_out[MB * OLD];
+    constexpr int KC = D < 64 ? D : 64;      // k per staged chunk
+    constexpr int CT = MB == 128 ? 8 : 4;    // columns per thread
+    constexpr int NCG = kSeg / CT;           // column groups
+    constexpr int NRG = 256 / NCG;           // row groups
+    constexpr int RT = MB / NRG;             // rows per thread
+    static_assert(RT >= 1 && RT * NRG == MB, "thread tile");
+    constexpr int QLD = MB + 4;              // floats per staged k row of q
+    constexpr int WLD = kSeg + 4;            // floats per staged k row of W
+    constexpr int OLD = kSeg + 4;            // floats per staged result row
+    constexpr int STAGE = KC * (QLD + WLD);
+    constexpr int LDSF = STAGE > MB * OLD ? STAGE : MB * OLD;
+    __shared__ __attribute__((aligned(16))) float lds[LDSF];
+    float *s_q = lds;                        // [KC][QLD]
+    float *s_w = lds + KC * QLD;             // [KC][WLD]
+    float *s_out = lds;                      // [MB][OLD], once the sums are done
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    const int g = blockIdx.y;          // segment
+    const int g = blockIdx.y;                // segment
     const int c0 = g * kSeg;
-    const int rg = MB == 128 ? wv : 0; // this wave's 32-row group
     const int64_t mb0 = (int64_t)blockIdx.x * MB;
-    const int64_t m0 = mb0 + rg * 32;
+    const int tr = tid / NCG, tc = tid % NCG;
 
-    bf16x8 a[KS];
-    {
-        const int64_t m = m0 + (lane & 31);
-        const int64_t mc = m < QH ? m : QH - 1;
+    double acc[RT][CT];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = *(const bf16x8 *)(q + mc * D + s * 16 + (lane >> 5) * 8);
-        if (m >= QH) {
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                bf16x8 z = {};
-                a[s] = z;
+        for (int j = 0; j < CT; ++j) acc[i][j] = 0.0;
+
+#pragma unroll 1
+    for (int k0 = 0; k0 < D; k0 += KC) {
+        if (k0) __syncthreads(); // every thread is done with the previous chunk
+        for (int it = tid; it < MB * (KC / 8); it += 256) {
+            const int row = it % MB, kk = (it / MB) * 8;
+            const int64_t m = mb0 + row;
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (m < QH) raw = *(const u32x4 *)(q + m * D + k0 + kk);
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s_q[(kk + 2 * i) * QLD + row] = __uint_as_float(wd[i] << 16);
+                s_q[(kk + 2 * i + 1) * QLD + row] = __uint_as_float(wd[i] & 0xFFFF0000u);
             }
         }
-    }
-    bf16x8 r0[NIT], r1[NIT];
+        for (int it = tid; it < KC * (kSeg / 8); it += 256) {
+            const int kk = it / (kSeg / 8), cc = (it % (kSeg / 8)) * 8;
+            const u32x4 raw = *(const u32x4 *)(W + (int64_t)(k0 + kk) * R + c0 + cc);
+            float *dst = s_w + kk * WLD + cc;
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-        int it = tid + k * 256;
-        it = it < ITEMS ? it : ITEMS - 1;
-        const int e = (it / (kSeg / 8)) * 2;
-        const int t0 = c0 + (it % (kSeg / 8)) * 8;
-        r0[k] = *(const bf16x8 *)(W + (int64_t)e * R + t0);
-        r1[k] = *(const bf16x8 *)(W + (int64_t)(e + 1) * R + t0);
-    }
+            for (int i = 0; i < 4; ++i) {
+                dst[2 * i] = __uint_as_float(wd[i] << 16);
+                dst[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < KC; ++kk) {
+            double a[RT], b[CT];
 #pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-        const int it = tid + k * 256;
-        if (it < ITEMS) {
-            const int e = (it / (kSeg / 8)) * 2;
-            const int tl = (it % (kSeg / 8)) * 8;
-            const u16 *h0 = (const u16 *)&r0[k];
-            const u16 *h1 = (const u16 *)&r1[k];
+            for (int i = 0; i < RT; ++i) a[i] = (double)s_q[kk * QLD + tr * RT + i];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *(uint32_t *)(wt + (tl + i) * LD + e) = (uint32_t)h0[i] | ((uint32_t)h1[i] << 16);
+            for (int j = 0; j < CT; ++j) b[j] = (double)s_w[kk * WLD + tc * CT + j];
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int j = 0; j < CT; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
         }
     }
+    __syncthreads(); // the staged chunks are no longer read: the space becomes s_out
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) s_out[(tr * RT + i) * OLD + tc * CT + j] = (float)acc[i][j];
     __syncthreads();
-    // MFMA: this wave's 32 rows x TPW column tiles, staged as fp32 rows
-#pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-        const int nt = MB == 128 ? ti : wv;
-        f32x16 acc = {};
-        const int n = nt * 32 + (lane & 31);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bf16x8 b = *(const bf16x8 *)(wt + n * LD + s * 16 + (lane >> 5) * 8);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s_out[(rg * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * OLD + n] = acc[r];
-    }
-    __syncthreads();
+    const int lane = tid & 63, wv = tid >> 6;
     // quantization: the MB rows split over the 8 half-waves, NR rows each per pass
     constexpr int ROWS_PER_HALF = MB / 8;
     constexpr int NR = ROWS_PER_HALF < 8 ? ROWS_PER_HALF : 8;
@@ -487,6 +494,194 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill scoring from the FP8 cache: workgroup = 4 consecutive queries (one
+// per wave) sharing every tile through an NBUF-deep LDS ring, one barrier
+// per tile, page ids staged in LDS per split; the same slot layout and
+// scaled MFMA as the decode kernel.  Each wave moves a quarter of a tile's
+// codes and a quarter of its scales.  No first-digit counting here (the
+// selection pass counts it), so two workgroups share a CU.
+// ---------------------------------------------------------------------------
+constexpr int kPrefillMaxTilesF8 = 2048; // max tiles per split (their page ids sit in LDS)
+
+template <int R, int HB, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill_fp8(
+    ScoreArgs a, const float *pool_scales, int64_t qscale_off, int tiles_per_split)
+{
+    constexpr int NSEG = R / kSeg;
+    constexpr int CODE_BYTES = kTile * R;
+    constexpr int SLOT = CODE_BYTES + 256;
+    constexpr int NIC = CODE_BYTES / 1024;
+    constexpr int NIW = NIC / 4;           // code DMA instructions per wave per tile
+    constexpr int CH = R / 16;
+    constexpr int KS = R / 64;
+    static_assert(NIW >= 1, "tile must split over 4 waves");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * SLOT];
+    __shared__ int32_t s_page_raw[kPrefillMaxTilesF8 / 2 + 2];
+    lds_u8 *ring = (lds_u8 *)ring_raw;
+    lds_i32 *s_page = (lds_i32 *)s_page_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qbase = blockIdx.x * 4;
+    const_i32_t *qseq = (const_i32_t *)a.qseq;
+    const_i32_t *qpos = (const_i32_t *)a.qpos;
+    const_i32_t *slen = (const_i32_t *)a.seq_lens;
+    int sb[4], sn[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int qq = qbase + u;
+        sb[u] = qq < a.Q ? qseq[qq] : -1;
+        sn[u] = qq < a.Q ? (int)min64(valid_rows(qpos[qq], slen[sb[u]]), a.max_rows) : 0;
+    }
+    const int q = qbase + wv;
+    int my_b = -1, my_n = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (u == wv) {
+            my_b = sb[u];
+            my_n = sn[u];
+        }
+    // this wave's query (zero codes past the batch)
+    i32x8 qa[HB][KS];
+    int sa[HB][NSEG];
+    float wr[HB][16];
+    {
+        const bool live = q < a.Q;
+        const int qc_i = live ? q : 0;
+        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)qc_i * a.H * R;
+        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)qc_i * a.H * NSEG;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const bool hv = live && h < a.H;
+            const int hc = h < a.H ? h : a.H - 1;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
+                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
+                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (!hv) {
+                    i32x8 z = {};
+                    v = z;
+                }
+                qa[hb][s] = v;
+            }
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g)
+                sa[hb][g] = hv ? (int)((__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu) : 127;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                wr[hb][r] = live && hh < a.H ? a.w[(int64_t)qc_i * a.H + hh] : 0.0f;
+            }
+        }
+    }
+    float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
+    const uint8_t *pool = (const uint8_t *)a.pool;
+    const int nr = lane & 31, gk = lane >> 5;
+
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+        const int b = sb[u];
+        bool skip = b < 0;
+        int nmax = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (v < u && sb[v] == b) skip = true;
+            if (sb[v] == b) nmax = max(nmax, sn[v]);
+        }
+        if (skip) continue;
+        const bool active = (my_b == b) && (q < a.Q);
+        const int ntiles_all = (nmax + kTile - 1) / kTile;
+        const int ts = blockIdx.y * tiles_per_split;
+        const int te = min(ts + tiles_per_split, ntiles_all);
+        if (ts >= te) continue;
+        const int nt = te - ts;
+        const int p0 = ts >> 1;
+        const int np = ((te - 1) >> 1) - p0 + 1;
+        __syncthreads(); // the previous pass is done with the ring and the page ids
+        for (int pi = threadIdx.x; pi < np; pi += 256) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
+        __syncthreads();
+        auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
+        auto issue = [&](int i, int page) {
+            const int64_t base = (int64_t)page * kPage + ((ts + i) & 1) * kTile; // first slot of the tile
+            lds_u8 *slot = ring + (i % NBUF) * SLOT;
+#pragma unroll
+            for (int j = 0; j < NIW; ++j) {
+                const int ii = wv * NIW + j;
+                const int p = ii * 64 + lane;
+                const int rr = p / CH, cs = p % CH;
+                const int c = cs ^ (rr % CH);
+                dma16(pool + (base + rr) * R + c * 16, slot + ii * 1024);
+            }
+            // scales: this wave's quarter (16 lanes x 4 bytes) of the tile's 32 x NSEG
+            const int f = wv * 16 + (lane & 15);
+            const int row = f / NSEG < kTile ? f / NSEG : kTile - 1;
+            if (lane < 16) dma4(pool_scales + (base + row) * NSEG + (f % NSEG), slot + CODE_BYTES + wv * 64);
+        };
+        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i));
+#pragma unroll 1
+        for (int i = 0; i < nt; ++i) {
+            const int inext = i + NBUF - 1;
+            const int pnext = inext < nt ? page_of(inext) : 0; // read before the barrier
+            // tile i landed (this wave's part), tiles i+1..i+NBUF-2 may still fly
+            wait_after<NIW + 1, NBUF - 2>(min(NBUF - 2, nt - 1 - i));
+            wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
+            if (inext < nt) issue(inext, pnext); // into tile i-1's slot
+            if (active) {
+                const lds_u8 *slot = ring + (i % NBUF) * SLOT;
+                int scb[NSEG];
+#pragma unroll
+                for (int g = 0; g < NSEG; ++g)
+                    scb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + CODE_BYTES +
+                                                                                       (nr * NSEG + g) * 4) >> 23) &
+                                   0xFFu);
+                f32x16 acc[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    f32x16 z = {};
+                    acc[hb] = z;
+                }
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int c = 4 * s + 2 * gk;
+                    const u32x4 lo = *(const lds_u32x4 *)(slot + (nr * CH + (c ^ (nr % CH))) * 16);
+                    const u32x4 hi = *(const lds_u32x4 *)(slot + (nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+                    const i32x8 bv = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    const int g = (s * 64) / kSeg;
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+                        acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[hb][s], bv, acc[hb], 0, 0, 0,
+                                                                                  sa[hb][g], 0, scb[g]);
+                }
+                const float pv = epilogue<HB>(acc, wr);
+                const int j = (ts + i) * kTile + lane;
+                if (lane < 32 && j < my_n) out[j] = pv;
+            }
+        }
+    }
+}
+
+template <int R, int HB>
+hipError_t launch_prefill_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
+                                 hipStream_t s)
+{
+    constexpr int NBUF = 6;
+    const int64_t tiles = (max_rows + kTile - 1) / kTile;
+    const int qblocks = (a.Q + 3) / 4;
+    int64_t splits = 1;
+    if (qblocks < 512) splits = std::min<int64_t>((512 + qblocks - 1) / qblocks, tiles);
+    if (splits < 1) splits = 1;
+    int64_t tps = (tiles + splits - 1) / splits;
+    if (tps > kPrefillMaxTilesF8) tps = kPrefillMaxTilesF8;
+    splits = (tiles + tps - 1) / tps;
+    hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s, a,
+                       pool_scales, qscale_off, (int)tps);
+    return hipGetLastError();
+}
+
 template <int R, int HB>
 hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
                                hipStream_t s)
@@ -508,9 +703,13 @@ hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int
 }
 
 template <int R>
-hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
-                              hipStream_t s)
+hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, bool prefill,
+                              int64_t max_rows, hipStream_t s)
 {
+    if (prefill) {
+        if (a.H <= 32) return launch_prefill_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s);
+        return launch_prefill_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
+    }
     if (a.H <= 32) return launch_score_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s);
     return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
 }
@@ -518,12 +717,16 @@ hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int6
 template <int R, int D>
 void launch_absorb_fp8_rd(const u16 *q, const u16 *W, uint8_t *codes, float *scales, int64_t QH, hipStream_t s)
 {
-    if ((QH + 127) / 128 >= 256) // many rows: W staged once per 128 rows
+    // many rows: big register tiles; few rows: small blocks, more workgroups
+    if ((QH + 127) / 128 >= 256)
         hipLaunchKernelGGL((k_absorb_fp8<R, D, 128>), dim3((unsigned)((QH + 127) / 128), R / kSeg), dim3(256), 0, s,
                            q, W, codes, scales, QH);
-    else
+    else if ((QH + 31) / 32 >= 64)
         hipLaunchKernelGGL((k_absorb_fp8<R, D, 32>), dim3((unsigned)((QH + 31) / 32), R / kSeg), dim3(256), 0, s, q,
                            W, codes, scales, QH);
+    else
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 8>), dim3((unsigned)((QH + 7) / 8), R / kSeg), dim3(256), 0, s, q, W,
+                           codes, scales, QH);
 }
 
 template <int R>
@@ -573,11 +776,12 @@ hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH,
 }
 
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
-                            int64_t max_rows, hipStream_t s)
+                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s)
 {
     if (a.Q <= 0 || max_rows <= 0) return hipSuccess;
-    if (r == 256) return launch_score_fp8_r<256>(a, pool_scales, qscale_off, max_rows, s);
-    if (r == 128) return launch_score_fp8_r<128>(a, pool_scales, qscale_off, max_rows, s);
+    const bool prefill = many_queries_per_seq && a.cand == nullptr && a.hist == nullptr;
+    if (r == 256) return launch_score_fp8_r<256>(a, pool_scales, qscale_off, prefill, max_rows, s);
+    if (r == 128) return launch_score_fp8_r<128>(a, pool_scales, qscale_off, prefill, max_rows, s);
     return hipErrorInvalidValue;
 }
 

@@ -58,13 +58,14 @@ hipError_t launch_absorb(const void *q, const void *W, void *qt, int64_t QH, int
                          hipStream_t s);
 
 // Segmented FP8: query buffer layout, append (rotate + quantize), absorption
-// into FP8, and FP8 scoring (decode-style kernel for every call).
+// into FP8, and FP8 scoring (the prefill kernel when many queries share a
+// sequence and no histogram is asked for; the decode kernel otherwise).
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r);
 hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
                              const int32_t *seq, const int32_t *pos, int T, hipStream_t s);
 hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH, int d, int r, hipStream_t s);
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
-                            int64_t max_rows, hipStream_t s);
+                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s);
 
 // Append rows into the paged pool.
 hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
