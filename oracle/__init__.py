@@ -20,6 +20,11 @@ per-layer steps into the two selection schemes of the LatentIndex paper
                   only those and takes its own top-min(k, |cand|)  (§3.2, §C.4)
   O6 explicit     score through rebuilt keys K_j = W_dec c_j       (§1, §3.1)
   O8 counters     rows scored per query and group                  (§3.4, §B.3)
+  O9 rope         rotate the latent's rotary sources by the native phase
+                  of their position before caching                  (§A.2, §A.4)
+  O10 absorb_rope structured absorption: per-frequency complex decoder
+                  coefficients, dense NoPE decoder, output bias     (§A.2-§A.4)
+  O11 explicit    scores through rebuilt post-RoPE native keys      (§3.1, §A.2)
 
 Parity: every function here is pinned by the CPU tests (hand-derived worked
 examples under tests/golden/, the absorption identity, brute-force selection
@@ -68,7 +73,7 @@ def _load(path: Optional[str] = None):
 def _bind(lib):
     lib.lio_absorb.argtypes = [_dp, _dp, _i64, _i64, _i64, _i64, _dp]
     lib.lio_absorb.restype = None
-    lib.lio_score.argtypes = [_dp, _dp, _dp, _ip, _i64, _i64, _i64, _dp]
+    lib.lio_score.argtypes = [_dp, _dp, _dp, _dp, _ip, _i64, _i64, _i64, _dp]
     lib.lio_score.restype = None
     lib.lio_score_explicit.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _dp]
     lib.lio_score_explicit.restype = None
@@ -89,8 +94,15 @@ def _bind(lib):
     lib.lio_pow2_exponent.restype = ctypes.c_int
     lib.lio_quantize_rows.argtypes = [_fp, _i64, _i64, _u8p, _fp]
     lib.lio_quantize_rows.restype = None
-    lib.lio_score_fp8.argtypes = [_u8p, _fp, _dp, _u8p, _fp, _ip, _i64, _i64, _i64, _dp]
+    lib.lio_score_fp8.argtypes = [_u8p, _fp, _dp, _dp, _u8p, _fp, _ip, _i64, _i64, _i64, _dp]
     lib.lio_score_fp8.restype = None
+    lib.lio_rope_rotate.argtypes = [_dp, _ip, _i64, _i64, _i64, _i64, ctypes.c_double]
+    lib.lio_rope_rotate.restype = None
+    lib.lio_absorb_rope.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _dp, _dp]
+    lib.lio_absorb_rope.restype = None
+    lib.lio_score_explicit_rope.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _ip, _i64, _i64, _i64, _i64, _i64, _i64,
+                                            ctypes.c_double, _dp]
+    lib.lio_score_explicit_rope.restype = None
     return lib
 
 
@@ -130,16 +142,21 @@ def absorb(q: np.ndarray, W: np.ndarray) -> np.ndarray:
 
 
 def score(qt: np.ndarray, w: np.ndarray, C: np.ndarray, n: Optional[int] = None,
-          rows: Optional[np.ndarray] = None) -> np.ndarray:
+          rows: Optional[np.ndarray] = None, bias: Optional[np.ndarray] = None) -> np.ndarray:
     """O3: scores of latent rows 0..n-1 (or of ``rows``) for one absorbed query.
 
-    qt [H][r], w [H], C [*][r].
+    qt [H][r], w [H], C [*][r]; bias [H] (the absorbed decoder bias) or None.
     """
     qt = _f64(qt)
     w = _f64(w)
     C = _f64(C)
     H, r = qt.shape
     assert C.shape[1] == r and w.shape == (H,)
+    bp = None
+    if bias is not None:
+        bias = _f64(bias)
+        assert bias.shape == (H,)
+        bp = _ptr(bias, _dp)
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int32)
         assert rows.size == 0 or (rows.min() >= 0 and rows.max() < C.shape[0])
@@ -151,7 +168,7 @@ def score(qt: np.ndarray, w: np.ndarray, C: np.ndarray, n: Optional[int] = None,
         rp = None
     out = np.empty(m, dtype=np.float64)
     if m:
-        _load().lio_score(_ptr(qt, _dp), _ptr(w, _dp), _ptr(C, _dp), rp, m, H, r, _ptr(out, _dp))
+        _load().lio_score(_ptr(qt, _dp), _ptr(w, _dp), bp, _ptr(C, _dp), rp, m, H, r, _ptr(out, _dp))
     return out
 
 
@@ -246,9 +263,11 @@ def quantize_rows(x) -> tuple:
     return codes, scales
 
 
-def score_fp8(qc, qs, w, cc, cs, n: Optional[int] = None, rows: Optional[np.ndarray] = None) -> np.ndarray:
+def score_fp8(qc, qs, w, cc, cs, n: Optional[int] = None, rows: Optional[np.ndarray] = None,
+              bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Scores from FP8 operands: qc [H][r] codes, qs [H][r/128], w [H],
-    cc [*][r] codes, cs [*][r/128]; rows 0..n-1 or the given ``rows``."""
+    cc [*][r] codes, cs [*][r/128]; rows 0..n-1 or the given ``rows``;
+    bias [H] (the absorbed decoder bias, added before the ReLU) or None."""
     qc = np.ascontiguousarray(qc, dtype=np.uint8)
     qs = np.ascontiguousarray(qs, dtype=np.float32)
     w = _f64(w)
@@ -264,9 +283,14 @@ def score_fp8(qc, qs, w, cc, cs, n: Optional[int] = None, rows: Optional[np.ndar
     else:
         m = cc.shape[0] if n is None else int(n)
         rp = None
+    bp = None
+    if bias is not None:
+        bias = _f64(bias)
+        assert bias.shape == (H,)
+        bp = _ptr(bias, _dp)
     out = np.empty(m, dtype=np.float64)
     if m:
-        _load().lio_score_fp8(_ptr(qc, _u8p), _ptr(qs, _fp), _ptr(w, _dp), _ptr(cc, _u8p), _ptr(cs, _fp), rp, m,
+        _load().lio_score_fp8(_ptr(qc, _u8p), _ptr(qs, _fp), _ptr(w, _dp), bp, _ptr(cc, _u8p), _ptr(cs, _fp), rp, m,
                               H, r, _ptr(out, _dp))
     return out
 
@@ -275,6 +299,65 @@ def absorb_fp8(q: np.ndarray, W: np.ndarray) -> tuple:
     """Absorbed query in FP8: qt = q W (fp64, then rounded once to fp32),
     rotated and quantized per 128-element segment."""
     return quantize_rows(absorb(q, W).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# RoPE-compatible structured decoder (§A.2-§A.4; see li_oracle.c)
+# ----------------------------------------------------------------------------
+def rope_rotate(rows, pos, F: int, S: int, base: float = 10000.0) -> np.ndarray:
+    """O9: latent rows [n][r] with their S*F source pairs rotated by the
+    native rotary phase of their positions (fp64; a new array)."""
+    x = _f64(rows).copy()
+    n = x.shape[0] if x.ndim == 2 else 0
+    r = x.shape[-1]
+    assert 2 * S * F <= r
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    assert pos.shape == (n,)
+    if n and S * F:
+        _load().lio_rope_rotate(_ptr(x, _dp), _ptr(pos, _ip), n, r, F, S, float(base))
+    return x
+
+
+def absorb_rope(q, D, Wn, beta, F: int, S: int) -> tuple:
+    """O10: structured absorption.  q [..., H, 2F + d_nope] (post-RoPE),
+    D [F][S][2] decoder coefficients (re, im), Wn [d_nope][r_nope], beta
+    [d_nope] -> (qt [..., H, 2SF + r_nope], bias [..., H])."""
+    q = _f64(q)
+    D = _f64(D).reshape(F, S, 2) if F * S else np.zeros((0,), dtype=np.float64)
+    Wn = _f64(Wn)
+    beta = _f64(beta)
+    d_nope, r_nope = Wn.shape
+    assert q.shape[-1] == 2 * F + d_nope and beta.shape == (d_nope,)
+    lead = q.shape[:-1]
+    QH = int(np.prod(lead)) if lead else 1
+    qt = np.empty(lead + (2 * S * F + r_nope,), dtype=np.float64)
+    b = np.empty(lead, dtype=np.float64)
+    D = np.ascontiguousarray(D)
+    _load().lio_absorb_rope(_ptr(q, _dp), _ptr(D, _dp), _ptr(Wn, _dp), _ptr(beta, _dp), QH, F, S, d_nope, r_nope,
+                            _ptr(qt, _dp), _ptr(b, _dp))
+    return qt, b
+
+
+def score_explicit_rope(q, D, Wn, beta, w, C, pos, F: int, S: int, base: float = 10000.0) -> np.ndarray:
+    """O11: scores of unrotated latent rows C [n][r] at positions ``pos``
+    through the rebuilt post-RoPE native keys of the layer (q [H][d])."""
+    q = _f64(q)
+    w = _f64(w)
+    C = _f64(C)
+    D = np.ascontiguousarray(_f64(D).reshape(F, S, 2) if F * S else np.zeros((1,)))
+    Wn = _f64(Wn)
+    beta = _f64(beta)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    H = q.shape[0]
+    d_nope, r_nope = Wn.shape
+    n = C.shape[0]
+    assert q.shape == (H, 2 * F + d_nope) and C.shape[1] == 2 * S * F + r_nope and pos.shape == (n,)
+    out = np.empty(n, dtype=np.float64)
+    if n:
+        _load().lio_score_explicit_rope(_ptr(q, _dp), _ptr(D, _dp), _ptr(Wn, _dp), _ptr(beta, _dp), _ptr(w, _dp),
+                                        _ptr(C, _dp), _ptr(pos, _ip), n, H, F, S, d_nope, r_nope, float(base),
+                                        _ptr(out, _dp))
+    return out
 
 
 # ----------------------------------------------------------------------------

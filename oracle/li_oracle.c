@@ -44,12 +44,15 @@ void lio_absorb(const double *q, const double *W, int64_t Q, int64_t H, int64_t 
 /*
  * Layer-specific scoring of latent rows (§3.1, §B.2: the layer keeps its own
  * query and head weights and scores the shared cache):
- *   s[i] = sum_h w[h] * max(0, sum_t qt[h][t] * C[row_i][t])
- * where row_i = rows[i] when rows != NULL, else row_i = i.
- * qt: [H][r] one absorbed query   w: [H]   C: latent [*][r]   s: [m]
+ *   s[i] = sum_h w[h] * max(0, sum_t qt[h][t] * C[row_i][t] + b[h])
+ * where row_i = rows[i] when rows != NULL, else row_i = i, and b[h] is the
+ * absorbed decoder bias (§A.3: each layer's NoPE decoder carries an output
+ * bias; its dot with the query is one number per head), 0 when bias == NULL.
+ * qt: [H][r] one absorbed query   w: [H]   bias: [H] or NULL
+ * C: latent [*][r]   s: [m]
  */
-void lio_score(const double *qt, const double *w, const double *C, const int32_t *rows, int64_t m,
-               int64_t H, int64_t r, double *s)
+void lio_score(const double *qt, const double *w, const double *bias, const double *C, const int32_t *rows,
+               int64_t m, int64_t H, int64_t r, double *s)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i) {
@@ -60,6 +63,7 @@ void lio_score(const double *qt, const double *w, const double *C, const int32_t
             double dot = 0.0;
             for (int64_t t = 0; t < r; ++t)
                 dot += qt[h * r + t] * c[t];
+            if (bias) dot += bias[h];
             total += w[h] * (dot > 0.0 ? dot : 0.0);
         }
         s[i] = total;
@@ -247,12 +251,13 @@ void lio_quantize_rows(const float *x, int64_t rows, int64_t r, uint8_t *codes, 
 /*
  * Score from FP8 rows (§3.1 score on the rotated, quantized operands):
  *   s[i] = sum_h w[h] max(0, sum_g qs[h][g] cs[row_i][g]
- *                                 sum_{t in segment g} dec(qc[h][t]) dec(cc[row_i][t]))
+ *                                 sum_{t in segment g} dec(qc[h][t]) dec(cc[row_i][t])
+ *                            + b[h])      (b: the absorbed decoder bias, or 0)
  * qc: [H][r] codes, qs: [H][r/128]; cc: [*][r] codes, cs: [*][r/128];
  * row_i = rows[i] when rows != NULL, else i.
  */
-void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const uint8_t *cc, const float *cs,
-                   const int32_t *rows, int64_t m, int64_t H, int64_t r, double *s)
+void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const double *bias, const uint8_t *cc,
+                   const float *cs, const int32_t *rows, int64_t m, int64_t H, int64_t r, double *s)
 {
     const int64_t nseg = r / 128;
 #pragma omp parallel for schedule(static)
@@ -267,9 +272,141 @@ void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const ui
                     seg += lio_e4m3_decode(qc[h * r + g * 128 + t]) * lio_e4m3_decode(cc[row * r + g * 128 + t]);
                 dot += (double)qs[h * nseg + g] * (double)cs[row * nseg + g] * seg;
             }
+            if (bias) dot += bias[h];
             total += w[h] * (dot > 0.0 ? dot : 0.0);
         }
         s[i] = total;
+    }
+}
+
+/*
+ * RoPE-compatible structured decoder (§A.2, §A.4, §A.3; §3.1: the RoPE and
+ * NoPE branches are concatenated and cached once per group).
+ *
+ * Latent row layout: the first 2*S*F elements are S shared complex sources
+ * for each of F rotary frequencies, stored as (re, im) pairs; pair j holds
+ * source s = j / F at frequency f = j % F.  The remaining r_nope elements are
+ * the NoPE latent.  The native indexer key of a layer is
+ * [k_rope (2F: F complex, (re, im) pairs) | k_nope (d_nope)].
+ *
+ * Rotary phase of frequency f at position p: p * theta_f with
+ * theta_f = base^(-2f / (2F)), the native RoPE of a 2F-wide rotary key.
+ */
+static double lio_theta(int64_t f, int64_t F, double base)
+{
+    return pow(base, -(double)(2 * f) / (double)(2 * F));
+}
+
+/*
+ * The sources share the native rotary phase, so the cached latent is rotated
+ * before caching (§A.2): each source pair of row i is multiplied by
+ * exp(i * pos[i] * theta_f).  rows: [n][r], in place; the NoPE part is left
+ * as it is.
+ */
+void lio_rope_rotate(double *rows, const int32_t *pos, int64_t n, int64_t r, int64_t F, int64_t S, double base)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double *x = rows + i * r;
+        for (int64_t j = 0; j < S * F; ++j) {
+            const int64_t f = j % F;
+            const double ang = (double)pos[i] * lio_theta(f, F, base);
+            const double c = cos(ang), sn = sin(ang);
+            const double re = x[2 * j], im = x[2 * j + 1];
+            x[2 * j] = re * c - im * sn;
+            x[2 * j + 1] = re * sn + im * c;
+        }
+    }
+}
+
+/*
+ * Absorption of the structured decoder into a post-RoPE query (§A.2: the
+ * decoder is absorbed into post-RoPE queries; §A.4: per frequency, layer
+ * decoder coefficients D[f][s] over shared complex sources; §A.3: a dense
+ * NoPE decoder Wn and an output bias beta).
+ *   rope slot (s, f):  qt = q_f * conj(D[f][s])     (q_f = q[2f] + i q[2f+1])
+ *   NoPE column t:     qt = sum_e q[2F + e] * Wn[e][t]
+ *   bias:              b  = sum_e q[2F + e] * beta[e]
+ * q: [QH][2F + d_nope]; D: [F][S][2] (re, im); Wn: [d_nope][r_nope];
+ * beta: [d_nope]; qt: [QH][2SF + r_nope]; b: [QH].
+ */
+void lio_absorb_rope(const double *q, const double *D, const double *Wn, const double *beta, int64_t QH,
+                     int64_t F, int64_t S, int64_t d_nope, int64_t r_nope, double *qt, double *b)
+{
+    const int64_t d = 2 * F + d_nope, r = 2 * S * F + r_nope;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < QH; ++i) {
+        const double *qi = q + i * d;
+        double *out = qt + i * r;
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t f = 0; f < F; ++f) {
+                const double a = qi[2 * f], bb = qi[2 * f + 1];
+                const double c = D[(f * S + s) * 2], e = D[(f * S + s) * 2 + 1];
+                /* (a + i bb)(c - i e) */
+                out[2 * (s * F + f)] = a * c + bb * e;
+                out[2 * (s * F + f) + 1] = bb * c - a * e;
+            }
+        for (int64_t t = 0; t < r_nope; ++t) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < d_nope; ++e)
+                acc += qi[2 * F + e] * Wn[e * r_nope + t];
+            out[2 * S * F + t] = acc;
+        }
+        double acc = 0.0;
+        for (int64_t e = 0; e < d_nope; ++e)
+            acc += qi[2 * F + e] * beta[e];
+        b[i] = acc;
+    }
+}
+
+/*
+ * The same score the long way (§3.1, §A.2): rebuild each row's native key
+ * from the unrotated latent, apply the native RoPE at the row's position to
+ * the decoded rotary key, and score with the un-absorbed post-RoPE query:
+ *   k_f    = exp(i pos theta_f) * sum_s D[f][s] z_{s,f}
+ *   k_nope = Wn^T n + beta
+ *   s[j]   = sum_h w[h] max(0, q_h . [k_rope | k_nope])
+ * q: [H][2F + d_nope]; C: unrotated latent rows [n][2SF + r_nope]; pos: [n].
+ */
+void lio_score_explicit_rope(const double *q, const double *D, const double *Wn, const double *beta, const double *w,
+                             const double *C, const int32_t *pos, int64_t n, int64_t H, int64_t F, int64_t S,
+                             int64_t d_nope, int64_t r_nope, double base, double *s)
+{
+    const int64_t d = 2 * F + d_nope, r = 2 * S * F + r_nope;
+#pragma omp parallel
+    {
+        double *key = (double *)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            const double *c = C + j * r;
+            for (int64_t f = 0; f < F; ++f) {
+                double kr = 0.0, ki = 0.0;
+                for (int64_t src = 0; src < S; ++src) {
+                    const double dr = D[(f * S + src) * 2], di = D[(f * S + src) * 2 + 1];
+                    const double zr = c[2 * (src * F + f)], zi = c[2 * (src * F + f) + 1];
+                    kr += dr * zr - di * zi;
+                    ki += dr * zi + di * zr;
+                }
+                const double ang = (double)pos[j] * lio_theta(f, F, base);
+                key[2 * f] = kr * cos(ang) - ki * sin(ang);
+                key[2 * f + 1] = kr * sin(ang) + ki * cos(ang);
+            }
+            for (int64_t e = 0; e < d_nope; ++e) {
+                double acc = beta[e];
+                for (int64_t t = 0; t < r_nope; ++t)
+                    acc += Wn[e * r_nope + t] * c[2 * S * F + t];
+                key[2 * F + e] = acc;
+            }
+            double total = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e)
+                    dot += q[h * d + e] * key[e];
+                total += w[h] * (dot > 0.0 ? dot : 0.0);
+            }
+            s[j] = total;
+        }
+        free(key);
     }
 }
 

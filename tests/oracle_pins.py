@@ -15,6 +15,7 @@ broken copies of it, so each pin is known to catch the mistakes it targets.
 from __future__ import annotations
 
 import itertools
+import math
 import json
 import os
 
@@ -491,6 +492,112 @@ def pin_rotation_keeps_the_score():
     cr = np.stack([rot(x) for x in C])
     a, b = oracle.score(q, w, C), oracle.score(qr, w, cr)
     assert np.max(np.abs(a - b)) <= 1e-4 * (1 + np.max(np.abs(a)))
+
+
+# ----------------------------------------------------------------------------
+# RoPE-compatible structured decoder (§A.2-§A.4)
+# ----------------------------------------------------------------------------
+def pin_worked_absorb_rope():
+    g = _golden("worked_rope.json")["absorb"]
+    qt, b = oracle.absorb_rope(np.array([g["q"]]), np.array(g["D"]), np.array(g["Wn"]), np.array(g["beta"]), 1, 1)
+    assert np.array_equal(qt[0], np.array(g["qt"])), qt
+    assert b[0] == g["bias"], b
+
+
+def pin_worked_rope_rotation():
+    g = _golden("worked_rope.json")["rotation"]
+    th = g["theta"]
+    p = g["pos"]
+    c0, s0 = math.cos(p * th[0]), math.sin(p * th[0])
+    c1, s1 = math.cos(p * th[1]), math.sin(p * th[1])
+    want = np.array([c0, s0, -s1, c1, 2 * c0, 2 * s0, 0.0, 0.0, 5.0])
+    got = oracle.rope_rotate(np.array([g["row"]]), np.array([p]), g["F"], g["S"], g["base"])[0]
+    assert np.allclose(got, want, rtol=0, atol=1e-15), (got, want)
+
+
+def pin_rope_zero_position_composition_and_norm():
+    rng = np.random.default_rng(21)
+    F, S, rn = 8, 2, 5
+    X = rng.standard_normal((6, 2 * S * F + rn))
+    assert np.array_equal(oracle.rope_rotate(X, np.zeros(6), F, S), X)
+    p1 = rng.integers(0, 60000, 6)
+    p2 = rng.integers(0, 60000, 6)
+    twice = oracle.rope_rotate(oracle.rope_rotate(X, p1, F, S), p2, F, S)
+    once = oracle.rope_rotate(X, p1 + p2, F, S)
+    assert np.allclose(twice, once, rtol=0, atol=1e-9)
+    Y = oracle.rope_rotate(X, p1, F, S)
+    pr = lambda Z: np.hypot(Z[:, 0:2 * S * F:2], Z[:, 1:2 * S * F:2])
+    assert np.allclose(pr(Y), pr(X), rtol=1e-14, atol=0)
+    assert np.array_equal(Y[:, 2 * S * F:], X[:, 2 * S * F:])
+
+
+def _rope_case(rng, H=3, F=4, S=2, dn=6, rn=8, n=60):
+    q = rng.standard_normal((H, 2 * F + dn))
+    D = rng.standard_normal((F, S, 2))
+    Wn = rng.standard_normal((dn, rn))
+    beta = rng.standard_normal(dn)
+    w = rng.random(H) + 0.1
+    C = rng.standard_normal((n, 2 * S * F + rn))
+    pos = rng.integers(0, 131072, n)
+    return q, D, Wn, beta, w, C, pos
+
+
+def pin_rope_absorption_identity():
+    rng = np.random.default_rng(22)
+    for (F, S, dn, rn) in ((4, 2, 6, 8), (3, 1, 5, 4), (6, 3, 2, 7)):
+        q, D, Wn, beta, w, C, pos = _rope_case(rng, F=F, S=S, dn=dn, rn=rn)
+        qt, b = oracle.absorb_rope(q, D, Wn, beta, F, S)
+        latent = oracle.score(qt, w, oracle.rope_rotate(C, pos, F, S), bias=b)
+        explicit = oracle.score_explicit_rope(q, D, Wn, beta, w, C, pos, F, S)
+        assert np.allclose(latent, explicit, rtol=1e-11, atol=1e-11), np.max(np.abs(latent - explicit))
+        assert np.mean(latent > 0) > 0.5
+
+
+def pin_rope_without_rotary_part_is_plain_absorption():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((2, 3, 5))
+    Wn = rng.standard_normal((5, 7))
+    qt, b = oracle.absorb_rope(q, np.zeros((0,)), Wn, np.zeros(5), 0, 0)
+    assert np.allclose(qt, oracle.absorb(q, Wn), rtol=1e-14, atol=1e-14)
+    assert np.array_equal(b, np.zeros((2, 3)))
+    C = rng.standard_normal((9, 7))
+    w = rng.random(3)
+    e1 = oracle.score_explicit_rope(q[0], np.zeros((0,)), Wn, np.zeros(5), w, C, np.arange(9), 0, 0)
+    e2 = oracle.score_explicit(q[0], Wn, w, C)
+    assert np.allclose(e1, e2, rtol=1e-13, atol=1e-13)
+
+
+def pin_worked_bias_before_relu():
+    g = _golden("worked_rope.json")["bias_relu"]
+    for bias, want in g["cases"]:
+        got = oracle.score(np.array(g["qt"]), np.array(g["w"]), np.array(g["c"]), bias=np.array([bias]))
+        assert got[0] == want, (bias, got)
+
+
+def pin_bias_is_an_extra_latent_column():
+    rng = np.random.default_rng(24)
+    H, r, n = 4, 9, 30
+    qt = rng.standard_normal((H, r))
+    b = rng.standard_normal(H) * 2.0
+    w = rng.random(H)
+    C = rng.standard_normal((n, r))
+    s1 = oracle.score(qt, w, C, bias=b)
+    s2 = oracle.score(np.concatenate([qt, b[:, None]], axis=1), w, np.concatenate([C, np.ones((n, 1))], axis=1))
+    assert np.array_equal(s1, s2)
+    assert np.any(s1 != oracle.score(qt, w, C))
+
+
+def pin_fp8_score_with_bias_is_plain_score_of_dequantized_rows():
+    rng = np.random.default_rng(25)
+    H, r, n = 5, 256, 40
+    qc, qs = oracle.quantize_rows(rng.standard_normal((H, r)).astype(np.float32))
+    cc, cs = oracle.quantize_rows(rng.standard_normal((n, r)).astype(np.float32))
+    b = rng.standard_normal(H) * 3.0
+    w = rng.random(H)
+    deq = lambda c, s: oracle.e4m3_decode(c) * np.repeat(s.astype(np.float64), 128, axis=-1)
+    want = oracle.score(deq(qc, qs), w, deq(cc, cs), bias=b)
+    got = oracle.score_fp8(qc, qs, w, cc, cs, bias=b)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -44,8 +44,22 @@ C_MUTANTS = {
     "pow2_off_by_one": ("int e = (2.0f * f <= 1.75f) ? E - 9 : E - 8;", "int e = (2.0f * f <= 1.75f) ? E - 8 : E - 8;"),
     "fp8_score_drops_scales": ("dot += (double)qs[h * nseg + g] * (double)cs[row * nseg + g] * seg;",
                                "dot += seg;"),
-    "fp8_score_relu_after_sum": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;\n    }\n}\n\n/* Number",
-                                 "total += w[h] * dot;\n        }\n        s[i] = total > 0.0 ? total : 0.0;\n    }\n}\n\n/* Number"),
+    "fp8_score_relu_after_sum": ("total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;\n    }\n}\n\n/*\n * RoPE",
+                                 "total += w[h] * dot;\n        }\n        s[i] = total > 0.0 ? total : 0.0;\n    }\n}\n\n/*\n * RoPE"),
+    "fp8_score_drops_bias": ("if (bias) dot += bias[h];\n            total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;\n    }\n}\n\n/*\n * RoPE",
+                             "total += w[h] * (dot > 0.0 ? dot : 0.0);\n        }\n        s[i] = total;\n    }\n}\n\n/*\n * RoPE"),
+    "score_bias_after_relu": ("if (bias) dot += bias[h];\n            total += w[h] * (dot > 0.0 ? dot : 0.0);",
+                              "total += w[h] * (dot > 0.0 ? dot : 0.0) + (bias ? w[h] * bias[h] : 0.0);"),
+    "rope_theta_exponent": ("return pow(base, -(double)(2 * f) / (double)(2 * F));",
+                            "return pow(base, -(double)f / (double)(2 * F));"),
+    "rope_wrong_sign": ("x[2 * j + 1] = re * sn + im * c;", "x[2 * j + 1] = re * sn - im * c;"),
+    "rope_frequency_index": ("const int64_t f = j % F;", "const int64_t f = j / S;"),
+    "absorb_rope_no_conjugate": ("out[2 * (s * F + f)] = a * c + bb * e;", "out[2 * (s * F + f)] = a * c - bb * e;"),
+    "absorb_rope_drops_bias": ("b[i] = acc;", "b[i] = 0.0;"),
+    "absorb_rope_nope_transposed": ("acc += qi[2 * F + e] * Wn[e * r_nope + t];", "acc += qi[2 * F + e] * Wn[t * d_nope + e];"),
+    "explicit_rope_no_beta": ("double acc = beta[e];", "double acc = 0.0;"),
+    "explicit_rope_rotation_sign": ("key[2 * f + 1] = kr * sin(ang) + ki * cos(ang);",
+                                    "key[2 * f + 1] = kr * sin(ang) - ki * cos(ang);"),
 }
 
 
