@@ -15,6 +15,12 @@
  *   - Hierarchical selection (HS, §3.2, §C.4): the anchor proposes its top-M
  *     rows (M = 8192 in the paper) and each follower rescores only those and
  *     selects its own top-k within them.
+ *   - RoPE-compatible structured decoders (§A.2-§A.4): the latent's rotary
+ *     sources are rotated by the native rotary phase before caching, each
+ *     layer's per-frequency complex decoder and dense NoPE decoder fold into
+ *     its post-RoPE query, and the NoPE output bias becomes one number per
+ *     (query, head) added inside the ReLU:
+ *     I_l(s) = sum_h w_{l,h} * max(0, qt_{l,h} . c_s + b_{l,h}).
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  Descriptor structs
@@ -43,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LI_ABI_VERSION 2
+#define LI_ABI_VERSION 3
 #define LI_API __attribute__((visibility("default")))
 #define LI_PAGE_SIZE 64      /* rows per cache page                        */
 #define LI_MAX_HEADS 64      /* indexer heads per query                    */
@@ -125,6 +131,34 @@ LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const
                            const int32_t *pos, int32_t T, hipStream_t stream);
 
 /*
+ * Rotary layout of a latent row (§A.2, §A.4, §3.1: the RoPE and NoPE
+ * branches are concatenated).  The first 2 * sources * freqs elements hold
+ * `sources` shared complex sources for each of `freqs` rotary frequencies as
+ * (re, im) pairs; pair j is source j / freqs at frequency f = j % freqs.  The
+ * rest of the row is the NoPE latent.  The native rotary phase of frequency f
+ * at position p is p * theta_f, theta_f = base^(-2f / (2 freqs)) (the RoPE of
+ * a native rotary key 2 * freqs wide).
+ */
+typedef struct {
+    int32_t freqs;   /* F >= 1                                       */
+    int32_t sources; /* S >= 1; 2 S F <= r                           */
+    double base;     /* > 1 (10000 for the usual RoPE)               */
+} li_rope;
+
+/*
+ * append_latent_rope — li_append_latent for a latent with rotary sources
+ * (§A.2: the sources share the native rotary phase, so the latent is rotated
+ * before caching).  rows [T][r] hold the unrotated sources (bf16 for LI_BF16
+ * and LI_FP8 caches, fp32 for LI_FP32); each source pair of row t is
+ * multiplied by exp(i pos[t] theta_f), computed in fp64, and the row is
+ * rounded once to the cache dtype (LI_FP8: to fp32, then rotated by the
+ * Walsh-Hadamard transform and quantized as li_append_latent does).  The NoPE
+ * part is stored as given.  rope (host) as above.
+ */
+LI_API li_status li_append_latent_rope(const li_cache *cache, const void *rows, const int32_t *seq,
+                                const int32_t *pos, int32_t T, const li_rope *rope, hipStream_t stream);
+
+/*
  * absorb_query — qt = q W_dec for every query and head (§3.1, §A.2, §B.2).
  *   q       [Q][H][d]   (dtype)
  *   w_dec   [d][r]      (dtype) the layer's key decoder, latent -> key
@@ -143,6 +177,34 @@ LI_API li_status li_append_latent(const li_cache *cache, const void *rows, const
 LI_API li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32_t Q, int32_t H,
                           int32_t d, int32_t r, li_dtype dtype, hipStream_t stream);
 
+/*
+ * rope_decoder — lowers a layer's structured decoder (§A.4: per-frequency
+ * complex coefficients over the shared sources; §A.3: a dense NoPE decoder)
+ * into the dense w_dec [d][r] that li_absorb_query takes, so that absorbing a
+ * post-RoPE query q = [q_rope (2F, (re, im) pairs) | q_nope (d_nope)] gives
+ *   qt[pair (s, f)] = q_f * conj(D[f][s])   and   qt[nope t] = q_nope . Wn[:, t].
+ *   D     [F][S][2] (re, im) decoder coefficients, dtype
+ *   w_nope [d_nope][r_nope] dtype
+ *   w_dec [d][r] out, dtype, d = 2F + d_nope, r = 2SF + r_nope: every entry is
+ *         a copy (possibly negated) of a coefficient, or zero, so no rounding
+ *         happens here.
+ * dtype LI_BF16 or LI_FP32.  rope (host) gives F and S (base is not used).
+ */
+LI_API li_status li_rope_decoder(const void *D, const void *w_nope, const li_rope *rope, int32_t d_nope,
+                          int32_t r_nope, void *w_dec, li_dtype dtype, hipStream_t stream);
+
+/*
+ * query_bias — the absorbed NoPE output bias (§A.3: each layer's NoPE
+ * decoder carries an output bias beta; k_nope = Wn^T n + beta, so
+ * q . k = qt . c + b with b = q_nope . beta, one number per query and head).
+ *   q     [Q][H][d] (dtype LI_BF16 or LI_FP32); its last d - d_rope elements
+ *         are q_nope
+ *   beta  [d - d_rope] fp32
+ *   bias  [Q][H] fp32 out: the products summed in fp64 and rounded once.
+ */
+LI_API li_status li_query_bias(const void *q, const float *beta, int32_t Q, int32_t H, int32_t d, int32_t d_rope,
+                        float *bias, li_dtype dtype, hipStream_t stream);
+
 /* Size and scale offset of an LI_FP8 query buffer (0 for invalid sizes). */
 LI_API size_t li_fp8_query_bytes(int32_t Q, int32_t H, int32_t r);
 LI_API size_t li_fp8_query_scale_offset(int32_t Q, int32_t H, int32_t r);
@@ -151,7 +213,9 @@ LI_API size_t li_fp8_query_scale_offset(int32_t Q, int32_t H, int32_t r);
  * score_topk — full-prefix scoring and per-query top-k (§3.1, §4.1).
  *   q_tilde [Q][H][r] absorbed queries (cache dtype; for an LI_FP8 cache the
  *           FP8 query buffer of li_absorb_query); w [Q][H] fp32 head
- *   weights (any sign).  scores[i][j] = sum_h w[i][h] max(0, q_tilde[i][h] . c_j)
+ *   weights (any sign); bias [Q][H] fp32 absorbed decoder bias
+ *   (li_query_bias) or NULL for none.
+ *   scores[i][j] = sum_h w[i][h] max(0, q_tilde[i][h] . c_j + bias[i][h])
  *   for j < n_i, accumulated in fp32.
  *   idx     [Q][k] out: the set of the min(k, n_i) highest-scoring positions
  *           (unordered; slots past count[i] are -1).  Among exactly equal
@@ -170,7 +234,7 @@ LI_API size_t li_fp8_query_scale_offset(int32_t Q, int32_t H, int32_t r);
  * decoder) is this call on a cache of r = d with q_tilde = q.
  */
 LI_API li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde,
-                        const float *w, int32_t H, int32_t k, int32_t *idx, int32_t *count,
+                        const float *w, const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count,
                         int32_t k_inner, int32_t *idx_inner, int32_t *count_inner, float *scores,
                         int64_t ld, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -184,11 +248,12 @@ LI_API li_status li_score_topk(const li_cache *cache, const li_queries *queries,
  *              best candidates (unordered, -1 padded); count [Q] out.
  *   cand_scores [Q][M] fp32 out (optional): the follower's candidate scores.
  *   ws         at least li_workspace_bytes(LI_OP_HS_SELECT, ...).
- * q_tilde as for li_score_topk (the FP8 query buffer for an LI_FP8 cache).
+ * q_tilde, w and bias as for li_score_topk (the FP8 query buffer for an
+ * LI_FP8 cache).
  */
 LI_API li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
                        const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w,
-                       int32_t H, int32_t k, int32_t *idx, int32_t *count, float *cand_scores,
+                       const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count, float *cand_scores,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace operations:

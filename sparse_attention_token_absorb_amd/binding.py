@@ -22,9 +22,9 @@ LI_OK, LI_ERR_NULL, LI_ERR_SHAPE, LI_ERR_UNSUPPORTED, LI_ERR_WORKSPACE, LI_ERR_H
 LI_BF16, LI_FP32, LI_FP8 = 0, 1, 2
 LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
-EXPORTED = ["li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select", "li_workspace_bytes",
-            "li_fp8_query_bytes", "li_fp8_query_scale_offset", "li_timing_enable", "li_timing_read", "li_status_str",
-            "li_last_error", "li_abi_version"]
+EXPORTED = ["li_append_latent", "li_append_latent_rope", "li_rope_decoder", "li_query_bias", "li_absorb_query",
+            "li_score_topk", "li_hs_select", "li_workspace_bytes", "li_fp8_query_bytes", "li_fp8_query_scale_offset",
+            "li_timing_enable", "li_timing_read", "li_status_str", "li_last_error", "li_abi_version"]
 (LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
  LI_KERNEL_APPEND) = range(6)
 
@@ -40,6 +40,10 @@ class _Cache(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("r", ctypes.c_int32), ("dtype", ctypes.c_int),
                 ("scales", ctypes.c_void_p)]
+
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("freqs", ctypes.c_int32), ("sources", ctypes.c_int32), ("base", ctypes.c_double)]
 
 
 class _Queries(ctypes.Structure):
@@ -60,9 +64,13 @@ def lib():
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         cp, qp = ctypes.POINTER(_Cache), ctypes.POINTER(_Queries)
         L.li_append_latent.argtypes = [cp, vp, vp, vp, i32, vp]
+        rp = ctypes.POINTER(_Rope)
+        L.li_append_latent_rope.argtypes = [cp, vp, vp, vp, i32, rp, vp]
+        L.li_rope_decoder.argtypes = [vp, vp, rp, i32, i32, vp, ctypes.c_int, vp]
+        L.li_query_bias.argtypes = [vp, vp, i32, i32, i32, i32, vp, ctypes.c_int, vp]
         L.li_absorb_query.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
-        L.li_score_topk.argtypes = [cp, qp, vp, vp, i32, i32, vp, vp, i32, vp, vp, vp, i64, vp, sz, vp]
-        L.li_hs_select.argtypes = [cp, qp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.li_score_topk.argtypes = [cp, qp, vp, vp, vp, i32, i32, vp, vp, i32, vp, vp, vp, i64, vp, sz, vp]
+        L.li_hs_select.argtypes = [cp, qp, vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.li_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32]
         L.li_workspace_bytes.restype = sz
         for f in ("li_fp8_query_bytes", "li_fp8_query_scale_offset"):
@@ -249,6 +257,63 @@ def append_latent(cache: LatentCache, rows: torch.Tensor, seq: torch.Tensor, pos
            "li_append_latent")
 
 
+def _rope(rope) -> _Rope:
+    F, S = int(rope[0]), int(rope[1])
+    base = float(rope[2]) if len(rope) > 2 else 10000.0
+    return _Rope(F, S, base)
+
+
+def append_latent_rope(cache: LatentCache, rows: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor, rope) -> None:
+    """li_append_latent_rope: rows [T][r] with unrotated rotary sources;
+    rope = (freqs, sources[, base])."""
+    _need(rows, "rows", torch.bfloat16 if cache.fp8 else cache.dtype, cache.device)
+    _need(seq, "seq", torch.int32, cache.device)
+    _need(pos, "pos", torch.int32, cache.device)
+    T = int(rows.shape[0])
+    if rows.dim() != 2 or rows.shape[1] != cache.r or seq.shape != (T,) or pos.shape != (T,):
+        raise ValueError("rows must be [T][r], seq and pos [T]")
+    c = cache.desc()
+    rd = _rope(rope)
+    _check(lib().li_append_latent_rope(ctypes.byref(c), _ptr(rows), _ptr(seq), _ptr(pos), T, ctypes.byref(rd),
+                                       _stream(cache.device)), "li_append_latent_rope")
+
+
+def rope_decoder(D: torch.Tensor, w_nope: torch.Tensor, rope, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """li_rope_decoder: D [F][S][2], w_nope [d_nope][r_nope] (bf16 or fp32)
+    -> the dense decoder w_dec [2F + d_nope][2SF + r_nope]."""
+    dt = _li_dtype(D.dtype)
+    F, S = int(rope[0]), int(rope[1])
+    _need(D, "D", D.dtype, D.device, (F, S, 2))
+    _need(w_nope, "w_nope", D.dtype, D.device)
+    if w_nope.dim() != 2:
+        raise ValueError("w_nope must be [d_nope][r_nope]")
+    d_nope, r_nope = (int(x) for x in w_nope.shape)
+    shape = (2 * F + d_nope, 2 * S * F + r_nope)
+    if out is None:
+        out = torch.empty(shape, dtype=D.dtype, device=D.device)
+    _need(out, "w_dec", D.dtype, D.device, shape)
+    rd = _rope(rope)
+    _check(lib().li_rope_decoder(_ptr(D), _ptr(w_nope), ctypes.byref(rd), d_nope, r_nope, _ptr(out), dt,
+                                 _stream(D.device)), "li_rope_decoder")
+    return out
+
+
+def query_bias(q: torch.Tensor, beta: torch.Tensor, d_rope: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """li_query_bias: q [Q][H][d] (bf16 or fp32), beta [d - d_rope] fp32 -> bias [Q][H] fp32."""
+    dt = _li_dtype(q.dtype)
+    _need(q, "q", q.dtype, q.device)
+    if q.dim() != 3:
+        raise ValueError("q must be [Q][H][d]")
+    Q, H, d = (int(x) for x in q.shape)
+    _need(beta, "beta", torch.float32, q.device, (d - d_rope,))
+    if out is None:
+        out = torch.empty((Q, H), dtype=torch.float32, device=q.device)
+    _need(out, "bias", torch.float32, q.device, (Q, H))
+    _check(lib().li_query_bias(_ptr(q), _ptr(beta), Q, H, d, d_rope, _ptr(out), dt, _stream(q.device)),
+           "li_query_bias")
+    return out
+
+
 def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out=None, fp8: bool = False):
     """li_absorb_query: q [Q][H][d] x W_dec [d][r] -> q_tilde [Q][H][r]
     (an Fp8Query with fp8=True: bf16 inputs, rotated and quantized output)."""
@@ -306,13 +371,16 @@ class TopK:
 
 def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int, q_tilde: torch.Tensor,
                w: torch.Tensor, k: int, k_inner: int = 0, keep_scores: bool = False,
-               ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None) -> TopK:
+               ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None,
+               bias: Optional[torch.Tensor] = None) -> TopK:
     """li_score_topk: score every valid row and take the top-k (+ nested top-k_inner)."""
     dev = cache.device
     qs = _queries(cache, seq, pos, max_valid)
     Q = qs.Q
     H, qbuf = _query_operand(cache, q_tilde, Q)
     _need(w, "w", torch.float32, dev, (Q, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (Q, H))
     if out is None:
         out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
         if k_inner:
@@ -330,7 +398,7 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
     nb = workspace_bytes(op, Q, max_valid, H, cache.r, k, 0)
     ws = _workspace(dev, nb, ws)
     c = cache.desc()
-    _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(qbuf), _ptr(w), H, k, _ptr(out.idx),
+    _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(qbuf), _ptr(w), _ptr(bias), H, k, _ptr(out.idx),
                                _ptr(out.count), k_inner, _ptr(out.idx_inner), _ptr(out.count_inner),
                                _ptr(out.scores), ld, _ptr(ws), ws.numel(), _stream(dev)), "li_score_topk")
     return out
@@ -338,7 +406,8 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
 
 def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int, cand: torch.Tensor,
               cand_count: torch.Tensor, q_tilde: torch.Tensor, w: torch.Tensor, k: int, keep_scores: bool = False,
-              ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None) -> TopK:
+              ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None,
+              bias: Optional[torch.Tensor] = None) -> TopK:
     """li_hs_select: rescore the anchor's candidates and take this layer's top-k of them."""
     dev = cache.device
     qs = _queries(cache, seq, pos, max_valid)
@@ -350,6 +419,8 @@ def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_vali
     _need(cand_count, "cand_count", torch.int32, dev, (Q,))
     H, qbuf = _query_operand(cache, q_tilde, Q)
     _need(w, "w", torch.float32, dev, (Q, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (Q, H))
     if out is None:
         out = TopK(torch.empty((Q, k), dtype=torch.int32, device=dev), torch.empty(Q, dtype=torch.int32, device=dev))
         if keep_scores:
@@ -362,6 +433,6 @@ def hs_select(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_vali
     ws = _workspace(dev, nb, ws)
     c = cache.desc()
     _check(lib().li_hs_select(ctypes.byref(c), ctypes.byref(qs), _ptr(cand), _ptr(cand_count), M, _ptr(qbuf),
-                              _ptr(w), H, k, _ptr(out.idx), _ptr(out.count), _ptr(out.scores), _ptr(ws),
+                              _ptr(w), _ptr(bias), H, k, _ptr(out.idx), _ptr(out.count), _ptr(out.scores), _ptr(ws),
                               ws.numel(), _stream(dev)), "li_hs_select")
     return out

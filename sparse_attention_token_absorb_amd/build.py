@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblatentindex.so")
-SOURCES = ["api.cpp", "timing.cpp", "append.hip", "absorb.hip", "score.hip", "select.hip", "fp8.hip"]
+SOURCES = ["api.cpp", "timing.cpp", "append.hip", "absorb.hip", "score.hip", "select.hip", "fp8.hip", "rope.hip"]
 ARCH = "gfx950"
 
 

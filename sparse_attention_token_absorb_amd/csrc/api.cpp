@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <math.h>
+
 #include <algorithm>
 #include <string>
 
@@ -77,6 +79,26 @@ li_status check_queries(const li_queries *qs, const li_cache *c)
     return LI_OK;
 }
 
+// Validates a rotary layout against a latent width and fills the kernel's
+// copy, with each frequency's phase step theta_f = base^(-2f / (2F)) in fp64.
+li_status rope_args(const li_rope *rope, int32_t r, li::RopeArgs *out)
+{
+    if (!rope) return fail(LI_ERR_NULL, "rope descriptor is NULL");
+    if (rope->freqs < 1 || rope->freqs > li::kMaxRopeFreqs || rope->sources < 1)
+        return fail(LI_ERR_SHAPE, "rope freqs=%d (1..%d), sources=%d (>= 1)", rope->freqs, li::kMaxRopeFreqs,
+                    rope->sources);
+    if ((int64_t)2 * rope->sources * rope->freqs > r)
+        return fail(LI_ERR_SHAPE, "2 * sources * freqs = %lld exceeds r=%d", (long long)2 * rope->sources * rope->freqs,
+                    r);
+    if (!(rope->base > 1.0) || !isfinite(rope->base)) return fail(LI_ERR_SHAPE, "rope base %g must be > 1", rope->base);
+    *out = li::RopeArgs{};
+    out->F = rope->freqs;
+    out->S = rope->sources;
+    for (int f = 0; f < rope->freqs; ++f)
+        out->theta[f] = pow(rope->base, -(double)(2 * f) / (double)(2 * rope->freqs));
+    return LI_OK;
+}
+
 li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt, const float *w, int32_t H)
 {
     li::ScoreArgs a{};
@@ -134,12 +156,19 @@ size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32
     }
 }
 
-li_status li_append_latent(const li_cache *cache, const void *rows, const int32_t *seq, const int32_t *pos, int32_t T,
-                           hipStream_t stream)
+namespace {
+
+li_status append_common(const li_cache *cache, const void *rows, const int32_t *seq, const int32_t *pos, int32_t T,
+                        const li_rope *rope, hipStream_t stream)
 {
     li_status st = check_cache(cache);
     if (st != LI_OK) return st;
     if (T < 0) return fail(LI_ERR_SHAPE, "T=%d", T);
+    li::RopeArgs ra{};
+    if (rope) {
+        st = rope_args(rope, cache->r, &ra);
+        if (st != LI_OK) return st;
+    }
     if (T == 0) return ok();
     if (!rows || !seq || !pos) return fail(LI_ERR_NULL, "rows/seq/pos is NULL");
     const int esize = cache->dtype == LI_BF16 ? 2 : 4;
@@ -148,12 +177,59 @@ li_status li_append_latent(const li_cache *cache, const void *rows, const int32_
         li::TimedScope ts(LI_KERNEL_APPEND, stream);
         if (cache->dtype == LI_FP8)
             e = li::launch_append_fp8(cache->pool, cache->scales, cache->block_table, cache->max_pages, cache->r, rows,
-                                      seq, pos, T, stream);
+                                      seq, pos, T, ra, stream);
+        else if (rope)
+            e = li::launch_append_rope(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq,
+                                       pos, T, ra, stream);
         else
             e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos,
                                   T, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "append_latent launch");
+    return ok();
+}
+
+} // namespace
+
+li_status li_append_latent(const li_cache *cache, const void *rows, const int32_t *seq, const int32_t *pos, int32_t T,
+                           hipStream_t stream)
+{
+    return append_common(cache, rows, seq, pos, T, nullptr, stream);
+}
+
+li_status li_append_latent_rope(const li_cache *cache, const void *rows, const int32_t *seq, const int32_t *pos,
+                                int32_t T, const li_rope *rope, hipStream_t stream)
+{
+    if (!rope) return fail(LI_ERR_NULL, "rope descriptor is NULL");
+    return append_common(cache, rows, seq, pos, T, rope, stream);
+}
+
+li_status li_rope_decoder(const void *D, const void *w_nope, const li_rope *rope, int32_t d_nope, int32_t r_nope,
+                          void *w_dec, li_dtype dtype, hipStream_t stream)
+{
+    if (!rope) return fail(LI_ERR_NULL, "rope descriptor is NULL");
+    if (rope->freqs < 1 || rope->freqs > li::kMaxRopeFreqs || rope->sources < 1)
+        return fail(LI_ERR_SHAPE, "rope freqs=%d (1..%d), sources=%d (>= 1)", rope->freqs, li::kMaxRopeFreqs,
+                    rope->sources);
+    if (d_nope < 0 || r_nope < 0) return fail(LI_ERR_SHAPE, "d_nope=%d, r_nope=%d", d_nope, r_nope);
+    if (dtype != LI_BF16 && dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "decoder dtype %d", (int)dtype);
+    if (!D || !w_dec || (d_nope > 0 && r_nope > 0 && !w_nope)) return fail(LI_ERR_NULL, "D/w_nope/w_dec is NULL");
+    hipError_t e = li::launch_rope_decoder(D, w_nope, rope->freqs, rope->sources, d_nope, r_nope, w_dec,
+                                           dtype == LI_BF16 ? 2 : 4, stream);
+    if (e != hipSuccess) return hip_fail(e, "rope_decoder launch");
+    return ok();
+}
+
+li_status li_query_bias(const void *q, const float *beta, int32_t Q, int32_t H, int32_t d, int32_t d_rope, float *bias,
+                        li_dtype dtype, hipStream_t stream)
+{
+    if (Q < 0 || H <= 0 || d <= 0 || d_rope < 0 || d_rope > d)
+        return fail(LI_ERR_SHAPE, "Q=%d H=%d d=%d d_rope=%d", Q, H, d, d_rope);
+    if (dtype != LI_BF16 && dtype != LI_FP32) return fail(LI_ERR_UNSUPPORTED, "query dtype %d", (int)dtype);
+    if (Q == 0) return ok();
+    if (!q || !bias || (d > d_rope && !beta)) return fail(LI_ERR_NULL, "q/beta/bias is NULL");
+    hipError_t e = li::launch_query_bias(q, beta, (int64_t)Q * H, d, d_rope, bias, dtype == LI_BF16, stream);
+    if (e != hipSuccess) return hip_fail(e, "query_bias launch");
     return ok();
 }
 
@@ -182,9 +258,9 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
 }
 
 li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
-                        int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner, int32_t *idx_inner,
-                        int32_t *count_inner, float *scores, int64_t ld, void *ws, size_t ws_bytes,
-                        hipStream_t stream)
+                        const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner,
+                        int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld, void *ws,
+                        size_t ws_bytes, hipStream_t stream)
 {
     li_status st = check_cache(cache);
     if (st != LI_OK) return st;
@@ -245,6 +321,7 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         }
         if (e != hipSuccess) return hip_fail(e, "histogram clear");
         li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
+        a.bias = bias;
         a.out = S;
         a.out_ld = sld;
         a.max_rows = queries->max_valid;
@@ -267,7 +344,8 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
 }
 
 li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
-                       const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w, int32_t H, int32_t k,
+                       const int32_t *cand_count, int32_t M, const void *q_tilde, const float *w, const float *bias,
+                       int32_t H, int32_t k,
                        int32_t *idx, int32_t *count, float *cand_scores, void *ws, size_t ws_bytes,
                        hipStream_t stream)
 {
@@ -309,6 +387,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     }
     if (e != hipSuccess) return hip_fail(e, "histogram clear");
     li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
+    a.bias = bias;
     a.cand = cand;
     a.cand_count = cand_count;
     a.cand_ld = M;

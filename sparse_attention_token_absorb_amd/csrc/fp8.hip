@@ -165,7 +165,8 @@ __device__ __forceinline__ void rotate_quantize(float (&x)[NR][4], int l32, int 
 // ---------------------------------------------------------------------------
 template <int R>
 __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales, const int32_t *bt, int max_pages,
-                                                    const u16 *rows, const int32_t *seq, const int32_t *pos, int T)
+                                                    const u16 *rows, const int32_t *seq, const int32_t *pos, int T,
+                                                    const RopeArgs rope)
 {
     constexpr int NSEG = R / kSeg;
     const int half = (int)((blockIdx.x * 256 + threadIdx.x) >> 5); // (row, segment) index
@@ -176,6 +177,21 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
     const uint2 raw = *(const uint2 *)(rows + (int64_t)tc * R + g * kSeg + 4 * l32);
     float x[1][4] = {{bf16_to_f32((u16)(raw.x & 0xFFFF)), bf16_to_f32((u16)(raw.x >> 16)),
                       bf16_to_f32((u16)(raw.y & 0xFFFF)), bf16_to_f32((u16)(raw.y >> 16))}};
+    if (rope.F > 0) {
+        // rotary source pairs among this lane's four elements: rotated in
+        // fp64 at the row's position, rounded once to fp32
+        const int p = pos[tc];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = g * (kSeg / 2) + 2 * l32 + u;
+            if (j < rope.S * rope.F) {
+                double re = x[0][2 * u], im = x[0][2 * u + 1];
+                rope_pair(re, im, p, rope.theta[j % rope.F]);
+                x[0][2 * u] = (float)re;
+                x[0][2 * u + 1] = (float)im;
+            }
+        }
+    }
     int ee[1];
     uint32_t cw[1];
     rotate_quantize<1>(x, l32, ee, cw);
@@ -346,6 +362,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     i32x8 qa[HB][KS];
     int sa[HB][NSEG];
     float wr[HB][16];
+    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
     {
         const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
         const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
@@ -371,6 +388,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             for (int r = 0; r < 16; ++r) {
                 const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 wr[hb][r] = hh < a.H ? a.w[(int64_t)q * a.H + hh] : 0.0f;
+                br[hb][r] = a.bias && hh < a.H ? a.bias[(int64_t)q * a.H + hh] : 0.0f;
             }
         }
     }
@@ -464,10 +482,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
                                                                                   (nr * NSEG + g) * 4) >> 23) & 0xFFu);
         f32x16 acc[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            f32x16 z = {};
-            acc[hb] = z;
-        }
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int c = 4 * s + 2 * gk;
@@ -546,6 +561,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     i32x8 qa[HB][KS];
     int sa[HB][NSEG];
     float wr[HB][16];
+    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
     {
         const bool live = q < a.Q;
         const int qc_i = live ? q : 0;
@@ -574,6 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int r = 0; r < 16; ++r) {
                 const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 wr[hb][r] = live && hh < a.H ? a.w[(int64_t)qc_i * a.H + hh] : 0.0f;
+                br[hb][r] = live && a.bias && hh < a.H ? a.bias[(int64_t)qc_i * a.H + hh] : 0.0f;
             }
         }
     }
@@ -639,10 +656,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                    0xFFu);
                 f32x16 acc[HB];
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) {
-                    f32x16 z = {};
-                    acc[hb] = z;
-                }
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const int c = 4 * s + 2 * gk;
@@ -748,17 +762,17 @@ hipError_t launch_absorb_fp8_r(const u16 *q, const u16 *W, uint8_t *codes, float
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r) { return (Q * H * r + 255) / 256 * 256; }
 
 hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
-                             const int32_t *seq, const int32_t *pos, int T, hipStream_t s)
+                             const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
     const int64_t halves = (int64_t)T * (r / kSeg);
     const unsigned blocks = (unsigned)((halves * 32 + 255) / 256);
     if (r == 256)
         hipLaunchKernelGGL((k_append_fp8<256>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
-                           (const u16 *)rows, seq, pos, T);
+                           (const u16 *)rows, seq, pos, T, rope);
     else if (r == 128)
         hipLaunchKernelGGL((k_append_fp8<128>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
-                           (const u16 *)rows, seq, pos, T);
+                           (const u16 *)rows, seq, pos, T, rope);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -19,6 +19,7 @@ typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef const __attribute__((address_space(3))) float lds_f32;
+typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
@@ -117,6 +118,38 @@ __device__ __forceinline__ float epilogue(const f32x16 (&acc)[HB], const float (
 #pragma unroll
     for (int hb = 1; hb < HB; ++hb) p += ps[hb];
     return p + __shfl_xor(p, 32);
+}
+
+// Multiplies the complex pair (re, im) by exp(i pos theta) in fp64: the
+// phase as one product, then plain products and sums (no fused
+// multiply-add), rounded as written.
+__device__ __forceinline__ void rope_pair(double &re, double &im, int pos, double theta)
+{
+#pragma clang fp contract(off)
+    const double ang = (double)pos * theta;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const double a = re * cs - im * sn;
+    const double b = re * sn + im * cs;
+    re = a;
+    im = b;
+}
+
+// Adds each accumulator's head bias (b: the query's 64 staged biases, heads
+// past H zero) before the ReLU; accumulator r of block hb holds head
+// hb*32 + (r/4)*8 + (lane/32)*4 + r%4 of tile row lane % 32.
+template <int HB>
+__device__ __forceinline__ void add_bias(f32x16 (&acc)[HB], const lds_f32 *b)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *(lds_f32x4 *)(b + hb * 32 + g * 8 + (lane >> 5) * 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[hb][g * 4 + t] += v[t];
+        }
 }
 
 __device__ __forceinline__ void hist_zero(uint32_t *h, int nthreads, int tid)

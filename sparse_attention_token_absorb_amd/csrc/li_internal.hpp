@@ -40,6 +40,7 @@ struct ScoreArgs {
     int64_t cand_ld;
     const void *qt;
     const float *w;
+    const float *bias; // optional [Q][H]: absorbed decoder bias, added before the ReLU
     int32_t H;
     int32_t Q;
     float *out;
@@ -61,8 +62,17 @@ hipError_t launch_absorb(const void *q, const void *W, void *qt, int64_t QH, int
 // into FP8, and FP8 scoring (the prefill kernel when many queries share a
 // sequence and no histogram is asked for; the decode kernel otherwise).
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r);
+// Rotary layout of a latent row (see li_rope): F frequencies, S sources, and
+// the phase step theta_f of each frequency (computed on the host in fp64).
+constexpr int kMaxRopeFreqs = 64;
+struct RopeArgs {
+    int32_t F; // 0: no rotary part
+    int32_t S;
+    double theta[kMaxRopeFreqs];
+};
+
 hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
-                             const int32_t *seq, const int32_t *pos, int T, hipStream_t s);
+                             const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s);
 hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH, int d, int r, hipStream_t s);
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
                             bool many_queries_per_seq, int64_t max_rows, hipStream_t s);
@@ -70,6 +80,15 @@ hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_
 // Append rows into the paged pool.
 hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
                          const int32_t *seq, const int32_t *pos, int T, hipStream_t s);
+
+// RoPE-compatible structured decoder: rotated append (bf16 / fp32 pools),
+// lowering of the decoder to a dense W, and the absorbed bias.
+hipError_t launch_append_rope(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
+                              const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s);
+hipError_t launch_rope_decoder(const void *D, const void *Wn, int F, int S, int d_nope, int r_nope, void *W, int esize,
+                               hipStream_t s);
+hipError_t launch_query_bias(const void *q, const float *beta, int64_t QH, int d, int d_rope, float *bias, bool bf16,
+                             hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Top-k selection over per-query virtual rows of scores.

@@ -37,6 +37,39 @@ template <int R, int HB>
 struct QueryRegs {
     bf16x8 a[HB][R / 16];
     float w[HB][16];
+    f32x16 b[HB]; // accumulator start values: each head's absorbed decoder bias (0 without one)
+
+    // Staged through LDS (see stage_query): row h of the query lives in the
+    // last ring slot of wave h / 16, row-local piece c at c ^ (h % PR); the
+    // head weights in s_w.  Heads past H read as zero.
+    template <int NB, int CHUNK>
+    __device__ __forceinline__ void from_lds(const lds_u8 *ring, const lds_f32 *s_w, const lds_f32 *s_b, bool has_bias,
+                                             int H)
+    {
+        constexpr int PR = R / 8; // 16-byte pieces per query row
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const lds_u8 *row = ring + ((h >> 4) * NB + NB - 1) * CHUNK + (h & 15) * PR * 16;
+#pragma unroll
+            for (int s = 0; s < R / 16; ++s) {
+                const int c = 2 * s + (lane >> 5);
+                bf16x8 v = *(const lds_bf16x8 *)(row + (c ^ (h & (PR - 1))) * 16);
+                if (h >= H) {
+                    bf16x8 z = {};
+                    v = z;
+                }
+                a[hb][s] = v;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                w[hb][r] = hh < H ? s_w[hh] : 0.0f;
+                b[hb][r] = has_bias && hh < H ? s_b[hh] : 0.0f;
+            }
+        }
+    }
 
     __device__ __forceinline__ void load(const u16 *qt, const float *wq, int H)
     {
@@ -134,6 +167,44 @@ __device__ __forceinline__ void issue_rows(const u16 *pool, const RowOff &rowoff
     }
 }
 
+// The query's rows into LDS, once per workgroup: wave w moves rows
+// 16w .. 16w+15 (HB * 32 rows in all; rows past H repeat row H-1 and are
+// zeroed when read) into the last slot of its ring, which the stream does not
+// touch before its (NB-1)-th chunk; wave 0 also moves the head weights and
+// wave 1 the heads' decoder biases (when there are any).
+// Returns the number of loads this wave issued.
+template <int R, int HB, int NB, int CHUNK>
+__device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const float *bq, int H, lds_u8 *ring,
+                                           lds_f32 *s_w, lds_f32 *s_b)
+{
+    constexpr int PR = R / 8;
+    constexpr int NIC = CHUNK / 1024;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int issued = 0;
+    if (wv * 16 < HB * 32) {
+        lds_u8 *slot = ring + (wv * NB + NB - 1) * CHUNK;
+#pragma unroll
+        for (int ii = 0; ii < NIC; ++ii) {
+            const int p = ii * 64 + lane;
+            const int hl = p / PR, cs = p % PR;
+            const int h = wv * 16 + hl;
+            const int hs = h < H ? h : H - 1;
+            dma16(qt + (int64_t)hs * R + (cs ^ (h & (PR - 1))) * 8, slot + ii * 1024);
+        }
+        issued = NIC;
+    }
+    if (wv == 0) {
+        dma4(wq + (lane < H ? lane : H - 1), (lds_u8 *)s_w);
+        ++issued;
+    }
+    if (wv == 1 && bq) {
+        dma4(bq + (lane < H ? lane : H - 1), (lds_u8 *)s_b);
+        ++issued;
+    }
+    return issued;
+}
+
 // ---------------------------------------------------------------------------
 // Decode: few queries, long rows.  Workgroup = 4 waves of one query; wave w
 // streams tiles row0 + (w + 4 i) * 32.  Each tile moves as two half-width
@@ -151,6 +222,8 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * CHUNK];
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTiles * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
+    __shared__ float s_w[64];
+    __shared__ float s_b[64];
 
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -168,8 +241,10 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     // the first chunks are issued as soon as the page ids arrive, before the
     // row count: a page id that is not in use is clamped into the pool, and
     // what such a chunk brings in is never scored.
-    QueryRegs<R, HB> qr;
-    qr.load((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H, a.H);
+    lds_u8 *const ring_all = (lds_u8 *)ring_raw;
+    stage_query<R, HB, NB, CHUNK>((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H,
+                                  a.bias ? a.bias + (int64_t)q * a.H : nullptr, a.H, ring_all, (lds_f32 *)s_w,
+                                  (lds_f32 *)s_b);
     // Scalar loads (constant address space): waited on with lgkmcnt, so
     // waiting for them never waits for the chunk loads below.
     const int b = ((const_i32_t *)a.qseq)[q];
@@ -235,7 +310,14 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     int nt = 0;
     if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
     const int nchunks = 2 * nt; // <= 2 * nt_max: chunks issued above past it are waited for, never used
-    if (a.hist) wg_barrier(); // histogram cleared before any wave counts into it
+    // the query's rows and weights were issued before the chunks: they have
+    // landed once at most the chunks are outstanding
+    wait_after<NIC, NB - 1>(npro);
+    wg_barrier(); // every wave's part of the query is in LDS (and the histogram is cleared)
+    QueryRegs<R, HB> qr;
+    qr.template from_lds<NB, CHUNK>(ring_all, (const lds_f32 *)s_w, (const lds_f32 *)s_b, a.bias != nullptr, a.H);
+    wait_lds();
+    wg_barrier(); // no wave overwrites a staging slot before every wave has read it
 
     float *out = a.out + (int64_t)q * a.out_ld;
     f32x16 acc[HB];
@@ -248,10 +330,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         const lds_u8 *buf = ring + (c % NB) * CHUNK;
         if ((c & 1) == 0) {
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                f32x16 z = {};
-                acc[hb] = z;
-            }
+            for (int hb = 0; hb < HB; ++hb) acc[hb] = qr.b[hb];
             mfma_steps<R, HB, 0, KSH, CH>(buf, qr, acc);
         } else {
             mfma_steps<R, HB, KSH, KSH, CH>(buf, qr, acc);
@@ -287,6 +366,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
     __shared__ uint32_t s_hist[kHistBins];
     __shared__ float s_out[4][kVrMaxTiles * kTile]; // scores, written out after the stream
     __shared__ float s_w[64];                       // head weights, zero past H
+    __shared__ float s_b[64];                       // heads' decoder biases, zero past H (or without)
 
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -356,6 +436,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
         }
     }
     const float wv_lane = a.w[(int64_t)q * a.H + (lane < a.H ? lane : a.H - 1)];
+    const float bv_lane = a.bias ? a.bias[(int64_t)q * a.H + (lane < a.H ? lane : a.H - 1)] : 0.0f;
     if (nt > 0) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) load(bf[d], d < nt ? d : nt - 1);
@@ -366,6 +447,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
         if (off < qbytes) *(lds_u32x4 *)((lds_u8 *)s_qt_raw + off) = qv[c];
     }
     if (wv == 0) s_w[lane] = lane < a.H ? wv_lane : 0.0f;
+    if (wv == 1) s_b[lane] = lane < a.H ? bv_lane : 0.0f;
     wg_barrier(); // every wave's part of the query is in LDS; histogram cleared
     QueryRegs<R, HB> qr;
     {
@@ -385,18 +467,18 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                qr.w[hb][r] = ((const lds_f32 *)s_w)[hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                qr.w[hb][r] = ((const lds_f32 *)s_w)[hh];
+                qr.b[hb][r] = ((const lds_f32 *)s_b)[hh];
+            }
     }
 
     float *out = a.out + (int64_t)q * a.out_ld;
     auto compute = [&](const bf16x8(&src)[KS]) {
         f32x16 acc[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            f32x16 z = {};
-            acc[hb] = z;
-        }
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = qr.b[hb];
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -461,30 +543,32 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
 // second wave on each SIMD covers barriers and epilogues; the first radix
 // digit is counted by the selection pass instead of here.
 // ---------------------------------------------------------------------------
-template <int R, int HB, int NBUF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill(ScoreArgs a,
-                                                                                            int tiles_per_split)
+template <int R, int HB, int NBUF, int QW>
+__global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill(
+    ScoreArgs a, int tiles_per_split)
 {
     constexpr int TILE_BYTES = kTile * R * 2;
     constexpr int CH = R / 8;
     constexpr int NI = R / 16;
-    constexpr int NIW = NI / 4;
-    static_assert(NIW >= 1, "tile must split over 4 waves");
+    constexpr int NIW = NI / QW;
+    constexpr int NT = 64 * QW;
+    static_assert(NIW >= 1 && NIW * QW == NI, "tile must split over the waves");
     static_assert(NBUF >= 3, "ring depth");
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * TILE_BYTES];
     __shared__ int32_t s_page_raw[kPrefillMaxTiles / 2 + 2];
+    __shared__ __attribute__((aligned(16))) float s_b[QW * 64]; // each wave's query: heads' decoder biases
     lds_u8 *ring = (lds_u8 *)ring_raw;
     lds_i32 *s_page = (lds_i32 *)s_page_raw;
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int qbase = blockIdx.x * 4;
+    const int qbase = blockIdx.x * QW;
     const_i32_t *qseq = (const_i32_t *)a.qseq;
     const_i32_t *qpos = (const_i32_t *)a.qpos;
     const_i32_t *slen = (const_i32_t *)a.seq_lens;
-    int sb[4], sn[4];
+    int sb[QW], sn[QW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < QW; ++u) {
         const int qq = qbase + u;
         sb[u] = qq < a.Q ? qseq[qq] : -1;
         sn[u] = qq < a.Q ? (int)min64(valid_rows(qpos[qq], slen[sb[u]]), a.max_rows) : 0;
@@ -492,7 +576,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int q = qbase + wv;
     int my_b = -1, my_n = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < QW; ++u)
         if (u == wv) {
             my_b = sb[u];
             my_n = sn[u];
@@ -503,16 +587,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     } else {
         qr.load((const u16 *)a.qt, a.w, 0); // zero fragments
     }
+    const bool has_bias = a.bias != nullptr;
+    if (has_bias) // read back by this wave only (its own LDS writes come first)
+        s_b[wv * 64 + lane] = q < a.Q && lane < a.H ? a.bias[(int64_t)q * a.H + lane] : 0.0f;
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
     const u16 *pool = (const u16 *)a.pool;
 
 #pragma unroll 1
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < QW; ++u) {
         const int b = sb[u];
         bool skip = b < 0;
         int nmax = 0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < QW; ++v) {
             if (v < u && sb[v] == b) skip = true;
             if (sb[v] == b) nmax = max(nmax, sn[v]);
         }
@@ -527,7 +614,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int p0 = ts >> 1;
         const int np = ((te - 1) >> 1) - p0 + 1;
         __syncthreads(); // the previous pass is done with the ring and the page ids
-        for (int pi = threadIdx.x; pi < np; pi += 256) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
+        for (int pi = threadIdx.x; pi < np; pi += NT) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
         __syncthreads();
         auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
         auto issue = [&](int i, int page) {
@@ -552,6 +639,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     acc[hb] = z;
                 }
                 mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
+                if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
                 const float p = epilogue<HB>(acc, qr.w);
                 const int j = (ts + i) * kTile + lane;
                 if (lane < 32 && j < my_n) out[j] = p;
@@ -567,6 +655,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
 {
     __shared__ float sq[64 * 256];
     __shared__ float sw[64];
+    __shared__ float sb[64];
     __shared__ uint32_t s_hist[kHistBins];
     const int q = blockIdx.y;
     const int b = a.qseq[q];
@@ -578,7 +667,10 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     const int64_t row1 = min64(row0 + rows_per_wg, n);
     const float *qt = (const float *)a.qt + (int64_t)q * a.H * R;
     for (int i = threadIdx.x; i < a.H * R; i += 256) sq[i] = qt[i];
-    for (int i = threadIdx.x; i < a.H; i += 256) sw[i] = a.w[(int64_t)q * a.H + i];
+    for (int i = threadIdx.x; i < a.H; i += 256) {
+        sw[i] = a.w[(int64_t)q * a.H + i];
+        sb[i] = a.bias ? a.bias[(int64_t)q * a.H + i] : 0.0f;
+    }
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     __syncthreads();
     for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
@@ -589,7 +681,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
         for (int h = 0; h < a.H; ++h) {
             float dot = 0.0f;
             for (int t = 0; t < R; ++t) dot = fmaf(sq[h * R + t], row[t], dot);
-            sc = fmaf(sw[h], fmaxf(dot, 0.0f), sc);
+            sc = fmaf(sw[h], fmaxf(dot + sb[h], 0.0f), sc);
         }
         a.out[(int64_t)q * a.out_ld + j] = sc;
         if (a.hist) atomicAdd(&s_hist[score_key(sc) >> kDigit0Shift], 1u);
@@ -628,15 +720,16 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     const int64_t tiles = (max_rows + kTile - 1) / kTile;
     if (prefill) {
         constexpr int NBUF = R == 256 ? 4 : 6;
-        const int qblocks = (a.Q + 3) / 4;
+        constexpr int QW = 4;
+        const int qblocks = (a.Q + QW - 1) / QW;
         int64_t splits = 1;
         if (qblocks < 512) splits = std::min<int64_t>((512 + qblocks - 1) / qblocks, tiles);
         if (splits < 1) splits = 1;
         int64_t tps = (tiles + splits - 1) / splits;
         if (tps > kPrefillMaxTiles) tps = kPrefillMaxTiles;
         splits = (tiles + tps - 1) / tps;
-        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s, a,
-                           (int)tps);
+        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW>), dim3(qblocks, (unsigned)splits), dim3(64 * QW), 0, s,
+                           a, (int)tps);
         return hipGetLastError();
     }
     // decode: about one round of one workgroup per CU

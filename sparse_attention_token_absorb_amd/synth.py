@@ -229,3 +229,52 @@ def config4(seed: int = 4, N: int = 131072, B: int = 4, keys_a: bool = True) -> 
 def config5(seed: int = 5, N: int = 65536, Qn: int = 4096) -> DecodeGroup:
     """Chunked prefill: 4096 queries at positions N-4096..N-1 of a 65536-row cache."""
     return make_prefill(f"prefill-Q{Qn}-N{N}", seed, N=N, Qn=Qn, r=256, H=64, d=128, k=2048)
+
+
+# ----------------------------------------------------------------------------
+# RoPE-compatible structured decoder (§A.2-§A.4): F rotary frequencies with S
+# complex sources each, and a NoPE latent.  The native key is 2F rotary + d_nope
+# NoPE wide; the latent 2SF rotary + r_nope NoPE wide.
+# ----------------------------------------------------------------------------
+@dataclass
+class RopeGroup:
+    """Per-layer structured decoders for one layer group.
+
+    D[l] [F][S][2] decoder coefficients (re, im), Wn[l] [d_nope][r_nope] NoPE
+    decoder, beta[l] [d_nope] NoPE output bias (fp32); F, S, base describe the
+    latent's rotary part.  Values are bf16-exact except beta."""
+    F: int
+    S: int
+    base: float
+    d_nope: int
+    r_nope: int
+    D: List[np.ndarray]
+    Wn: List[np.ndarray]
+    beta: List[np.ndarray]
+
+    @property
+    def d_rope(self) -> int:
+        return 2 * self.F
+
+    @property
+    def d(self) -> int:
+        return 2 * self.F + self.d_nope
+
+    @property
+    def r(self) -> int:
+        return 2 * self.S * self.F + self.r_nope
+
+
+def make_rope(seed: int, *, G: int = 4, F: int = 32, S: int = 2, d_nope: int = 64, r_nope: int = 128,
+              base: float = 10000.0, beta_scale: float = 0.5) -> RopeGroup:
+    """Decoders: D ~ complex N(0, 1/S) per coefficient, Wn ~ N(0, 1/r_nope),
+    beta ~ N(0, beta_scale^2); all but beta rounded to bf16."""
+    ss = np.random.SeedSequence(seed)
+    Ds, Wns, betas = [], [], []
+    for ls in ss.spawn(G):
+        rng = np.random.Generator(np.random.PCG64(ls))
+        Ds.append(round_bf16(rng.standard_normal((F, S, 2), dtype=np.float32) * np.float32(1.0 / np.sqrt(2.0 * S))))
+        Wns.append(round_bf16(rng.standard_normal((d_nope, r_nope), dtype=np.float32) *
+                              np.float32(1.0 / np.sqrt(r_nope))))
+        betas.append((rng.standard_normal(d_nope, dtype=np.float32) * np.float32(beta_scale)).astype(np.float32))
+    return RopeGroup(F=F, S=S, base=base, d_nope=d_nope, r_nope=r_nope, D=Ds, Wn=Wns, beta=betas)

@@ -45,7 +45,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings(L):
-    assert L.li_abi_version() == 2
+    assert L.li_abi_version() == 3
     assert L.li_status_str(0) == b"LI_OK"
     assert L.li_status_str(4) == b"LI_ERR_WORKSPACE"
     assert L.li_status_str(99) == b"LI_ERR_UNKNOWN"
@@ -69,7 +69,7 @@ def score_topk(L, c=None, q=None, H=64, k=16, k_inner=0, inner=None, ws_bytes=1 
     c = cache() if c is None else c
     q = queries() if q is None else q
     return L.li_score_topk(ctypes.byref(c) if c is not False else None, ctypes.byref(q) if q is not False else None,
-                           qt, w, H, k, idx, cnt, k_inner, inner, inner, scores, ld, ws, ws_bytes, None)
+                           qt, w, None, H, k, idx, cnt, k_inner, inner, inner, scores, ld, ws, ws_bytes, None)
 
 
 def test_score_topk_validation(L):
@@ -103,8 +103,8 @@ def test_hs_select_validation(L):
     c, q = cache(), queries()
 
     def call(M=64, k=16, cand=FAKE, ws_bytes=1 << 30, H=64):
-        return L.li_hs_select(ctypes.byref(c), ctypes.byref(q), cand, FAKE, M, FAKE, FAKE, H, k, FAKE, FAKE, None,
-                              FAKE, ws_bytes, None)
+        return L.li_hs_select(ctypes.byref(c), ctypes.byref(q), cand, FAKE, M, FAKE, FAKE, None, H, k, FAKE, FAKE,
+                              None, FAKE, ws_bytes, None)
 
     assert call(M=0) == B.LI_ERR_SHAPE
     assert call(M=70000) == B.LI_ERR_SHAPE
@@ -170,3 +170,30 @@ def test_fp8_validation_and_sizes(L):
     assert L.li_fp8_query_scale_offset(1, 3, 128) == 512
     assert L.li_fp8_query_bytes(1, 3, 128) == 512 + 3 * 4
     assert L.li_fp8_query_bytes(1, 64, 64) == 0 and L.li_fp8_query_bytes(1, 0, 256) == 0
+
+
+def test_rope_entry_points_validation(L):
+    c = cache()
+    rope = lambda F=32, S=2, base=10000.0: ctypes.byref(B._Rope(F, S, base))
+    ap = lambda rp, T=3, rows=FAKE, cc=c: L.li_append_latent_rope(ctypes.byref(cc), rows, FAKE, FAKE, T, rp, None)
+    assert ap(None) == B.LI_ERR_NULL
+    assert ap(rope(F=0)) == B.LI_ERR_SHAPE
+    assert ap(rope(F=65)) == B.LI_ERR_SHAPE
+    assert ap(rope(S=0)) == B.LI_ERR_SHAPE
+    assert ap(rope(F=64, S=3)) == B.LI_ERR_SHAPE          # 2 S F = 384 > r = 256
+    assert ap(rope(base=1.0)) == B.LI_ERR_SHAPE
+    assert ap(rope(), rows=None) == B.LI_ERR_NULL
+    assert ap(rope(), T=-1) == B.LI_ERR_SHAPE
+    assert ap(rope(), T=0, rows=None) == B.LI_OK
+    assert ap(rope(), cc=cache(page_size=16)) == B.LI_ERR_UNSUPPORTED
+    dec = lambda rp, dt=B.LI_BF16, D=FAKE: L.li_rope_decoder(D, FAKE, rp, 64, 128, FAKE, dt, None)
+    assert dec(None) == B.LI_ERR_NULL
+    assert dec(rope(F=0)) == B.LI_ERR_SHAPE
+    assert dec(rope(), dt=B.LI_FP8) == B.LI_ERR_UNSUPPORTED
+    assert dec(rope(), D=None) == B.LI_ERR_NULL
+    qb = lambda Q=1, d=128, d_rope=64, dt=B.LI_BF16, q=FAKE: L.li_query_bias(q, FAKE, Q, 64, d, d_rope, FAKE, dt, None)
+    assert qb(d_rope=200) == B.LI_ERR_SHAPE
+    assert qb(Q=-1) == B.LI_ERR_SHAPE
+    assert qb(dt=B.LI_FP8) == B.LI_ERR_UNSUPPORTED
+    assert qb(q=None) == B.LI_ERR_NULL
+    assert qb(Q=0, q=None) == B.LI_OK
