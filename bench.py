@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--counters", choices=("decode", "prefill"), default=None,
                     help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
@@ -366,6 +367,42 @@ def main() -> int:
         del f8pool, f8sc, f8cache, f8q
 
     # ------------------------------------------------------------------
+    # RoPE-compatible structured decoder (32 rotary frequencies x 2 sources
+    # + 128 NoPE columns of the same 256-wide latent, 64 + 64 wide native
+    # keys): rotated append + lowered-decoder absorption + bias per layer,
+    # then full LatentIndex with the bias in the scoring epilogue
+    # ------------------------------------------------------------------
+    rope = None
+    if not args.no_rope:
+        F_, S_ = 32, 2
+        rg = synth.make_rope(11, G=G, F=F_, S=S_, d_nope=d - 2 * F_, r_nope=r - 2 * S_ * F_)
+        Wd = [B.rope_decoder(tdev(rg.D[l], bf), tdev(rg.Wn[l], bf), (F_, S_)) for l in range(G)]
+        betas = [torch.from_numpy(rg.beta[l]).to(dev) for l in range(G)]
+        qt_r = [B.absorb_query(q[l], Wd[l]) for l in range(G)]
+        bias_r = [B.query_bias(q[l], betas[l], 2 * F_) for l in range(G)]
+
+        def r_prep():
+            B.append_latent_rope(cache, new_rows, new_seq, new_pos, (F_, S_))
+            for l in range(G):
+                B.absorb_query(q[l], Wd[l], out=qt_r[l])
+                B.query_bias(q[l], betas[l], 2 * F_, out=bias_r[l])
+
+        def r_full():
+            for l in range(G):
+                B.score_topk(cache, seq, pos, N, qt_r[l], w[l], k, ws=ws, out=out_b[l], bias=bias_r[l])
+
+        r_ms_prep = time_graph(capture(r_prep), reps)
+        r_ms_full = time_graph(capture(r_full), reps)
+        r_score_ms, _ = kernel_time(r_full, B.LI_KERNEL_SCORE_DECODE, reps)
+        rope = {"layout": f"{F_} frequencies x {S_} sources rotary + {r - 2 * S_ * F_} NoPE of r={r}; native key "
+                          f"{2 * F_} rotary + {d - 2 * F_} NoPE",
+                "append_rope_plus_absorb_plus_bias_x4_us": round(r_ms_prep * 1e3, 2),
+                "full_latentindex_with_bias_us_per_layer": round(r_ms_full * 1e3 / G, 2),
+                "score_kernel_with_bias_us": round(r_score_ms * 1e3, 2),
+                "score_frac_hbm_with_bias": round(bytes_launch / (r_score_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"rope {rope}")
+
+    # ------------------------------------------------------------------
     # CPU baseline: the fp64 oracle on a bounded sample of the same workload
     # ------------------------------------------------------------------
     cpu = None
@@ -413,6 +450,11 @@ def main() -> int:
                    "score_ms": round(sc_ms, 3), "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
                    "frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4), "select_ms": round(sel_ms, 3),
                    "absorb_ms": round(ab_ms, 3), "valid_pairs": pl.pairs}
+        if not args.no_rope:
+            pl.bias = torch.randn((pl.Q, H), dtype=torch.float32, device=dev)
+            b_ms, _ = kernel_time(pl.layer, B.LI_KERNEL_SCORE_PREFILL, preps)
+            prefill["score_ms_with_bias"] = round(b_ms, 3)
+            pl.bias = None
         log(f"prefill {prefill}")
         if not args.no_fp8:
             del pl
@@ -438,7 +480,8 @@ def main() -> int:
                                f"+ HS (M={M}) + per-layer baseline indexer x{G}",
                    "batch": Bn, "context": N, "heads": H, "d": d, "r": r, "k": k, "M": M, "group": G,
                    "parallelism": "single GPU"},
-        "modes": modes, "roofline": roofline, "sweep": sweep, "fp8": fp8, "prefill": prefill, "cpu_baseline": cpu,
+        "modes": modes, "roofline": roofline, "sweep": sweep, "fp8": fp8, "rope": rope, "prefill": prefill,
+        "cpu_baseline": cpu,
     }
     s = json.dumps(line)
     print(s, flush=True)
@@ -503,10 +546,12 @@ class PrefillLayer:
         self.k = p5.k
         self.pairs = int(np.sum(np.minimum(p5.qpos.astype(np.int64) + 1, n)))
         self.B = B
+        self.bias = None  # optional [Q][H] decoder bias
 
     def layer(self):
         self.B.absorb_query(self.q, self.W, out=self.qt, fp8=self.fp8)
-        self.B.score_topk(self.cache, self.seq, self.pos, self.n, self.qt, self.w, self.k, ws=self.ws, out=self.out)
+        self.B.score_topk(self.cache, self.seq, self.pos, self.n, self.qt, self.w, self.k, ws=self.ws, out=self.out,
+                          bias=self.bias)
 
 
 def setup_prefill(B, synth, dev, bf, i32, tdev, n, fp8=False):

@@ -632,14 +632,16 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
             wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
             if (inext < nt) issue(inext, pnext); // into tile i-1's slot
             if (active) {
+                // accumulators start from the heads' biases (read with the
+                // tile's first fragments) or from zero
                 f32x16 acc[HB];
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     f32x16 z = {};
                     acc[hb] = z;
                 }
-                mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                 if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
+                mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                 const float p = epilogue<HB>(acc, qr.w);
                 const int j = (ts + i) * kTile + lane;
                 if (lane < 32 && j < my_n) out[j] = p;
