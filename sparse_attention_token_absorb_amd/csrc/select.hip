@@ -207,12 +207,20 @@ struct RowGlobal {
     __device__ uint32_t key(int i) const { return key_at(r, q, i); }
     __device__ int32_t out(int i) const { return out_id(r, q, i); }
 };
+// The global tie list a filter pass wrote: (key, row index) pairs.
+struct CandGlobal {
+    const uint2 *c;
+    SelRow r;
+    int q;
+    __device__ uint32_t key(int i) const { return c[i].x; }
+    __device__ int32_t out(int i) const { return out_id(r, q, (int64_t)c[i].y); }
+};
 
 // Levels 1 and 2 over m elements restricted to (key & pmask) == prefix;
 // emits the `remaining` best of them at out[sh.cnt[0] ...].  All threads.
 // Rows left equal on all 32 bits are taken in element order, so two calls
 // over the same elements with budgets a <= b take nested sets.
-template <int T, class Src>
+template <int T, class Src, int U = 8>
 __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
                               int32_t *out, Scratch<T> &sh)
 {
@@ -225,23 +233,34 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
         const uint32_t dmask = (uint32_t)nb - 1u;
         for (int j = tid; j < nb; j += T) sh.hist[j] = 0;
         __syncthreads();
-        for (int i = tid; i < m; i += T) {
-            const uint32_t key = src.key(i);
-            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        // U elements per thread per round: their (possibly global) loads go
+        // out together before the LDS updates that use them
+        for (int i0 = tid; i0 < m; i0 += T * U) {
+            uint32_t kk[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) kk[u] = i0 + u * T < m ? src.key(i0 + u * T) : 0u;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * T < m && (kk[u] & pmask) == prefix) atomicAdd(&sh.hist[(kk[u] >> shift) & dmask], 1u);
         }
         __syncthreads();
         find_bin<T>(sh.hist, nb, remaining, sh);
         const int bin = sh.res[0];
         const uint32_t above = (uint32_t)sh.res[1];
         if (bin < 0) break; // inconsistent counts: nothing sensible to emit
-        for (int i0 = wbase; i0 < m; i0 += T) {
-            const int i = i0 + lane;
-            bool e = false;
-            if (i < m) {
-                const uint32_t key = src.key(i);
-                e = (key & pmask) == prefix && ((key >> shift) & dmask) > (uint32_t)bin;
+        for (int i0 = wbase; i0 < m; i0 += T * U) {
+            uint32_t kk[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * T + lane;
+                kk[u] = i < m ? src.key(i) : 0u;
             }
-            emit(e, e ? src.out(i) : 0, out, &sh.cnt[0]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * T + lane;
+                const bool e = i < m && (kk[u] & pmask) == prefix && ((kk[u] >> shift) & dmask) > (uint32_t)bin;
+                emit(e, e ? src.out(i) : 0, out, &sh.cnt[0]);
+            }
         }
         remaining -= above;
         prefix |= (uint32_t)bin << shift;
@@ -429,12 +448,15 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                 const uint32_t prefix = (uint32_t)bin << kDigit0Shift;
                 const uint32_t pmask = 0xFFFFFFFFu << kDigit0Shift;
                 const uint32_t need = (uint32_t)(K - above);
+                // batch depth of the level passes: 2 in the streaming mode,
+                // which runs in 64 registers
+                constexpr int UB = MODE == kStream ? 2 : 8;
                 if (nc <= CAP) {
-                    finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
+                    finish_levels<NT, CandLds, UB>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
                 } else if (cached) {
-                    finish_levels<NT>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, sh);
+                    finish_levels<NT, CacheLds, UB>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, sh);
                 } else {
-                    finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
+                    finish_levels<NT, RowGlobal, UB>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
                 }
             }
         }
@@ -646,6 +668,10 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
                 }
                 __syncthreads();
                 finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
+            } else if (nc <= ws.cap) {
+                // every tie is in the global list: rank it instead of the row
+                const uint2 *lst = (inner && !shared_list ? ws.cand2 : ws.cand) + (int64_t)q * ws.cap;
+                finish_levels<NT>(CandGlobal{lst, c.row, q}, nc, prefix, pmask, need, out, sh);
             } else {
                 finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
             }

@@ -387,6 +387,25 @@ def test_hs_nested_selection_on_a_shared_tie_digit():
     verify_hs(g, anchor, followers, M=4096, k=2048, tag="nested")
 
 
+def test_hs_anchor_tie_digit_wider_than_lds():
+    """Plain normal rows give a narrow score distribution: more rows share the
+    anchor's top-M threshold digit than the LDS tie list holds, but all of
+    them fit the workspace's candidate list, which is ranked instead of the
+    whole row."""
+    h = H()
+    say("HS anchor, tie digit wider than LDS")
+    g = synth.make_decode("widetie", 59, B=1, lens=[131072], r=256, H=64, d=128, k=2048, M=8192, G=2,
+                          heavy_frac=0.0, structure=False)
+    s = oracle.score(oracle.absorb(g.q[0][0], g.W[0]), g.w[0][0], g.latent[0], 131072)
+    key = np.sort(s)[-8192].astype(np.float32).view(np.uint32) >> 20
+    ties = int(np.sum((s.astype(np.float32).view(np.uint32) >> 20) == key))
+    assert ties > 8192, ties  # the case this test is for
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    anchor, followers = h.hs_group(g, cache, qs)
+    verify_hs(g, anchor, followers, tag="widetie")
+
+
 def test_many_queries_rows_between_8k_and_16k():
     """Prefill-style selection whose rows fit the LDS key cache (8K < n <= 16K),
     with a run of equal scores at the threshold."""
