@@ -221,7 +221,10 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
 {
     static_assert(MB == 8 || MB == 32 || MB == 128, "row block");
     constexpr int NSEG = R / kSeg;
-    constexpr int KC = D < 64 ? D : 64;      // k per staged chunk
+    // k per staged chunk: all of k at once for the small row blocks (few
+    // rows: one load round instead of two), 64 for the prefill-sized blocks
+    // (two workgroups per CU)
+    constexpr int KC = MB < 128 ? (D < 128 ? D : 128) : (D < 64 ? D : 64);
     constexpr int CT = MB == 128 ? 8 : 4;    // columns per thread
     constexpr int NCG = kSeg / CT;           // column groups
     constexpr int NRG = 256 / NCG;           // row groups
