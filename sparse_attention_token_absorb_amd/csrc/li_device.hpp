@@ -117,7 +117,11 @@ __device__ __forceinline__ float epilogue(const f32x16 (&acc)[HB], const float (
     float p = ps[0];
 #pragma unroll
     for (int hb = 1; hb < HB; ++hb) p += ps[hb];
-    return p + __shfl_xor(p, 32);
+    // the two lane halves hold the two head halves of each row: swap halves
+    // across the wave (a VALU permute; the results hold lane l%32's value and
+    // lane l%32+32's, one each) and add
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Multiplies the complex pair (re, im) by exp(i pos theta) in fp64: the

@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
 // second wave on each SIMD covers barriers and epilogues; the first radix
 // digit is counted by the selection pass instead of here.
 // ---------------------------------------------------------------------------
-template <int R, int HB, int NBUF, int QW>
+template <int R, int HB, int NBUF, int QW, int TPB>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill(
     ScoreArgs a, int tiles_per_split)
 {
@@ -622,29 +622,48 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
             issue_rows<R, CH, NIW>(pool, [&](int nr) { return base + (int64_t)nr * R; }, 0,
                                    ring + (i % NBUF) * TILE_BYTES, wv * NIW, NIW);
         };
-        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i));
-#pragma unroll 1
-        for (int i = 0; i < nt; ++i) {
-            const int inext = i + NBUF - 1;
-            const int pnext = inext < nt ? page_of(inext) : 0; // read before the barrier
-            // tile i landed (this wave's part), tiles i+1..i+NBUF-2 may still fly
-            wait_after<NIW, NBUF - 2>(min(NBUF - 2, nt - 1 - i));
-            wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
-            if (inext < nt) issue(inext, pnext); // into tile i-1's slot
-            if (active) {
-                // accumulators start from the heads' biases (read with the
-                // tile's first fragments) or from zero
-                f32x16 acc[HB];
+        // Tiles move in groups of TPB: one wait and one barrier per group.
+        // Tile i sits in slot i % NBUF; group g+NG-1 refills group g-1's slots.
+        constexpr int NG = NBUF / TPB;
+        static_assert(NG * TPB == NBUF && NG >= 2, "ring groups");
+        const int ngr = (nt + TPB - 1) / TPB;
+        for (int gq = 0; gq < NG - 1 && gq < ngr; ++gq)
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) {
-                    f32x16 z = {};
-                    acc[hb] = z;
+            for (int t = 0; t < TPB; ++t)
+                if (gq * TPB + t < nt) issue(gq * TPB + t, page_of(gq * TPB + t));
+#pragma unroll 1
+        for (int gq = 0; gq < ngr; ++gq) {
+            const int gnext = gq + NG - 1;
+            int pnext[TPB];
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) // read before the barrier
+                pnext[t] = gnext * TPB + t < nt ? page_of(gnext * TPB + t) : 0;
+            // this group landed (this wave's parts); the tiles issued after it may still fly
+            const int after = min((gq + NG - 1) * TPB, nt) - (gq + 1) * TPB;
+            wait_after<NIW, (NG - 2) * TPB < 1 ? 1 : (NG - 2) * TPB>(after > 0 ? after : 0);
+            wg_barrier(); // every part of the group landed; every wave is done with the previous group
+#pragma unroll
+            for (int t = 0; t < TPB; ++t)
+                if (gnext < ngr && gnext * TPB + t < nt) issue(gnext * TPB + t, pnext[t]);
+            if (active) {
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) {
+                    const int i = gq * TPB + t;
+                    if (i >= nt) break;
+                    // accumulators start from the heads' biases (read with the
+                    // tile's first fragments) or from zero
+                    f32x16 acc[HB];
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) {
+                        f32x16 z = {};
+                        acc[hb] = z;
+                    }
+                    if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
+                    mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
+                    const float p = epilogue<HB>(acc, qr.w);
+                    const int j = (ts + i) * kTile + lane;
+                    if (lane < 32 && j < my_n) out[j] = p;
                 }
-                if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
-                mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
-                const float p = epilogue<HB>(acc, qr.w);
-                const int j = (ts + i) * kTile + lane;
-                if (lane < 32 && j < my_n) out[j] = p;
             }
         }
     }
@@ -723,6 +742,7 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     if (prefill) {
         constexpr int NBUF = R == 256 ? 4 : 6;
         constexpr int QW = 4;
+        constexpr int TPB = 1; // tiles per barrier
         const int qblocks = (a.Q + QW - 1) / QW;
         int64_t splits = 1;
         if (qblocks < 512) splits = std::min<int64_t>((512 + qblocks - 1) / qblocks, tiles);
@@ -730,8 +750,8 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
         int64_t tps = (tiles + splits - 1) / splits;
         if (tps > kPrefillMaxTiles) tps = kPrefillMaxTiles;
         splits = (tiles + tps - 1) / tps;
-        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW>), dim3(qblocks, (unsigned)splits), dim3(64 * QW), 0, s,
-                           a, (int)tps);
+        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB>), dim3(qblocks, (unsigned)splits), dim3(64 * QW), 0,
+                           s, a, (int)tps);
         return hipGetLastError();
     }
     // decode: about one round of one workgroup per CU
