@@ -406,6 +406,21 @@ def test_hs_anchor_tie_digit_wider_than_lds():
     verify_hs(g, anchor, followers, tag="widetie")
 
 
+def test_largest_budgets():
+    """k = 65536 (the largest budget the selectors take) over sequences longer
+    and shorter than it, and HS with M = 65536, k = 32768."""
+    h = H()
+    say("largest budgets")
+    g = synth.make_decode("maxk", 60, B=2, lens=[70000, 40000], r=256, H=64, d=128, k=65536, M=65536, G=2)
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    res = h.full_layer(g, cache, qs, 0)
+    verify_full(g, 0, res, tag="maxk")
+    assert np.array_equal(h.host(res.count), np.minimum(65536, g.lens))
+    anchor, followers = h.hs_group(g, cache, qs, M=65536, k=32768)
+    verify_hs(g, anchor, followers, M=65536, k=32768, tag="maxk-hs")
+
+
 def test_many_queries_rows_between_8k_and_16k():
     """Prefill-style selection whose rows fit the LDS key cache (8K < n <= 16K),
     with a run of equal scores at the threshold."""
