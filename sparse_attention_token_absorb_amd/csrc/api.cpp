@@ -308,11 +308,14 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
 
     const bool many = Q >= 4 * cache->batch;
     const bool scored = queries->max_valid > 0;
-    // Decode scoring counts the first radix digit as it writes (the row is
-    // read once more by selection anyway); prefill scoring is MFMA-bound and
+    // Decode scoring over rows longer than 8192 counts the first radix digit
+    // as it writes (the row is read once more by selection anyway); over
+    // shorter rows the one-workgroup selection counts the keys it holds, which
+    // saves the histogram-clearing kernel; prefill scoring is MFMA-bound and
     // leaves the count to the selection pass.
     const bool fp8 = cache->dtype == LI_FP8;
-    const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8));
+    const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8)) &&
+                            li::selection_wants_counts(queries->max_valid);
     hipError_t e = hipSuccess;
     if (scored) {
         if (fused_hist) {
@@ -380,8 +383,9 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     sc.idx = idx;
     sc.count = count;
 
-    hipError_t e;
-    {
+    hipError_t e = hipSuccess;
+    const bool fused_hist = li::selection_wants_counts(M);
+    if (fused_hist) {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
         e = li::launch_hist_clear(sw, Q, stream);
     }
@@ -394,7 +398,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.out = S;
     a.out_ld = M;
     a.max_rows = M;
-    a.hist = sw.hist;
+    a.hist = fused_hist ? sw.hist : nullptr;
     {
         li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
         if (cache->dtype == LI_FP8)
@@ -406,7 +410,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     if (e != hipSuccess) return hip_fail(e, "hs score launch");
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(sc, sw, true, stream);
+        e = li::launch_select(sc, sw, fused_hist, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "hs select launch");
     return ok();

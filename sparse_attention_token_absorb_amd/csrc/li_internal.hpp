@@ -132,4 +132,11 @@ hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s);
 // filled ws.hist (histogram and row counts) for these very scores.
 hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s);
 
+// Whether a selection over rows of up to max_n scores wants the scoring
+// kernel to count the first radix digit: rows of up to 8192 scores are
+// counted by the one-workgroup selection from the keys it holds in LDS
+// anyway, which costs less than clearing the histogram in a kernel of its
+// own; longer rows are counted by the scoring kernel.
+bool selection_wants_counts(int64_t max_n);
+
 } // namespace li

@@ -694,6 +694,8 @@ int64_t cand_cap(int64_t Q, int64_t max_n) { return use_filter(Q, max_n) ? std::
 
 } // namespace
 
+bool selection_wants_counts(int64_t max_n) { return max_n > kCandCap; }
+
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n)
 {
     size_t b = (size_t)Q * kHistStride * 4;
