@@ -237,10 +237,11 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         first < a.max_rows ? (int)min64(tiles_per_wave, (a.max_rows - first + 4 * kTile - 1) / (4 * kTile)) : 0;
 
     // Start-up is a chain of dependent loads (sequence id, then page ids and
-    // the row count).  The query's fragments do not depend on it and go first;
-    // the first chunks are issued as soon as the page ids arrive, before the
-    // row count: a page id that is not in use is clamped into the pool, and
-    // what such a chunk brings in is never scored.
+    // the row count).  The query's rows, weights and biases do not depend on
+    // it and go first (into LDS, read back once all have landed); the first
+    // chunks are issued as soon as the page ids arrive, before the row count:
+    // a page id that is not in use is clamped into the pool, and what such a
+    // chunk brings in is never scored.
     lds_u8 *const ring_all = (lds_u8 *)ring_raw;
     stage_query<R, HB, NB, CHUNK>((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H,
                                   a.bias ? a.bias + (int64_t)q * a.H : nullptr, a.H, ring_all, (lds_f32 *)s_w,
