@@ -88,12 +88,34 @@ __device__ __forceinline__ int query_n(const SelCall &c, int q)
 
 __device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
+// Inclusive prefix sum over the lanes of a wave (lane 0 first), on DPP: row
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the last lane of
+// row 0 (and of row 2) is added to row 1 (row 3), and that of row 1 to rows
+// 2 and 3.  Lanes without a source read 0.  Whole waves must reach it.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    int v = (int)x;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
+    return (uint32_t)v;
+}
+
 template <int T>
 struct Scratch {
-    uint32_t hist[2048];
+    uint32_t hist[2048]; // second digit, bits [19:9]
+    uint32_t hist2[512]; // third digit, bits [8:0]
     uint32_t wtot[T / 64];
-    int res[2];
+    int res[4];
     int cnt[4];
+    // Both level histograms start at zero; visible after the caller's next barrier.
+    __device__ __forceinline__ void clear_levels()
+    {
+        for (int j = threadIdx.x; j < 2048 + 512; j += T) (j < 2048 ? hist[j] : hist2[j - 2048]) = 0;
+    }
 };
 
 // The first-digit histogram of one query, held in registers between its
@@ -113,79 +135,84 @@ struct HistRegs {
     }
 };
 
-// Block-wide search on an LDS histogram of nbins bins: the bin b holding
-// the `remaining`-th largest element and `above` = elements in bins > b.
-// sh.res[0] = b (-1 if remaining exceeds the total), sh.res[1] = above.
-template <int T>
-__device__ void find_bin(const uint32_t *h, int nbins, uint32_t remaining, Scratch<T> &sh)
+// Block-wide search on an LDS histogram of NB bins (bin order = key order)
+// for NR budgets at once: for budget j, sh.res[2j] = the bin b holding the
+// rem[j]-th largest element (-1 if rem[j] exceeds the total) and
+// sh.res[2j+1] = elements in bins > b.  Each thread sums a run of adjacent
+// bins, a DPP scan and the wave totals give every thread the count above its
+// run, and the thread whose run crosses a budget searches it.  Two barriers;
+// the caller puts a barrier between its reads of an earlier result and the
+// next call.
+template <int T, int NB, int NR>
+__device__ void find_bins(const uint32_t *h, const uint32_t (&rem)[NR], Scratch<T> &sh)
 {
+    constexpr int NW = T / 64;
+    constexpr int PER = NB >= T ? NB / T : 1; // bins per thread
+    constexpr int ACT = NB / PER;             // threads holding bins
+    static_assert(PER * ACT == NB && NR <= 2, "bins per thread");
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int per = (nbins + T - 1) / T;
-    uint32_t sum = 0;
-    for (int j = 0; j < per; ++j) {
-        const int bb = tid * per + j;
-        if (bb < nbins) sum += h[bb];
+    uint32_t v[PER];
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        v[j] = tid < ACT ? h[tid * PER + j] : 0u;
+        s += v[j];
     }
-    uint32_t suf = sum; // suffix sum within the wave: lanes >= lane
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(suf, off);
-        if (lane + off < 64) suf += v;
-    }
-    if (lane == 0) sh.wtot[wv] = suf;
-    if (tid == 0) sh.res[0] = -1;
+    // run of this thread and all later ones: the wave's suffix plus later waves
+    const uint32_t p = wave_incl_scan(s);
+    const uint32_t wtotal = (uint32_t)__builtin_amdgcn_readlane((int)p, 63);
+    if (lane == 0) sh.wtot[wv] = wtotal;
+    if (tid < NR) sh.res[2 * tid] = -1;
     __syncthreads();
     uint32_t later = 0;
-    for (int w2 = wv + 1; w2 < T / 64; ++w2) later += sh.wtot[w2];
-    const uint32_t incl = suf + later;
-    const uint32_t excl = incl - sum;
-    if (excl < remaining && incl >= remaining) {
-        uint32_t acc = excl;
-        for (int j = per - 1; j >= 0; --j) {
-            const int bb = tid * per + j;
-            if (bb >= nbins) continue;
-            if (acc + h[bb] >= remaining) {
-                sh.res[0] = bb;
-                sh.res[1] = (int)acc;
-                break;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) later += w2 > wv ? sh.wtot[w2] : 0u;
+    const uint32_t incl = wtotal - p + s + later; // elements in this run and above it
+    const uint32_t excl = incl - s;               // elements above this run
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        if (excl < rem[j] && incl >= rem[j]) {
+            uint32_t acc = excl;
+#pragma unroll
+            for (int jj = PER - 1; jj >= 0; --jj) {
+                if (acc + v[jj] >= rem[j]) {
+                    sh.res[2 * j] = tid * PER + jj;
+                    sh.res[2 * j + 1] = (int)acc;
+                    break;
+                }
+                acc += v[jj];
             }
-            acc += h[bb];
         }
     }
     __syncthreads();
 }
 
-// Lanes with e set append `val` at out[*cnt ...] (one LDS atomic per wave).
-// Whole waves must reach it.
-__device__ __forceinline__ void emit(bool e, int32_t val, int32_t *out, int *cnt)
+// Compacting append for U rounds at once: lanes with e[u] set get slots
+// base + (rank in round order, then lane order) from one LDS atomic per
+// wave on *cnt, and store(u, slot) is called for slots below cap (the count
+// still grows past cap, so overflow stays visible).  Whole waves must reach it.
+template <int U, class Store>
+__device__ __forceinline__ void wave_append(const bool (&e)[U], int *cnt, int cap, Store store)
 {
-    const uint64_t m = __ballot(e);
-    if (m == 0ull) return;
+    uint64_t m[U];
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        m[u] = __ballot(e[u]);
+        tot += __popcll(m[u]);
+    }
+    if (tot == 0) return;
     int base = 0;
-    if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, __popcll(m));
-    base = __shfl(base, 0);
-    if (e) out[base + __popcll(m & lanes_below())] = val;
-}
-
-// Lanes with e set append (key, id) to the LDS tie list (capacity CAP; the
-// slot count keeps growing past it so overflow is detectable).
-template <int CAP = kCandCap>
-__device__ __forceinline__ void push_tie(bool e, uint32_t key, int32_t id, uint32_t *ck, int32_t *ci, int *cnt)
-{
-    const uint64_t m = __ballot(e);
-    if (m == 0ull) return;
-    int base = 0;
-    if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, __popcll(m));
-    base = __shfl(base, 0);
-    const int slot = base + __popcll(m & lanes_below());
-    if (e && slot < CAP) {
-        ck[slot] = key;
-        ci[slot] = id;
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(cnt, tot);
+    base = __builtin_amdgcn_readfirstlane(base);
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int slot = base + __popcll(m[u] & below);
+        if (e[u] && slot < cap) store(u, slot);
+        base += __popcll(m[u]);
     }
 }
-
-// Digits below the first: bits [19:9] then [8:0].
-__device__ __forceinline__ int lvl_shift(int l) { return l == 1 ? 9 : 0; }
-__device__ __forceinline__ int lvl_bins(int l) { return l == 1 ? 2048 : 512; }
 
 // Element sources for the in-block levels: key(i) and the id to output.
 struct CandLds {
@@ -216,80 +243,87 @@ struct CandGlobal {
     __device__ int32_t out(int i) const { return out_id(r, q, (int64_t)c[i].y); }
 };
 
-// Levels 1 and 2 over m elements restricted to (key & pmask) == prefix;
-// emits the `remaining` best of them at out[sh.cnt[0] ...].  All threads.
-// Rows left equal on all 32 bits are taken in element order, so two calls
-// over the same elements with budgets a <= b take nested sets.
-template <int T, class Src, int U = 8>
-__device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
-                              int32_t *out, Scratch<T> &sh)
+// One digit level over m elements restricted to (key & pmask) == prefix,
+// the level's histogram pre-cleared: count, find the threshold digit, emit
+// the elements above it at out[sh.cnt[0] ...], then narrow prefix/pmask and
+// the budget.  False if the counts are inconsistent.
+template <int T, class Src, int U, int SHIFT, int NB>
+__device__ __forceinline__ bool digit_level(const Src &src, int m, uint32_t &prefix, uint32_t &pmask,
+                                            uint32_t &remaining, int32_t *out, int cap, uint32_t *hist,
+                                            Scratch<T> &sh)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wbase = tid - lane;
-    int level = 1;
-    for (; level < 3 && remaining > 0; ++level) {
-        const int shift = lvl_shift(level);
-        const int nb = lvl_bins(level);
-        const uint32_t dmask = (uint32_t)nb - 1u;
-        for (int j = tid; j < nb; j += T) sh.hist[j] = 0;
-        __syncthreads();
-        // U elements per thread per round: their (possibly global) loads go
-        // out together before the LDS updates that use them
-        for (int i0 = tid; i0 < m; i0 += T * U) {
-            uint32_t kk[U];
+    constexpr uint32_t dmask = (uint32_t)NB - 1u;
+    // U elements per thread per round: their (possibly global) loads go
+    // out together before the LDS updates that use them
+    for (int i0 = tid; i0 < m; i0 += T * U) {
+        uint32_t kk[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) kk[u] = i0 + u * T < m ? src.key(i0 + u * T) : 0u;
+        for (int u = 0; u < U; ++u) kk[u] = i0 + u * T < m ? src.key(i0 + u * T) : 0u;
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (i0 + u * T < m && (kk[u] & pmask) == prefix) atomicAdd(&sh.hist[(kk[u] >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        find_bin<T>(sh.hist, nb, remaining, sh);
-        const int bin = sh.res[0];
-        const uint32_t above = (uint32_t)sh.res[1];
-        if (bin < 0) break; // inconsistent counts: nothing sensible to emit
-        for (int i0 = wbase; i0 < m; i0 += T * U) {
-            uint32_t kk[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * T + lane;
-                kk[u] = i < m ? src.key(i) : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * T + lane;
-                const bool e = i < m && (kk[u] & pmask) == prefix && ((kk[u] >> shift) & dmask) > (uint32_t)bin;
-                emit(e, e ? src.out(i) : 0, out, &sh.cnt[0]);
-            }
-        }
-        remaining -= above;
-        prefix |= (uint32_t)bin << shift;
-        pmask |= dmask << shift;
-        __syncthreads();
-    }
-    if (remaining > 0 && level == 3) {
-        // All 32 bits resolved: the survivors share one key.  Take the first
-        // `remaining` of them in element order (rank by a block-wide count).
-        uint32_t base = 0;
-        for (int i0 = 0; i0 < m && base < remaining; i0 += T) {
-            const int i = i0 + tid;
-            const bool tie = i < m && src.key(i) == prefix;
-            const uint64_t tm = __ballot(tie);
-            if (lane == 0) sh.wtot[wv] = (uint32_t)__popcll(tm);
-            __syncthreads();
-            uint32_t before = base, total = 0;
-            for (int w2 = 0; w2 < T / 64; ++w2) {
-                const uint32_t v = sh.wtot[w2];
-                before += w2 < wv ? v : 0u;
-                total += v;
-            }
-            const bool take = tie && before + (uint32_t)__popcll(tm & lanes_below()) < remaining;
-            __syncthreads();
-            emit(take, take ? src.out(i) : 0, out, &sh.cnt[0]);
-            base += total;
-        }
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * T < m && (kk[u] & pmask) == prefix) atomicAdd(&hist[(kk[u] >> SHIFT) & dmask], 1u);
     }
     __syncthreads();
+    const uint32_t rem[1] = {remaining};
+    find_bins<T, NB, 1>(hist, rem, sh);
+    const int bin = sh.res[0];
+    const uint32_t above = (uint32_t)sh.res[1];
+    if (bin < 0) return false;
+    for (int i0 = wbase; i0 < m; i0 += T * U) {
+        bool e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * T + lane;
+            const uint32_t k = i < m ? src.key(i) : 0u;
+            e[u] = i < m && (k & pmask) == prefix && ((k >> SHIFT) & dmask) > (uint32_t)bin;
+        }
+        wave_append<U>(e, &sh.cnt[0], cap, [&](int u, int slot) { out[slot] = src.out(i0 + u * T + lane); });
+    }
+    remaining -= above;
+    prefix |= (uint32_t)bin << SHIFT;
+    pmask |= dmask << SHIFT;
+    return true;
+}
+
+// Levels 1 and 2 (bits [19:9], then [8:0]) over m elements restricted to
+// (key & pmask) == prefix; emits the `remaining` best of them at
+// out[sh.cnt[0] ...] (slots below cap).  Both level histograms must be clear
+// (Scratch::clear_levels before an earlier barrier).  All threads.  Rows
+// left equal on all 32 bits are taken in element order, so two calls over
+// the same elements with budgets a <= b take nested sets.
+template <int T, class Src, int U = 8>
+__device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
+                              int32_t *out, int cap, Scratch<T> &sh)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (remaining == 0) return;
+    if (!digit_level<T, Src, U, 9, 2048>(src, m, prefix, pmask, remaining, out, cap, sh.hist, sh)) return;
+    if (remaining == 0) return;
+    if (!digit_level<T, Src, U, 0, 512>(src, m, prefix, pmask, remaining, out, cap, sh.hist2, sh)) return;
+    if (remaining == 0) return;
+    // All 32 bits resolved: the survivors share one key.  Take the first
+    // `remaining` of them in element order (rank by a block-wide count).
+    __syncthreads(); // every thread has read sh.res before wtot is reused
+    uint32_t base = 0;
+    for (int i0 = 0; i0 < m && base < remaining; i0 += T) {
+        const int i = i0 + tid;
+        const bool tie = i < m && src.key(i) == prefix;
+        const uint64_t tm = __ballot(tie);
+        if (lane == 0) sh.wtot[wv] = (uint32_t)__popcll(tm);
+        __syncthreads();
+        uint32_t before = base, total = 0;
+        for (int w2 = 0; w2 < T / 64; ++w2) {
+            const uint32_t v = sh.wtot[w2];
+            before += w2 < wv ? v : 0u;
+            total += v;
+        }
+        const bool take[1] = {tie && before + (uint32_t)__popcll(tm & lanes_below()) < remaining};
+        __syncthreads();
+        wave_append<1>(take, &sh.cnt[0], cap, [&](int, int slot) { out[slot] = src.out(i); });
+        base += total;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -323,6 +357,7 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
         sh.cnt[0] = 0;
         sh.cnt[1] = 0;
     }
+    sh.clear_levels();
     int K = 0;
     if constexpr (MODE == kSmall) {
         constexpr int E = kCandCap / NT;
@@ -359,20 +394,27 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                     if (e * NT + tid < n) atomicAdd(&h0[kk[e] >> kDigit0Shift], 1u);
             }
             __syncthreads();
-            find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+            const uint32_t rem[1] = {(uint32_t)K};
+            find_bins<NT, kHistBins, 1>(h0, rem, sh);
             const int bin = sh.res[0];
             const int above = sh.res[1];
             if (bin >= 0) {
+                bool up[E], tie[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const bool ok = e * NT + tid < n;
                     const int dg = (int)(kk[e] >> kDigit0Shift);
-                    emit(ok && dg > bin, id[e], out, &sh.cnt[0]);
-                    push_tie(ok && dg == bin, kk[e], id[e], ck, ci, &sh.cnt[1]);
+                    up[e] = ok && dg > bin;
+                    tie[e] = ok && dg == bin;
                 }
+                wave_append<E>(up, &sh.cnt[0], c.k, [&](int u, int slot) { out[slot] = id[u]; });
+                wave_append<E>(tie, &sh.cnt[1], CAP, [&](int u, int slot) {
+                    ck[slot] = kk[u];
+                    ci[slot] = id[u];
+                });
                 __syncthreads();
-                finish_levels<NT>(CandLds{ck, ci}, sh.cnt[1], (uint32_t)bin << kDigit0Shift,
-                                  0xFFFFFFFFu << kDigit0Shift, (uint32_t)(K - above), out, sh);
+                finish_levels<NT>(CandLds{ck, ci}, min(sh.cnt[1], CAP), (uint32_t)bin << kDigit0Shift,
+                                  0xFFFFFFFFu << kDigit0Shift, (uint32_t)(K - above), out, c.k, sh);
             }
         }
     } else {
@@ -391,7 +433,8 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                 hr.load(hq);
                 hr.store(h0);
                 __syncthreads();
-                find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+                const uint32_t rem[1] = {(uint32_t)K};
+                find_bins<NT, kHistBins, 1>(h0, rem, sh);
             } else {
                 for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
                 __syncthreads();
@@ -412,7 +455,8 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                         }
                 }
                 __syncthreads();
-                find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+                const uint32_t rem[1] = {(uint32_t)K};
+                find_bins<NT, kHistBins, 1>(h0, rem, sh);
             }
             const int bin = sh.res[0];
             const int above = sh.res[1];
@@ -431,17 +475,22 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                         }
                     }
 #pragma unroll
-                    for (int b = 0; b < KB; ++b)
+                    for (int b = 0; b < KB; ++b) {
+                        const int64_t i4 = r0 + 4 * ((int64_t)b * NT + tid);
+                        bool up[4], tie[4];
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            const int64_t i = r0 + 4 * ((int64_t)b * NT + tid) + t;
                             const int dg = (int)(kk[b][t] >> kDigit0Shift);
-                            const bool ok = i < n;
-                            const bool up = ok && dg > bin;
-                            emit(up, up ? out_id(c.row, q, i) : 0, out, &sh.cnt[0]);
-                            const bool tie = ok && dg == bin;
-                            push_tie<CAP>(tie, kk[b][t], tie ? out_id(c.row, q, i) : 0, ck, ci, &sh.cnt[1]);
+                            const bool ok = i4 + t < n;
+                            up[t] = ok && dg > bin;
+                            tie[t] = ok && dg == bin;
                         }
+                        wave_append<4>(up, &sh.cnt[0], c.k, [&](int t, int slot) { out[slot] = out_id(c.row, q, i4 + t); });
+                        wave_append<4>(tie, &sh.cnt[1], CAP, [&](int t, int slot) {
+                            ck[slot] = kk[b][t];
+                            ci[slot] = out_id(c.row, q, i4 + t);
+                        });
+                    }
                 }
                 __syncthreads();
                 const int nc = sh.cnt[1];
@@ -452,11 +501,12 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
                 // which runs in 64 registers
                 constexpr int UB = MODE == kStream ? 2 : 8;
                 if (nc <= CAP) {
-                    finish_levels<NT, CandLds, UB>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
+                    finish_levels<NT, CandLds, UB>(CandLds{ck, ci}, nc, prefix, pmask, need, out, c.k, sh);
                 } else if (cached) {
-                    finish_levels<NT, CacheLds, UB>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, sh);
+                    finish_levels<NT, CacheLds, UB>(CacheLds{cache, c.row, q}, n, prefix, pmask, need, out, c.k,
+                                                    sh);
                 } else {
-                    finish_levels<NT, RowGlobal, UB>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
+                    finish_levels<NT, RowGlobal, UB>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, c.k, sh);
                 }
             }
         }
@@ -529,14 +579,10 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
     if (tid < 4) s_cnt[tid] = 0;
     hr.store(h0);
     __syncthreads();
-    find_bin<T>(h0, kHistBins, (uint32_t)K, sh);
+    const uint32_t rem[2] = {(uint32_t)K, (uint32_t)(Ki > 0 ? Ki : K)};
+    find_bins<T, kHistBins, 2>(h0, rem, sh);
     const int bin = sh.res[0];
-    int bin_i = -1;
-    if (Ki > 0) {
-        __syncthreads(); // every thread has read sh.res before it is rewritten
-        find_bin<T>(h0, kHistBins, (uint32_t)Ki, sh);
-        bin_i = sh.res[0];
-    }
+    const int bin_i = Ki > 0 ? sh.res[2] : -1;
     if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
     const bool inner = Ki > 0;
     const bool sep = inner && bin_i != bin; // inner ties need a list of their own
@@ -556,10 +602,19 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
                 }
             }
         }
-    const int lu = nup ? atomicAdd(&s_cnt[0], nup) : 0;
-    const int lt = ntie ? atomicAdd(&s_cnt[1], ntie) : 0;
-    const int lui = nupi ? atomicAdd(&s_cnt[2], nupi) : 0;
-    const int lti = ntiei ? atomicAdd(&s_cnt[3], ntiei) : 0;
+    // this thread's offsets in the workgroup's four runs: an exclusive wave
+    // scan plus one LDS atomic per wave and run
+    const int cnts[4] = {nup, ntie, nupi, ntiei};
+    int loc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t incl = wave_incl_scan((uint32_t)cnts[j]);
+        const int wt = __builtin_amdgcn_readlane((int)incl, 63);
+        int wb = 0;
+        if (wt && (tid & 63) == 0) wb = atomicAdd(&s_cnt[j], wt);
+        wb = __builtin_amdgcn_readfirstlane(wb);
+        loc[j] = wb + (int)incl - cnts[j];
+    }
     __syncthreads();
     if (tid < 4) {
         const int slot = tid == 0 ? kSlotUpO : tid == 1 ? kSlotTieO : tid == 2 ? kSlotUpI : kSlotTieI;
@@ -567,7 +622,7 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
         s_base[tid] = v ? atomicAdd(&hq[slot], v) : 0;
     }
     __syncthreads();
-    int pu = s_base[0] + lu, pt = s_base[1] + lt, pui = s_base[2] + lui, pti = s_base[3] + lti;
+    int pu = s_base[0] + loc[0], pt = s_base[1] + loc[1], pui = s_base[2] + loc[2], pti = s_base[3] + loc[3];
     int32_t *out = c.idx + (int64_t)q * c.k;
     int32_t *outi = inner ? c.idx_inner + (int64_t)q * c.k_inner : nullptr;
     uint2 *cand = ws.cand + (int64_t)q * ws.cap;
@@ -580,14 +635,16 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
             if (i < n) {
                 const int dg = (int)(kk[b][t] >> kDigit0Shift);
                 if (dg > bin) {
-                    out[pu++] = out_id(c.row, q, i);
+                    if (pu < c.k) out[pu] = out_id(c.row, q, i);
+                    ++pu;
                 } else if (dg == bin) {
                     if (pt < ws.cap) cand[pt] = make_uint2(kk[b][t], (uint32_t)i);
                     ++pt;
                 }
                 if (inner) {
                     if (dg > bin_i) {
-                        outi[pui++] = out_id(c.row, q, i);
+                        if (pui < c.k_inner) outi[pui] = out_id(c.row, q, i);
+                        ++pui;
                     } else if (sep && dg == bin_i) {
                         if (pti < ws.cap) cand2[pti] = make_uint2(kk[b][t], (uint32_t)i);
                         ++pti;
@@ -612,6 +669,7 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
     const int kout = inner ? c.k_inner : c.k;
     int32_t *out = (inner ? c.idx_inner : c.idx) + (int64_t)q * kout;
+    sh.clear_levels();
     // Loaded up front: the histogram, the counters, and the head of this
     // part's tie list (the nested part's list is the likely one; the outer
     // list is read later only when the two threshold digits coincide).
@@ -633,15 +691,11 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     if (Kp > 0) {
         hr.store(h0);
         __syncthreads();
-        find_bin<NT>(h0, kHistBins, (uint32_t)K, sh);
+        const uint32_t rem[2] = {(uint32_t)K, (uint32_t)Kp};
+        find_bins<NT, kHistBins, 2>(h0, rem, sh);
         const int bin_o = sh.res[0];
-        int bin = bin_o, above = sh.res[1];
-        if (inner) {
-            __syncthreads(); // every thread has read sh.res before it is rewritten
-            find_bin<NT>(h0, kHistBins, (uint32_t)Kp, sh);
-            bin = sh.res[0];
-            above = sh.res[1];
-        }
+        const int bin = inner ? sh.res[2] : bin_o;
+        const int above = inner ? sh.res[3] : sh.res[1];
         if (bin >= 0 && bin_o >= 0) {
             const bool shared_list = inner && bin == bin_o;
             const int nc = inner && !shared_list ? tie_i : tie_o;
@@ -667,13 +721,13 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
                     }
                 }
                 __syncthreads();
-                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, sh);
+                finish_levels<NT>(CandLds{ck, ci}, nc, prefix, pmask, need, out, kout, sh);
             } else if (nc <= ws.cap) {
                 // every tie is in the global list: rank it instead of the row
                 const uint2 *lst = (inner && !shared_list ? ws.cand2 : ws.cand) + (int64_t)q * ws.cap;
-                finish_levels<NT>(CandGlobal{lst, c.row, q}, nc, prefix, pmask, need, out, sh);
+                finish_levels<NT>(CandGlobal{lst, c.row, q}, nc, prefix, pmask, need, out, kout, sh);
             } else {
-                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, sh);
+                finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, kout, sh);
             }
         }
     }
