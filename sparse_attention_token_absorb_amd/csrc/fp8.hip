@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
 // ---------------------------------------------------------------------------
 constexpr int kPrefillMaxTilesF8 = 2048; // max tiles per split (their page ids sit in LDS)
 
-template <int R, int HB, int NBUF>
+template <int R, int HB, int NBUF, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill_fp8(
     ScoreArgs a, const float *pool_scales, int64_t qscale_off, int tiles_per_split)
 {
@@ -657,9 +657,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     scb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + CODE_BYTES +
                                                                                        (nr * NSEG + g) * 4) >> 23) &
                                    0xFFu);
+                // accumulators start from the heads' biases, or (no bias) the
+                // first step adds to a constant zero
                 f32x16 acc[HB];
+                if constexpr (BIAS) {
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
+                    for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
+                }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const int c = 4 * s + 2 * gk;
@@ -669,9 +673,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     const int g = (s * 64) / kSeg;
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb)
-                        acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[hb][s], bv, acc[hb], 0, 0, 0,
-                                                                                  sa[hb][g], 0, scb[g]);
+                    for (int hb = 0; hb < HB; ++hb) {
+                        const f32x16 zero = {};
+                        acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            qa[hb][s], bv, !BIAS && s == 0 ? zero : acc[hb], 0, 0, 0, sa[hb][g], 0, scb[g]);
+                    }
                 }
                 const float pv = epilogue<HB>(acc, wr);
                 const int j = (ts + i) * kTile + lane;
@@ -694,8 +700,12 @@ hipError_t launch_prefill_fp8_rh(const ScoreArgs &a, const float *pool_scales, i
     int64_t tps = (tiles + splits - 1) / splits;
     if (tps > kPrefillMaxTilesF8) tps = kPrefillMaxTilesF8;
     splits = (tiles + tps - 1) / tps;
-    hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s, a,
-                       pool_scales, qscale_off, (int)tps);
+    if (a.bias)
+        hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF, true>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s,
+                           a, pool_scales, qscale_off, (int)tps);
+    else
+        hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF, false>), dim3(qblocks, (unsigned)splits), dim3(256), 0,
+                           s, a, pool_scales, qscale_off, (int)tps);
     return hipGetLastError();
 }
 

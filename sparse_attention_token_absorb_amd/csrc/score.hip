@@ -114,7 +114,9 @@ __device__ __forceinline__ void mfma_steps(const lds_u8 *buf, const QueryRegs<R,
 
 // All R/16 MFMA steps over one full-width tile in LDS, with the B fragments
 // read D steps ahead of their use so LDS latency hides behind the MFMAs.
-template <int R, int HB, int CH, int D>
+// ZC: the accumulators start from zero (the first step takes a constant 0
+// as its addend; acc is not read).
+template <int R, int HB, int CH, int D, bool ZC = false>
 __device__ __forceinline__ void mfma_tile_prefetch(const lds_u8 *buf, const QueryRegs<R, HB> &qr,
                                                    f32x16 (&acc)[HB])
 {
@@ -134,8 +136,11 @@ __device__ __forceinline__ void mfma_tile_prefetch(const lds_u8 *buf, const Quer
         const bf16x8 cur = b[s % DD];
         if (s + DD < KS) b[s % DD] = frag(s + DD);
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][s], cur, acc[hb], 0, 0, 0);
+        for (int hb = 0; hb < HB; ++hb) {
+            const f32x16 zero = {};
+            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][s], cur, ZC && s == 0 ? zero : acc[hb], 0, 0,
+                                                              0);
+        }
     }
     // Keep that order in the schedule: the first DD reads, then per step
     // its HB MFMAs followed by the read for step s + DD.
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
 // second wave on each SIMD covers barriers and epilogues; the first radix
 // digit is counted by the selection pass instead of here.
 // ---------------------------------------------------------------------------
-template <int R, int HB, int NBUF, int QW, int TPB>
+template <int R, int HB, int NBUF, int QW, int TPB, bool BIAS>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) void k_score_prefill(
     ScoreArgs a, int tiles_per_split)
 {
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
         qr.load((const u16 *)a.qt, a.w, 0); // zero fragments
     }
-    const bool has_bias = a.bias != nullptr;
+    const bool has_bias = BIAS && a.bias != nullptr;
     if (has_bias) // read back by this wave only (its own LDS writes come first)
         s_b[wv * 64 + lane] = q < a.Q && lane < a.H ? a.bias[(int64_t)q * a.H + lane] : 0.0f;
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
@@ -651,16 +656,18 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
                 for (int t = 0; t < TPB; ++t) {
                     const int i = gq * TPB + t;
                     if (i >= nt) break;
-                    // accumulators start from the heads' biases (read with the
-                    // tile's first fragments) or from zero
+                    // accumulators start from the heads' biases (read from LDS
+                    // with the tile's first fragments) or from zero
                     f32x16 acc[HB];
+                    if constexpr (BIAS) {
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        f32x16 z = {};
-                        acc[hb] = z;
+                        for (int hb = 0; hb < HB; ++hb) {
+                            f32x16 z = {};
+                            acc[hb] = z;
+                        }
+                        if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
                     }
-                    if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
-                    mfma_tile_prefetch<R, HB, CH, 4>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
+                    mfma_tile_prefetch<R, HB, CH, 4, !BIAS>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                     const float p = epilogue<HB>(acc, qr.w);
                     const int j = (ts + i) * kTile + lane;
                     if (lane < 32 && j < my_n) out[j] = p;
@@ -751,8 +758,12 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
         int64_t tps = (tiles + splits - 1) / splits;
         if (tps > kPrefillMaxTiles) tps = kPrefillMaxTiles;
         splits = (tiles + tps - 1) / tps;
-        hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB>), dim3(qblocks, (unsigned)splits), dim3(64 * QW), 0,
-                           s, a, (int)tps);
+        if (a.bias)
+            hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB, true>), dim3(qblocks, (unsigned)splits),
+                               dim3(64 * QW), 0, s, a, (int)tps);
+        else
+            hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB, false>), dim3(qblocks, (unsigned)splits),
+                               dim3(64 * QW), 0, s, a, (int)tps);
         return hipGetLastError();
     }
     // decode: about one round of one workgroup per CU
