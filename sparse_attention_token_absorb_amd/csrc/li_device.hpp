@@ -139,6 +139,15 @@ __device__ __forceinline__ void rope_pair(double &re, double &im, int pos, doubl
     im = b;
 }
 
+// x rounded to the nearest bf16 value (ties to even), returned as a float
+// (finite x).
+__device__ __forceinline__ float bf16_round(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __uint_as_float(u & 0xFFFF0000u);
+}
+
 // Adds each accumulator's head bias (b: the query's 64 staged biases, heads
 // past H zero) before the ReLU; accumulator r of block hb holds head
 // hb*32 + (r/4)*8 + (lane/32)*4 + r%4 of tile row lane % 32.

@@ -562,7 +562,6 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
     static_assert(NBUF >= 3, "ring depth");
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * TILE_BYTES];
     __shared__ int32_t s_page_raw[kPrefillMaxTiles / 2 + 2];
-    __shared__ __attribute__((aligned(16))) float s_b[QW * 64]; // each wave's query: heads' decoder biases
     lds_u8 *ring = (lds_u8 *)ring_raw;
     lds_i32 *s_page = (lds_i32 *)s_page_raw;
 
@@ -593,9 +592,34 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
         qr.load((const u16 *)a.qt, a.w, 0); // zero fragments
     }
-    const bool has_bias = BIAS && a.bias != nullptr;
-    if (has_bias) // read back by this wave only (its own LDS writes come first)
-        s_b[wv * 64 + lane] = q < a.Q && lane < a.H ? a.bias[(int64_t)q * a.H + lane] : 0.0f;
+    // With a bias, each tile's accumulators start as A_b . B_1: A_b holds
+    // the head's bias split into three bf16 parts (exact: 8 + 8 + 8
+    // significant bits) at k = 0..2, B_1 ones at k = 0..2 for every row, so
+    // one MFMA per head block sets every row to the fp32 bias.
+    bf16x8 ab[HB], bones;
+    if constexpr (BIAS) {
+        const bool lo_half = lane < 32;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const float b = lo_half && q < a.Q && h < a.H ? a.bias[(int64_t)q * a.H + h] : 0.0f;
+            const float hi = bf16_round(b);
+            const float mid = bf16_round(b - hi);
+            const float lo = bf16_round((b - hi) - mid);
+            bf16x8 v = {};
+            v[0] = (__bf16)hi;
+            v[1] = (__bf16)mid;
+            v[2] = (__bf16)lo;
+            ab[hb] = v;
+        }
+        bf16x8 o = {};
+        if (lo_half) {
+            o[0] = (__bf16)1.0f;
+            o[1] = (__bf16)1.0f;
+            o[2] = (__bf16)1.0f;
+        }
+        bones = o;
+    }
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
     const u16 *pool = (const u16 *)a.pool;
 
@@ -656,16 +680,14 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
                 for (int t = 0; t < TPB; ++t) {
                     const int i = gq * TPB + t;
                     if (i >= nt) break;
-                    // accumulators start from the heads' biases (read from LDS
-                    // with the tile's first fragments) or from zero
+                    // the chains start from the heads' biases or a constant zero
                     f32x16 acc[HB];
                     if constexpr (BIAS) {
 #pragma unroll
                         for (int hb = 0; hb < HB; ++hb) {
-                            f32x16 z = {};
-                            acc[hb] = z;
+                            const f32x16 zero = {};
+                            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[hb], bones, zero, 0, 0, 0);
                         }
-                        if (has_bias) add_bias<HB>(acc, (const lds_f32 *)s_b + wv * 64);
                     }
                     mfma_tile_prefetch<R, HB, CH, 4, !BIAS>(ring + (i % NBUF) * TILE_BYTES, qr, acc);
                     const float p = epilogue<HB>(acc, qr.w);
