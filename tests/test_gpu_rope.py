@@ -264,3 +264,58 @@ def test_bias_on_the_register_staged_and_fp32_paths():
             check_scores(sc[i, :n], o, f"bias r={r} q{i} scores")
             K = min(g.k, n)
             check_topk(sel[i], int(cnt[i]), oracle.topk(o, K), o, None, K, rms(o), f"bias r={r} q{i} top-k")
+
+
+@pytest.mark.parametrize("H", [1, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("many", [False, True])
+def test_bias_enters_exactly(H, dtype, many):
+    """On all-zero latent rows every score is sum_h w_h max(b_h, 0): the bias
+    must reach the ReLU as the exact fp32 value (the prefill kernels build it
+    from three bf16 parts inside the MFMA).  One head: the score is one fp32
+    product, within 2^-22; 64 heads: within the fp32 sum's rounding (1e-5 of
+    the sum of magnitudes), which also catches a head mapped to another's
+    bias.  Biases span 2^-12..2^12, weights take both signs."""
+    h = _gpu()
+    dev = h.device()
+    say(f"bias exact H={H} {dtype} {'prefill' if many else 'decode'}")
+    rng = np.random.default_rng(9100 + H + (7 if many else 0) + (3 if dtype == "fp8" else 0))
+    r, d = 256, 128
+    lens = [300, 170]
+    pages = [(n + 63) // 64 for n in lens]
+    bt = np.full((len(lens), max(pages)), -1, dtype=np.int32)
+    nxt = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = np.arange(nxt, nxt + p)
+        nxt += p
+    if many:  # 8 queries per sequence at spread positions: the prefill kernels
+        qseq = np.repeat(np.arange(len(lens)), 8)
+        qpos = np.concatenate([np.linspace(0, n - 1, 8).astype(np.int64) for n in lens])
+    else:
+        qseq = np.arange(len(lens))
+        qpos = np.asarray(lens) - 1
+    Q = len(qseq)
+    if dtype == "fp8":
+        cache = B.LatentCache(torch.zeros((nxt, 64, r), dtype=torch.uint8, device=dev), h.i32(bt), h.i32(lens),
+                              torch.zeros((nxt, 64, r // 128), dtype=torch.float32, device=dev))
+        q = h.to_dev(rng.standard_normal((Q, H, d)).astype(np.float32), torch.bfloat16)
+        W = h.to_dev((rng.standard_normal((d, r)) / 16).astype(np.float32), torch.bfloat16)
+        qt = B.absorb_query(q, W, fp8=True)
+    else:
+        cache = B.LatentCache(torch.zeros((nxt, 64, r), dtype=torch.bfloat16, device=dev), h.i32(bt), h.i32(lens))
+        qt = h.to_dev(rng.standard_normal((Q, H, r)).astype(np.float32), torch.bfloat16)
+    w = rng.standard_normal((Q, H)).astype(np.float32)
+    bias = (rng.standard_normal((Q, H)) * np.exp2(rng.uniform(-12, 12, (Q, H)))).astype(np.float32)
+    nvalid = np.minimum(qpos + 1, np.asarray(lens)[qseq])
+    maxv = int(nvalid.max())
+    out = B.score_topk(cache, h.i32(qseq), h.i32(qpos), maxv, qt, torch.from_numpy(w).to(dev), 64,
+                       keep_scores=True, bias=torch.from_numpy(bias).to(dev))
+    got = out.scores.cpu().numpy()
+    terms = w.astype(np.float64) * np.maximum(bias.astype(np.float64), 0.0)
+    want = terms.sum(axis=1)
+    mag = np.abs(terms).sum(axis=1)
+    tol = mag * (2.0 ** -22 if H == 1 else 1e-5) + 1e-30
+    for i in range(Q):
+        row = got[i, : nvalid[i]].astype(np.float64)
+        err = np.abs(row - want[i]).max()
+        assert err <= tol[i], f"query {i}: max error {err:.3e} > {tol[i]:.3e} (score {want[i]:.6e})"
