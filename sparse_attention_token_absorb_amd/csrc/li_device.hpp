@@ -148,6 +148,38 @@ __device__ __forceinline__ float bf16_round(float x)
     return __uint_as_float(u & 0xFFFF0000u);
 }
 
+// MFMA operands that set a 32x32 accumulator block to the heads' biases:
+// A_b row h (lanes 0..31) holds bias[h] split into three bf16 parts at
+// k = 0..2 (exact: 8 + 8 + 8 significant bits), B_1 ones at k = 0..2 for
+// every column, so v_mfma_f32_32x32x16_bf16(A_b, B_1, 0) gives bias[h] in
+// every row of head h.  bias: the query's H values (null or !live: zeros).
+template <int HB>
+__device__ __forceinline__ void bias_operands(const float *bias, int H, bool live, bf16x8 (&ab)[HB], bf16x8 &bones)
+{
+    const int lane = threadIdx.x & 63;
+    const bool lo_half = lane < 32;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 32 + (lane & 31);
+        const float b = bias && lo_half && live && h < H ? bias[h] : 0.0f;
+        const float hi = bf16_round(b);
+        const float mid = bf16_round(b - hi);
+        const float lo = bf16_round((b - hi) - mid);
+        bf16x8 v = {};
+        v[0] = (__bf16)hi;
+        v[1] = (__bf16)mid;
+        v[2] = (__bf16)lo;
+        ab[hb] = v;
+    }
+    bf16x8 o = {};
+    if (lo_half) {
+        o[0] = (__bf16)1.0f;
+        o[1] = (__bf16)1.0f;
+        o[2] = (__bf16)1.0f;
+    }
+    bones = o;
+}
+
 // Adds each accumulator's head bias (b: the query's 64 staged biases, heads
 // past H zero) before the ReLU; accumulator r of block hb holds head
 // hb*32 + (r/4)*8 + (lane/32)*4 + r%4 of tile row lane % 32.

@@ -592,34 +592,9 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
         qr.load((const u16 *)a.qt, a.w, 0); // zero fragments
     }
-    // With a bias, each tile's accumulators start as A_b . B_1: A_b holds
-    // the head's bias split into three bf16 parts (exact: 8 + 8 + 8
-    // significant bits) at k = 0..2, B_1 ones at k = 0..2 for every row, so
-    // one MFMA per head block sets every row to the fp32 bias.
+    // with a bias, one MFMA per head block starts each tile's accumulators
     bf16x8 ab[HB], bones;
-    if constexpr (BIAS) {
-        const bool lo_half = lane < 32;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const int h = hb * 32 + (lane & 31);
-            const float b = lo_half && q < a.Q && h < a.H ? a.bias[(int64_t)q * a.H + h] : 0.0f;
-            const float hi = bf16_round(b);
-            const float mid = bf16_round(b - hi);
-            const float lo = bf16_round((b - hi) - mid);
-            bf16x8 v = {};
-            v[0] = (__bf16)hi;
-            v[1] = (__bf16)mid;
-            v[2] = (__bf16)lo;
-            ab[hb] = v;
-        }
-        bf16x8 o = {};
-        if (lo_half) {
-            o[0] = (__bf16)1.0f;
-            o[1] = (__bf16)1.0f;
-            o[2] = (__bf16)1.0f;
-        }
-        bones = o;
-    }
+    if constexpr (BIAS) bias_operands<HB>(a.bias + (int64_t)(q < a.Q ? q : 0) * a.H, a.H, q < a.Q, ab, bones);
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
     const u16 *pool = (const u16 *)a.pool;
 
