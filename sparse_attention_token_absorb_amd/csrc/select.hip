@@ -6,11 +6,11 @@
 // them (§3.2, §C.4).
 //
 // Scores become order-preserving uint32 keys, selected by radix digits of
-// 12, 11 and 9 bits (most significant first).  The decode scoring kernels
-// already count the first digit (key >> 20) into a per-query 4096-bin
-// histogram as they write the scores, and record the row count beside it,
-// so the threshold bin is known before the rows are read again; otherwise
-// the selection counts it itself.  One pass over each row then emits the
+// 12, 11 and 9 bits (most significant first).  For rows longer than 8192
+// the decode scoring kernels already count the first digit (key >> 20)
+// into a per-query 4096-bin histogram as they write the scores, and record
+// the row count beside it, so the threshold bin is known before the rows
+// are read again; otherwise the selection counts it itself.  One pass over each row then emits the
 // rows above the threshold digit and compacts the rows on it; the last two
 // digits are resolved among those few in LDS.
 //   * Few queries with long rows (decode at 8K-128K): the pass is spread
@@ -22,11 +22,13 @@
 //     (k_select); rows of at most 8192 elements are loaded once, up front.
 // Every kernel issues all of its input loads before its first wait (rows
 // are read 16 bytes per lane; the scores were written by other XCDs, so
-// each load misses the local L2).  Emission uses wavefront ballots (one LDS
-// atomic per wave, mbcnt offsets).  Rows whose key equals the final
-// threshold key are taken in element order, as many as the budget needs:
-// equal scores are interchangeable, and the fixed order keeps nested
-// selections nested.
+// each load misses the local L2).  The kernels are chains of short
+// dependent steps, so the steps are few: threshold searches scan with DPP
+// (no LDS permutes), and emission ranks lanes with ballots and popcounts
+// under one LDS atomic per wave for all of a thread's elements.  Rows whose
+// key equals the final threshold key are taken in element order, as many as
+// the budget needs: equal scores are interchangeable, and the fixed order
+// keeps nested selections nested.
 #include "li_internal.hpp"
 
 #include <algorithm>
