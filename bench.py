@@ -503,7 +503,8 @@ def main() -> int:
 def model_step(B, dev, i32, capture, time_graph, reps):
     """Indexer work of one decode step (batch 1) over a 61-layer map shaped
     like the pages' DeepSeek-V3.2 setting (§C.3, §C.4, §B.3): layer 0 keeps
-    its own indexer, layers 1-60 form 15 groups of G = 4.  Every cache is
+    its own indexer, layers 1-60 form 15 groups of G = 4 (and, as the pages'
+    G = 8 variant of §4.4 and §A.5, 7 groups of 8 plus one of 4).  Every cache is
     segmented FP8 as in the pages' inference (§B.2, §C.1): native per-layer
     keys 128 wide (128 code bytes + one scale: the 132 B per token and layer
     of §B.1), group latents 256 wide.  Each layer's work is what its indexer
@@ -514,14 +515,16 @@ def model_step(B, dev, i32, capture, time_graph, reps):
       latentindex layer 0 as dsa; each group caches one latent, all 4 layers
                   score it with their absorbed queries and select top-2048
       hs          as latentindex, but the anchor proposes its top-8192 and the
-                  3 followers rescore only those (§3.2, §C.4)
+                  group's followers rescore only those (§3.2, §C.4)
       indexcache  layer 0 and every group's anchor as dsa; followers reuse
                   the anchor's selection (no work)
     Inputs are seeded device-side normals; only timing is reported."""
     import numpy as np
     import torch
-    L_max, H, d, r, k, M, G, n_groups = 131072, 64, 128, 256, 2048, 8192, 4, 15
-    n_layers = 1 + G * n_groups
+    L_max, H, d, r, k, M = 131072, 64, 128, 256, 2048, 8192
+    maps = {"G4": [4] * 15, "G8": [8] * 7 + [4]}
+    n_layers = 1 + 60
+    n_groups = max(len(m) for m in maps.values())
     bf = torch.bfloat16
     gen = torch.Generator(device=dev)
     gen.manual_seed(61)
@@ -560,10 +563,10 @@ def model_step(B, dev, i32, capture, time_graph, reps):
         B.absorb_query(q[l], eye, out=qk[l], fp8=True)
         B.score_topk(keys[l], seq0, pos, Lc, qk[l], w[l], k, ws=ws, out=out)
 
-    def run(method, Lc, pos):
+    def run(method, Lc, pos, groups):
         dsa_layer(0, Lc, pos)
-        for gi in range(n_groups):
-            l0 = 1 + gi * G
+        l0 = 1
+        for gi, G in enumerate(groups):
             if method == "dsa":
                 for l in range(l0, l0 + G):
                     dsa_layer(l, Lc, pos)
@@ -579,23 +582,32 @@ def model_step(B, dev, i32, capture, time_graph, reps):
                         B.score_topk(lat[gi], seq0, pos, Lc, ql[l], w[l], M, k_inner=k, ws=ws, out=outM)
                     else:
                         B.hs_select(lat[gi], seq0, pos, Lc, outM.idx, outM.count, ql[l], w[l], k, ws=ws_hs, out=out)
+            l0 += G
 
-    res = {}
+    res, res8 = {}, {}
     for Lc in (8192, 32768, 131072):
         pos = i32([Lc - 1])
-        ms = {}
+        ms, ms8 = {}, {}
         for method in ("dsa", "latentindex", "hs", "indexcache"):
-            gr = capture(lambda: run(method, Lc, pos))
+            gr = capture(lambda: run(method, Lc, pos, maps["G4"]))
             ms[method] = time_graph(gr, reps)
             del gr
+            if method != "dsa":  # the same work under either map
+                gr = capture(lambda: run(method, Lc, pos, maps["G8"]))
+                ms8[method] = time_graph(gr, reps)
+                del gr
         res[str(Lc)] = {f"{m}_ms": round(v, 4) for m, v in ms.items()}
+        res8[str(Lc)] = {f"{m}_ms": round(v, 4) for m, v in ms8.items()}
         for m in ("latentindex", "hs", "indexcache"):
             res[str(Lc)][f"{m}_speedup_vs_dsa"] = round(ms["dsa"] / ms[m], 3)
+            res8[str(Lc)][f"{m}_speedup_vs_dsa"] = round(ms["dsa"] / ms8[m], 3)
     del keys, lat
     torch.cuda.empty_cache()
-    return {"layer_map": f"{n_layers} layers: layer 0 independent + {n_groups} groups of {G} (FP8 caches; native "
+    return {"layer_map": f"{n_layers} layers: layer 0 independent + 15 groups of 4 (FP8 caches; native "
                          f"keys {d} wide, latents {r} wide; H={H}, k={k}, M={M}, batch 1)",
             "per_step": res,
+            "layer_map_g8": "layer 0 independent + 7 groups of 8 + 1 group of 4, otherwise the same",
+            "per_step_g8": res8,
             "context_from_the_pages": "HS 2.30-2.72x over native DSA decode indexer time across 8K-128K, measured "
                                       "on eight GPUs with tensor parallelism 8 (another machine; context only)"}
 
