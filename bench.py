@@ -570,7 +570,6 @@ def model_step(B, dev, i32, capture, time_graph, reps):
     q = [torch.randn((1, H, d), generator=gen, device=dev).to(bf) for _ in range(n_layers)]
     W = [(torch.randn((d, r), generator=gen, device=dev) / 16.0).to(bf) for _ in range(n_layers)]
     w = [torch.nn.functional.softplus(torch.randn((1, H), generator=gen, device=dev)) for _ in range(n_layers)]
-    eye = torch.eye(d, device=dev).to(bf)
     new_key = torch.randn((1, d), generator=gen, device=dev).to(bf)
     new_lat = torch.randn((1, r), generator=gen, device=dev).to(bf)
     qk = [B.Fp8Query.empty(1, H, d, dev) for _ in range(n_layers)]
@@ -584,7 +583,7 @@ def model_step(B, dev, i32, capture, time_graph, reps):
 
     def dsa_layer(l, Lc, pos):
         B.append_latent(keys[l], new_key, seq0, pos)
-        B.absorb_query(q[l], eye, out=qk[l], fp8=True)
+        B.absorb_query(q[l], None, out=qk[l], fp8=True)  # a native query: quantized, no decoder
         B.score_topk(keys[l], seq0, pos, Lc, qk[l], w[l], k, ws=ws, out=out)
 
     def run(method, Lc, pos, groups):

@@ -173,6 +173,9 @@ LI_API li_status li_append_latent_rope(const li_cache *cache, const void *rows, 
  * buffer of li_fp8_query_bytes(Q, H, r) bytes holding the codes [Q][H][r]
  * followed, at byte offset li_fp8_query_scale_offset(Q, H, r), by the
  * scales [Q][H][r/128] fp32.  r in {128, 256}, d in {32,64,128,256}.
+ * LI_FP8 with w_dec NULL (d == r): no decoder; q itself is rotated and
+ * quantized (the query of a per-layer indexer scoring its own FP8 keys),
+ * exactly as with an identity w_dec.  Other dtypes require w_dec.
  */
 LI_API li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32_t Q, int32_t H,
                           int32_t d, int32_t r, li_dtype dtype, hipStream_t stream);

@@ -314,17 +314,25 @@ def query_bias(q: torch.Tensor, beta: torch.Tensor, d_rope: int, out: Optional[t
     return out
 
 
-def absorb_query(q: torch.Tensor, w_dec: torch.Tensor, out=None, fp8: bool = False):
+def absorb_query(q: torch.Tensor, w_dec: Optional[torch.Tensor], out=None, fp8: bool = False):
     """li_absorb_query: q [Q][H][d] x W_dec [d][r] -> q_tilde [Q][H][r]
-    (an Fp8Query with fp8=True: bf16 inputs, rotated and quantized output)."""
+    (an Fp8Query with fp8=True: bf16 inputs, rotated and quantized output;
+    with fp8=True, w_dec None quantizes q itself, r = d)."""
     dev = q.device
     _need(q, "q", q.dtype, dev)
     dt = _li_dtype(q.dtype)
-    _need(w_dec, "w_dec", q.dtype, dev)
-    if q.dim() != 3 or w_dec.dim() != 2 or w_dec.shape[0] != q.shape[2]:
-        raise ValueError("q must be [Q][H][d] and w_dec [d][r]")
+    if w_dec is None:
+        if not fp8:
+            raise ValueError("w_dec may be None only with fp8=True")
+        if q.dim() != 3:
+            raise ValueError("q must be [Q][H][d]")
+        r = int(q.shape[2])
+    else:
+        _need(w_dec, "w_dec", q.dtype, dev)
+        if q.dim() != 3 or w_dec.dim() != 2 or w_dec.shape[0] != q.shape[2]:
+            raise ValueError("q must be [Q][H][d] and w_dec [d][r]")
+        r = int(w_dec.shape[1])
     Q, H, d = (int(x) for x in q.shape)
-    r = int(w_dec.shape[1])
     if fp8:
         if q.dtype != torch.bfloat16:
             raise TypeError("FP8 absorption takes bf16 q and w_dec")

@@ -243,8 +243,10 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
     if (dtype != LI_FP32 && d != 32 && d != 64 && d != 128 && d != 256)
         return fail(LI_ERR_UNSUPPORTED, "bf16 absorption needs d in {32,64,128,256}, got %d", d);
     if (dtype == LI_FP32 && (d <= 0 || d > 1024)) return fail(LI_ERR_SHAPE, "d=%d outside [1, 1024]", d);
+    if (!w_dec && dtype != LI_FP8) return fail(LI_ERR_NULL, "w_dec is NULL (only LI_FP8 takes no decoder)");
+    if (!w_dec && d != r) return fail(LI_ERR_SHAPE, "without a decoder d (%d) must equal r (%d)", d, r);
     if (Q == 0) return ok();
-    if (!q || !w_dec || !q_tilde) return fail(LI_ERR_NULL, "q/w_dec/q_tilde is NULL");
+    if (!q || !q_tilde) return fail(LI_ERR_NULL, "q/q_tilde is NULL");
     hipError_t e;
     {
         li::TimedScope ts(LI_KERNEL_ABSORB, stream);

@@ -215,7 +215,10 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
 // through the same LDS and each (row, segment) is rotated and quantized by a
 // half-wave.
 // ---------------------------------------------------------------------------
-template <int R, int D, int MB>
+// IDENT: no decoder (W unused, D == R): the query itself is rotated and
+// quantized (a per-layer indexer's query).
+constexpr int64_t kAbsorbRowMax = 1024; // rows up to which the per-row kernel is used
+template <int R, int D, int MB, bool IDENT = false>
 __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, uint8_t *codes, float *qscales,
                                                     int64_t QH)
 {
@@ -245,6 +248,23 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
     const int64_t mb0 = (int64_t)blockIdx.x * MB;
     const int tr = tid / NCG, tc = tid % NCG;
 
+    if constexpr (IDENT) {
+        static_assert(D == R, "the identity keeps the width");
+        // this segment of each row, bf16 -> fp32 (exact)
+        for (int it = tid; it < MB * (kSeg / 8); it += 256) {
+            const int row = it / (kSeg / 8), cc = (it % (kSeg / 8)) * 8;
+            const int64_t m = mb0 + row;
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (m < QH) raw = *(const u32x4 *)(q + m * R + c0 + cc);
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+            float *dst = s_out + row * OLD + cc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[2 * i] = __uint_as_float(wd[i] << 16);
+                dst[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+            }
+        }
+    } else {
     double acc[RT][CT];
 #pragma unroll
     for (int i = 0; i < RT; ++i)
@@ -296,6 +316,7 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
     for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < CT; ++j) s_out[(tr * RT + i) * OLD + tc * CT + j] = (float)acc[i][j];
+    }
     __syncthreads();
     const int lane = tid & 63, wv = tid >> 6;
     // quantization: the MB rows split over the 8 half-waves, NR rows each per pass
@@ -322,6 +343,57 @@ __global__ __launch_bounds__(256) void k_absorb_fp8(const u16 *q, const u16 *W, 
                 *(uint32_t *)(codes + m * R + c0 + 4 * l32) = cw[k];
                 if (l32 == 0) qscales[m * NSEG + g] = exp2i(e[k]);
             }
+        }
+    }
+}
+
+// Few rows (decode): one workgroup per (query, head) row and segment, so a
+// batch-1 decode step spreads over H x R/128 workgroups instead of a handful.
+// Thread t owns output column t % 128 and half of k; the two fp64 partial
+// sums meet in LDS (exact, as above, so the split does not change the
+// result); the first wave rotates and quantizes the row segment.
+// IDENT as above.
+template <int R, int D, bool IDENT>
+__global__ __launch_bounds__(256) void k_absorb_fp8_row(const u16 *q, const u16 *W, uint8_t *codes, float *qscales)
+{
+    constexpr int NSEG = R / kSeg;
+    constexpr int KH = D / 2; // k per thread
+    __shared__ float s_q[D];
+    __shared__ double s_part[kSeg];
+    __shared__ float s_out[kSeg];
+    const int tid = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const int g = blockIdx.y;
+    const int c0 = g * kSeg;
+    const int c = tid & (kSeg - 1), half = tid >> 7;
+    if constexpr (IDENT) {
+        static_assert(D == R, "the identity keeps the width");
+        if (tid < kSeg) s_out[tid] = bf16_to_f32(q[m * D + c0 + tid]);
+    } else {
+        for (int i = tid; i < D; i += 256) s_q[i] = bf16_to_f32(q[m * D + i]);
+        float wv[KH];
+#pragma unroll
+        for (int kk = 0; kk < KH; ++kk) wv[kk] = bf16_to_f32(W[(int64_t)(half * KH + kk) * R + c0 + c]);
+        __syncthreads();
+        double acc = 0.0;
+#pragma unroll
+        for (int kk = 0; kk < KH; ++kk) acc = __builtin_fma((double)s_q[half * KH + kk], (double)wv[kk], acc);
+        if (half) s_part[c] = acc;
+        __syncthreads();
+        if (!half) s_out[c] = (float)(acc + s_part[c]);
+    }
+    __syncthreads();
+    if (tid < 64) { // both half-waves of wave 0 take the row; the first stores it
+        const int l32 = tid & 31;
+        float x[1][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[0][t] = s_out[4 * l32 + t];
+        int e[1];
+        uint32_t cw[1];
+        rotate_quantize<1>(x, l32, e, cw);
+        if (tid < 32) {
+            *(uint32_t *)(codes + m * R + c0 + 4 * l32) = cw[0];
+            if (l32 == 0) qscales[m * NSEG + g] = exp2i(e[0]);
         }
     }
 }
@@ -741,19 +813,25 @@ hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int6
     return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
 }
 
-template <int R, int D>
+template <int R, int D, bool IDENT = false>
 void launch_absorb_fp8_rd(const u16 *q, const u16 *W, uint8_t *codes, float *scales, int64_t QH, hipStream_t s)
 {
-    // many rows: big register tiles; few rows: small blocks, more workgroups
+    // many rows: big register tiles; few rows: small blocks, more workgroups;
+    // decode-sized: a workgroup per row segment
+    if (QH <= kAbsorbRowMax) {
+        hipLaunchKernelGGL((k_absorb_fp8_row<R, D, IDENT>), dim3((unsigned)QH, R / kSeg), dim3(256), 0, s, q, W, codes,
+                           scales);
+        return;
+    }
     if ((QH + 127) / 128 >= 256)
-        hipLaunchKernelGGL((k_absorb_fp8<R, D, 128>), dim3((unsigned)((QH + 127) / 128), R / kSeg), dim3(256), 0, s,
-                           q, W, codes, scales, QH);
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 128, IDENT>), dim3((unsigned)((QH + 127) / 128), R / kSeg), dim3(256),
+                           0, s, q, W, codes, scales, QH);
     else if ((QH + 31) / 32 >= 64)
-        hipLaunchKernelGGL((k_absorb_fp8<R, D, 32>), dim3((unsigned)((QH + 31) / 32), R / kSeg), dim3(256), 0, s, q,
-                           W, codes, scales, QH);
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 32, IDENT>), dim3((unsigned)((QH + 31) / 32), R / kSeg), dim3(256), 0,
+                           s, q, W, codes, scales, QH);
     else
-        hipLaunchKernelGGL((k_absorb_fp8<R, D, 8>), dim3((unsigned)((QH + 7) / 8), R / kSeg), dim3(256), 0, s, q, W,
-                           codes, scales, QH);
+        hipLaunchKernelGGL((k_absorb_fp8<R, D, 8, IDENT>), dim3((unsigned)((QH + 7) / 8), R / kSeg), dim3(256), 0, s,
+                           q, W, codes, scales, QH);
 }
 
 template <int R>
@@ -797,6 +875,13 @@ hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH,
     uint8_t *codes = (uint8_t *)qt;
     float *scales = (float *)((uint8_t *)qt + fp8_query_scale_offset(QH, 1, r));
     const u16 *qq = (const u16 *)q, *ww = (const u16 *)W;
+    if (!W) { // no decoder: the query (d == r) is rotated and quantized as it is
+        if (d != r) return hipErrorInvalidValue;
+        if (r == 256) launch_absorb_fp8_rd<256, 256, true>(qq, nullptr, codes, scales, QH, s);
+        else if (r == 128) launch_absorb_fp8_rd<128, 128, true>(qq, nullptr, codes, scales, QH, s);
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (r == 256) return launch_absorb_fp8_r<256>(qq, ww, codes, scales, QH, d, s);
     if (r == 128) return launch_absorb_fp8_r<128>(qq, ww, codes, scales, QH, d, s);
     return hipErrorInvalidValue;

@@ -124,6 +124,11 @@ def test_absorb_and_append_validation(L):
     assert a(Q=-2) == B.LI_ERR_SHAPE
     assert a(q=None) == B.LI_ERR_NULL
     assert a(Q=0) == B.LI_OK
+    # no decoder: only for FP8, and only at d == r
+    n = lambda **kw: L.li_absorb_query(FAKE, None, FAKE, 1, 64, kw.get("d", 128), kw.get("r", 128),
+                                       kw.get("dt", B.LI_FP8), None)
+    assert n(dt=B.LI_BF16) == B.LI_ERR_NULL
+    assert n(d=128, r=256) == B.LI_ERR_SHAPE
     c = cache()
     assert L.li_append_latent(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == B.LI_ERR_SHAPE
     assert L.li_append_latent(ctypes.byref(c), None, FAKE, FAKE, 3, None) == B.LI_ERR_NULL

@@ -93,6 +93,24 @@ def test_fp8_absorb_is_bit_exact():
         assert np.array_equal(gc, oc), f"codes differ at {np.argwhere(gc != oc)[:4].tolist()}"
 
 
+def test_fp8_query_without_decoder_is_bit_exact():
+    """No decoder (a per-layer indexer's own query): q itself is rotated and
+    quantized, bit for bit what the oracle gives for an identity decoder, at
+    every row-block size."""
+    h = _gpu()
+    for (Q, H, r) in ((1, 64, 128), (3, 64, 256), (40, 64, 128), (530, 64, 256)):
+        say(f"no-decoder quantization Q={Q} H={H} r={r}")
+        rng = np.random.default_rng(700 + Q + r)
+        q = synth.round_bf16(rng.standard_normal((Q, H, r)).astype(np.float32))
+        q[0, 0] = 0.0
+        q[-1, -1, :7] = synth.round_bf16(np.float32(3e4))
+        fq = B.absorb_query(h.to_dev(q, torch.bfloat16), None, fp8=True)
+        gc, gs = h.host(fq.codes()), h.host(fq.scales())
+        oc, os_ = oracle.absorb_fp8(q, np.eye(r, dtype=np.float32))
+        assert np.array_equal(gs, os_), f"scales differ at {np.argwhere(gs != os_)[:4].tolist()}"
+        assert np.array_equal(gc, oc), f"codes differ at {np.argwhere(gc != oc)[:4].tolist()}"
+
+
 def fp8_layer(h, g, cache, qs, l, k=None, k_inner=0):
     fq = B.absorb_query(h.to_dev(g.q[l], torch.bfloat16), h.to_dev(g.W[l], torch.bfloat16), fp8=True)
     out = B.score_topk(cache, qs.seq, qs.pos, qs.max_valid, fq, h.head_weights(g, l), g.k if k is None else k,
