@@ -273,15 +273,24 @@ __device__ __forceinline__ bool digit_level(const Src &src, int m, uint32_t &pre
     const int bin = sh.res[0];
     const uint32_t above = (uint32_t)sh.res[1];
     if (bin < 0) return false;
+    // when the threshold digit holds exactly the elements still needed (the
+    // usual case once the list is down to a few hundred), they are all taken
+    // here and the next level is skipped
+    const bool all = above + hist[bin] == remaining;
     for (int i0 = wbase; i0 < m; i0 += T * U) {
         bool e[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = i0 + u * T + lane;
             const uint32_t k = i < m ? src.key(i) : 0u;
-            e[u] = i < m && (k & pmask) == prefix && ((k >> SHIFT) & dmask) > (uint32_t)bin;
+            const uint32_t dg = (k >> SHIFT) & dmask;
+            e[u] = i < m && (k & pmask) == prefix && (dg > (uint32_t)bin || (all && dg == (uint32_t)bin));
         }
         wave_append<U>(e, &sh.cnt[0], cap, [&](int u, int slot) { out[slot] = src.out(i0 + u * T + lane); });
+    }
+    if (all) {
+        remaining = 0;
+        return true;
     }
     remaining -= above;
     prefix |= (uint32_t)bin << SHIFT;
