@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--no-model", action="store_true")
@@ -348,6 +349,71 @@ def main() -> int:
         log(f"sweep {sweep}")
 
     # ------------------------------------------------------------------
+    # The two other decode workloads: a single 8K sequence (config 2, full
+    # LatentIndex on all four layers) and 16 ragged paged sequences of
+    # 16K-32K rows (config 3, full LatentIndex and HS); each layer absorbs
+    # its decoder, scores and selects, as one captured graph per mode
+    # ------------------------------------------------------------------
+    configs = {}
+    if not args.no_configs:
+        for cname, gc in (("config2_decode_b1_n8192", synth.config2()), ("config3_ragged_b16_n16k_32k", synth.config3())):
+            log(f"{cname} inputs")
+            Bc = gc.B
+            pool_c = torch.zeros((gc.num_pages, 64, gc.r), dtype=bf, device=dev)
+            cache_c = B.LatentCache(pool_c, i32(gc.block_table), i32(gc.lens))
+            for b in range(Bc):
+                n_b = int(gc.lens[b])
+                B.append_latent(cache_c, tdev(gc.latent[b][:n_b], bf), i32(np.full(n_b, b)), i32(np.arange(n_b)))
+            seq_c, pos_c = i32(gc.qseq), i32(gc.qpos)
+            n_q = [int(min(gc.qpos[i] + 1, gc.lens[gc.qseq[i]])) for i in range(gc.Q)]
+            Nc = max(n_q)
+            q_c = [tdev(gc.q[l], bf) for l in range(gc.G)]
+            W_c = [tdev(gc.W[l], bf) for l in range(gc.G)]
+            w_c = [torch.from_numpy(gc.w[l]).to(dev) for l in range(gc.G)]
+            qt_c = [torch.empty((gc.Q, gc.H, gc.r), dtype=bf, device=dev) for _ in range(gc.G)]
+            ws_c = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, gc.Q, Nc, gc.H, gc.r, gc.M, 0), dtype=torch.uint8,
+                               device=dev)
+            ws_hc = torch.empty(B.workspace_bytes(B.LI_OP_HS_SELECT, gc.Q, 0, gc.H, gc.r, gc.k, gc.M),
+                                dtype=torch.uint8, device=dev)
+            ti = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+            o_full = [B.TopK(ti(gc.Q, gc.k), ti(gc.Q)) for _ in range(gc.G)]
+            o_anc = B.TopK(ti(gc.Q, gc.M), ti(gc.Q), ti(gc.Q, gc.k), ti(gc.Q))
+
+            def full_c():
+                for l in range(gc.G):
+                    B.absorb_query(q_c[l], W_c[l], out=qt_c[l])
+                    B.score_topk(cache_c, seq_c, pos_c, Nc, qt_c[l], w_c[l], gc.k, ws=ws_c, out=o_full[l])
+
+            def hs_c():
+                for l in range(gc.G):
+                    B.absorb_query(q_c[l], W_c[l], out=qt_c[l])
+                    if l == 0:
+                        B.score_topk(cache_c, seq_c, pos_c, Nc, qt_c[0], w_c[0], gc.M, k_inner=gc.k, ws=ws_c,
+                                     out=o_anc)
+                    else:
+                        B.hs_select(cache_c, seq_c, pos_c, Nc, o_anc.idx, o_anc.count, qt_c[l], w_c[l], gc.k, ws=ws_hc,
+                                    out=o_full[l])
+
+            entry = {"batch": Bc, "rows_per_query": [min(n_q), max(n_q)]}
+            gr = capture(full_c)
+            ms_f = time_graph(gr, reps)
+            del gr
+            entry["full_latentindex_us_per_layer"] = round(ms_f * 1e3 / gc.G, 2)
+            entry["full_rows_per_s"] = round(gc.G * sum(n_q) / (ms_f * 1e-3), 1)
+            if Bc > 1:
+                gr = capture(hs_c)
+                ms_h = time_graph(gr, reps)
+                del gr
+                entry["hs_us_per_group"] = round(ms_h * 1e3, 2)
+                entry["hs_rows_per_s"] = round((sum(n_q) + (gc.G - 1) * sum(min(gc.M, n) for n in n_q)) /
+                                               (ms_h * 1e-3), 1)
+                entry["hs_speedup_over_full_group"] = round(ms_f / ms_h, 3)
+            configs[cname] = entry
+            del cache_c, pool_c, ws_c, ws_hc, gc
+            torch.cuda.empty_cache()
+        log(f"configs {configs}")
+
+    # ------------------------------------------------------------------
     # Segmented FP8 cache (same latent, rotated and quantized on append):
     # full LatentIndex x4 layers and HS, decode scoring against HBM
     # ------------------------------------------------------------------
@@ -513,7 +579,8 @@ def main() -> int:
                                f"+ HS (M={M}) + per-layer baseline indexer x{G}",
                    "batch": Bn, "context": N, "heads": H, "d": d, "r": r, "k": k, "M": M, "group": G,
                    "parallelism": "single GPU"},
-        "modes": modes, "roofline": roofline, "sweep": sweep, "fp8": fp8, "rope": rope, "model": model,
+        "modes": modes, "roofline": roofline, "sweep": sweep, "configs": configs, "fp8": fp8, "rope": rope,
+        "model": model,
         "prefill": prefill, "cpu_baseline": cpu,
     }
     s = json.dumps(line)

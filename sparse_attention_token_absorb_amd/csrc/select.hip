@@ -350,6 +350,53 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
 enum { kSmall = 0, kCached = 1, kStream = 2 };
 constexpr int kStreamCap = 4096; // tied rows kept in LDS by the streaming mode
 
+// Keys and output ids of elements e * T + tid (e < E) of a row of at most mx
+// elements (zero past mx).  The map and the row are branched on once, not
+// per element, and indices are clamped into the row, so every load of a
+// phase is in flight at once: one round trip for the map, one for the keys
+// and ids.  Map entries past the row's count may be -1; they read element 0,
+// whose key is never used for them.
+template <int E>
+__device__ __forceinline__ void load_small(const SelRow &r, int q, int mx, uint32_t (&kk)[E], int32_t (&id)[E])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        kk[e] = 0u;
+        id[e] = 0;
+    }
+    if (mx <= 0) return;
+    int64_t j[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) j[e] = min(e * NT + tid, mx - 1);
+    if (r.gmap) {
+        const int32_t *g = r.gmap + (int64_t)q * r.gld;
+        int32_t v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = g[j[e]];
+#pragma unroll
+        for (int e = 0; e < E; ++e) j[e] = v[e] < 0 ? 0 : (v[e] < r.ld ? v[e] : r.ld - 1);
+    }
+    const float *S = r.S + (int64_t)q * r.ld;
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = S[j[e]];
+    if (r.omap) {
+        const int32_t *o = r.omap + (int64_t)q * r.old;
+#pragma unroll
+        for (int e = 0; e < E; ++e) id[e] = o[min(e * NT + tid, mx - 1)];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) id[e] = e * NT + tid;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool live = e * NT + tid < mx;
+        kk[e] = live ? score_key(s[e]) : 0u;
+        id[e] = live ? id[e] : 0;
+    }
+}
+
 template <bool HIST, int MODE>
 __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspace &ws)
 {
@@ -375,16 +422,7 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
         const int mx = (int)c.max_n;
         uint32_t kk[E];
         int32_t id[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int i = e * NT + tid;
-            kk[e] = 0u;
-            id[e] = 0;
-            if (i < mx) {
-                kk[e] = key_at(c.row, q, i);
-                id[e] = out_id(c.row, q, i);
-            }
-        }
+        load_small<E>(c.row, q, mx, kk, id);
         HistRegs<NT> hr;
         int n;
         if constexpr (HIST) {
