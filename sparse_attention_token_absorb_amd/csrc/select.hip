@@ -106,11 +106,37 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
     return (uint32_t)v;
 }
 
+// Smallest and largest of x over the wave (unsigned), in every lane: DPP
+// row shifts leave each row's extreme in its last lane (a lane without a
+// source keeps its own value), and the four rows are combined by readlane.
+__device__ __forceinline__ void wave_min_max(uint32_t &lo, uint32_t &hi)
+{
+#define LI_MINMAX_STEP(ctrl)                                                                     \
+    lo = min(lo, (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, ctrl, 0xf, 0xf, false)); \
+    hi = max(hi, (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, ctrl, 0xf, 0xf, false));
+    LI_MINMAX_STEP(0x111) // row_shr:1
+    LI_MINMAX_STEP(0x112) // row_shr:2
+    LI_MINMAX_STEP(0x114) // row_shr:4
+    LI_MINMAX_STEP(0x118) // row_shr:8
+#undef LI_MINMAX_STEP
+    uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)lo, 15);
+    uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hi, 15);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        l = min(l, (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r + 15));
+        h = max(h, (uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r + 15));
+    }
+    lo = l;
+    hi = h;
+}
+
 template <int T>
 struct Scratch {
     uint32_t hist[2048]; // second digit, bits [19:9]
     uint32_t hist2[512]; // third digit, bits [8:0]
     uint32_t wtot[T / 64];
+    uint32_t wlo[T / 64]; // per-wave key range (short-row selection)
+    uint32_t whi[T / 64];
     int res[4];
     int cnt[4];
     // Both level histograms start at zero; visible after the caller's next barrier.
@@ -436,11 +462,40 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
             if constexpr (HIST) {
                 hr.store(h0);
             } else {
+                // The keys of the row move to (key - min) << s, s as large as
+                // the row's key range allows: a strictly increasing map, so
+                // the selection and its ties are those of the raw keys, but
+                // the first digit now splits the row's own range 4096 ways
+                // (rows of similar scores otherwise pile into a few bins of
+                // the raw top 12 bits: contended counts, long tie lists).
+                uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (e * NT + tid < n) {
+                        lo = min(lo, kk[e]);
+                        hi = max(hi, kk[e]);
+                    }
+                wave_min_max(lo, hi);
+                if ((tid & 63) == 0) {
+                    sh.wlo[tid >> 6] = lo;
+                    sh.whi[tid >> 6] = hi;
+                }
                 for (int j = tid; j < kHistBins; j += NT) h0[j] = 0;
                 __syncthreads();
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (e * NT + tid < n) atomicAdd(&h0[kk[e] >> kDigit0Shift], 1u);
+                for (int w2 = 0; w2 < NT / 64; ++w2) {
+                    lo = min(lo, sh.wlo[w2]);
+                    hi = max(hi, sh.whi[w2]);
+                }
+                const int bits = 32 - __clz(hi - lo);               // bits of the key range
+                const int shl = kDigit0Shift - max(bits - 12, 0); // left shift, 0..20
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if (e * NT + tid < n) {
+                        kk[e] = (kk[e] - lo) << shl;
+                        atomicAdd(&h0[kk[e] >> kDigit0Shift], 1u);
+                    }
+                }
             }
             __syncthreads();
             const uint32_t rem[1] = {(uint32_t)K};
