@@ -183,7 +183,8 @@ __device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const
                                            lds_f32 *s_w, lds_f32 *s_b)
 {
     constexpr int PR = R / 8;
-    constexpr int NIC = CHUNK / 1024;
+    constexpr int NIC = R / 32; // 16 query rows of 2R bytes, 1 KiB per instruction
+    static_assert(CHUNK >= 32 * R, "a ring slot holds 16 query rows");
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int issued = 0;
@@ -212,18 +213,20 @@ __device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const
 
 // ---------------------------------------------------------------------------
 // Decode: few queries, long rows.  Workgroup = 4 waves of one query; wave w
-// streams tiles row0 + (w + 4 i) * 32.  Each tile moves as two half-width
-// chunks (32 rows x r/2 columns) through a per-wave ring of NB chunk
-// buffers, so NB-1 chunks stay in flight while the wave computes.
+// streams tiles row0 + (w + 4 i) * 32.  Each tile moves as CPT chunks of
+// 32 rows x r/CPT columns (two half-width chunks at r = 256, where a whole
+// tile is 16 KiB; whole tiles at r <= 128) through a per-wave ring of NB
+// chunk buffers, so NB-1 chunks stay in flight while the wave computes.
 // ---------------------------------------------------------------------------
-template <int R, int HB, bool GATHER, int NB>
+template <int R, int HB, bool GATHER, int NB, int CPT>
 __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per_wave)
 {
-    constexpr int HALF = R / 2;                 // columns per chunk
-    constexpr int CHUNK = kTile * HALF * 2;     // bytes per chunk
+    static_assert(CPT == 1 || CPT == 2, "chunks per tile");
+    constexpr int WC = R / CPT;                 // columns per chunk
+    constexpr int CHUNK = kTile * WC * 2;       // bytes per chunk
     constexpr int NIC = CHUNK / 1024;           // DMA instructions per chunk
-    constexpr int CH = HALF / 8;                // 16-byte pieces per chunk row
-    constexpr int KSH = HALF / 16;              // MFMA k-steps per chunk
+    constexpr int CH = WC / 8;                  // 16-byte pieces per chunk row
+    constexpr int KSH = WC / 16;                // MFMA k-steps per chunk
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * CHUNK];
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTiles * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
@@ -292,19 +295,19 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         wait_lds();
     }
     auto issue = [&](int c) {
-        const int i = c >> 1;
+        const int i = c / CPT;
         lds_u8 *buf = ring + (c % NB) * CHUNK;
         if constexpr (GATHER) {
             const __attribute__((address_space(3))) int32_t *rows =
                 (const __attribute__((address_space(3))) int32_t *)s_row + (wv * kGatherTiles + i) * kTile;
-            issue_rows<R, CH, NIC>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c & 1) * HALF, buf, 0, NIC);
+            issue_rows<R, CH, NIC>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c % CPT) * WC, buf, 0, NIC);
         } else {
             const int64_t t0 = tile_row0(i);
             const int64_t base = ((int64_t)clamp_page(bt[t0 >> 6]) * kPage + (t0 & 63)) * R;
-            issue_rows<R, CH, NIC>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c & 1) * HALF, buf, 0, NIC);
+            issue_rows<R, CH, NIC>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c % CPT) * WC, buf, 0, NIC);
         }
     };
-    const int npro = min(NB - 1, 2 * nt_max);
+    const int npro = min(NB - 1, CPT * nt_max);
     for (int c = 0; c < npro; ++c) issue(c);
 
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     int nt = 0;
     if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
-    const int nchunks = 2 * nt; // <= 2 * nt_max: chunks issued above past it are waited for, never used
+    const int nchunks = CPT * nt; // <= CPT * nt_max: chunks issued above past it are waited for, never used
     // the query's rows and weights were issued before the chunks: they have
     // landed once at most the chunks are outstanding
     wait_after<NIC, NB - 1>(npro);
@@ -334,14 +337,16 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         }
         wait_after<NIC, NB - 1>(min(NB - 1, nchunks - 1 - c));
         const lds_u8 *buf = ring + (c % NB) * CHUNK;
-        if ((c & 1) == 0) {
+        if (CPT == 1 || c % CPT == 0) {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) acc[hb] = qr.b[hb];
             mfma_steps<R, HB, 0, KSH, CH>(buf, qr, acc);
         } else {
-            mfma_steps<R, HB, KSH, KSH, CH>(buf, qr, acc);
+            if constexpr (CPT == 2) mfma_steps<R, HB, KSH, KSH, CH>(buf, qr, acc);
+        }
+        if (c % CPT == CPT - 1) {
             const float p = epilogue<HB>(acc, qr.w);
-            const int64_t j = tile_row0(c >> 1) + lane;
+            const int64_t j = tile_row0(c / CPT) + lane;
             if (lane < 32 && j < n) {
                 out[j] = p;
                 if (a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
@@ -719,9 +724,10 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
 }
 
 // Decode kernel choice.  Measured on MI355X: the register-staged kernel is
-// faster for r <= 128 over contiguous prefixes (its deeper in-flight window
-// matters most when each tile is small); the LDS ring is faster for r = 256
-// and for gathered rows.  LI_DECODE_PATH=lds|vgpr overrides (read once).
+// faster for r = 64 over contiguous prefixes (its deeper in-flight window
+// matters most when each tile is small); the LDS ring is faster from r = 128
+// (whole-tile chunks there) and for gathered rows.  LI_DECODE_PATH=lds|vgpr
+// overrides (read once).
 int decode_path_override()
 {
     static const int path = [] {
@@ -737,7 +743,7 @@ bool use_vgpr_decode(int r, bool gather)
 {
     const int o = decode_path_override();
     if (o >= 0) return o == 1;
-    return r <= 128 && !gather;
+    return r <= 64 && !gather;
 }
 
 template <int R, int HB>
@@ -785,11 +791,14 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
         return hipGetLastError();
     }
     // chunk ring depth: as deep as LDS allows next to the histogram
-    constexpr int NB = R == 256 ? 4 : 8;
+    constexpr int CPT = R == 256 ? 2 : 1;
+    constexpr int NB = R == 128 ? 4 : (R == 256 ? 4 : 8);
     if (a.cand)
-        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                           (int)tpw);
     else
-        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                           (int)tpw);
     return hipGetLastError();
 }
 
