@@ -137,6 +137,7 @@ struct Scratch {
     uint32_t wtot[T / 64];
     uint32_t wlo[T / 64]; // per-wave key range (short-row selection)
     uint32_t whi[T / 64];
+    int few[64]; // element indices of a threshold digit holding at most 64 elements
     int res[4];
     int cnt[4];
     // Both level histograms start at zero; visible after the caller's next barrier.
@@ -271,6 +272,34 @@ struct CandGlobal {
     __device__ int32_t out(int i) const { return out_id(r, q, (int64_t)c[i].y); }
 };
 
+// The last step when at most 64 elements are left to choose from: wave 0
+// holds one per lane (element list[l], or element l without a list) and
+// ranks it by a pass over the other lanes' keys (larger key first, then
+// lower element index), so element x is taken iff fewer than `need` live
+// elements precede it; its slot is base + rank.  This is the order the
+// digit passes give (ties in element order) without their barriers.  Live:
+// (key & pmask) == prefix.  Wave 0 only.
+template <class Src>
+__device__ __forceinline__ void rank_take(const Src &src, int cnt, const int *list, uint32_t prefix, uint32_t pmask,
+                                          uint32_t need, int32_t *out, int cap, int base)
+{
+    const int lane = threadIdx.x & 63;
+    const int x = lane < cnt ? (list ? list[lane] : lane) : 0;
+    const uint32_t k = lane < cnt ? src.key(x) : 0u;
+    const bool live = lane < cnt && (k & pmask) == prefix;
+    const uint64_t lm = __ballot(live);
+    uint32_t rank = 0;
+    for (int j = 0; j < cnt; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)k, j);
+        const int xj = __builtin_amdgcn_readlane(x, j);
+        rank += ((lm >> j) & 1ull) && (kj > k || (kj == k && xj < x)) ? 1u : 0u;
+    }
+    if (live && rank < need) {
+        const int slot = base + (int)rank;
+        if (slot < cap) out[slot] = src.out(x);
+    }
+}
+
 // One digit level over m elements restricted to (key & pmask) == prefix,
 // the level's histogram pre-cleared: count, find the threshold digit, emit
 // the elements above it at out[sh.cnt[0] ...], then narrow prefix/pmask and
@@ -283,6 +312,7 @@ __device__ __forceinline__ bool digit_level(const Src &src, int m, uint32_t &pre
     const int tid = threadIdx.x, lane = tid & 63;
     const int wbase = tid - lane;
     constexpr uint32_t dmask = (uint32_t)NB - 1u;
+    if (tid == 0) sh.cnt[2] = 0; // the short list below; find_bins' barriers publish it
     // U elements per thread per round: their (possibly global) loads go
     // out together before the LDS updates that use them
     for (int i0 = tid; i0 < m; i0 += T * U) {
@@ -303,18 +333,32 @@ __device__ __forceinline__ bool digit_level(const Src &src, int m, uint32_t &pre
     // usual case once the list is down to a few hundred), they are all taken
     // here and the next level is skipped
     const bool all = above + hist[bin] == remaining;
+    // a threshold digit of at most 64 elements is listed in this pass and
+    // ranked in one wave after it, which ends the selection here
+    const bool listed = !all && hist[bin] <= 64u;
     for (int i0 = wbase; i0 < m; i0 += T * U) {
-        bool e[U];
+        bool e[U], f[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = i0 + u * T + lane;
             const uint32_t k = i < m ? src.key(i) : 0u;
             const uint32_t dg = (k >> SHIFT) & dmask;
-            e[u] = i < m && (k & pmask) == prefix && (dg > (uint32_t)bin || (all && dg == (uint32_t)bin));
+            const bool in = i < m && (k & pmask) == prefix;
+            e[u] = in && (dg > (uint32_t)bin || (all && dg == (uint32_t)bin));
+            f[u] = listed && in && dg == (uint32_t)bin;
         }
         wave_append<U>(e, &sh.cnt[0], cap, [&](int u, int slot) { out[slot] = src.out(i0 + u * T + lane); });
+        if (listed) wave_append<U>(f, &sh.cnt[2], 64, [&](int u, int slot) { sh.few[slot] = i0 + u * T + lane; });
     }
     if (all) {
+        remaining = 0;
+        return true;
+    }
+    if (listed) {
+        __syncthreads(); // the list and the output count are complete
+        if (tid < 64)
+            rank_take(src, min(sh.cnt[2], 64), sh.few, prefix | ((uint32_t)bin << SHIFT), pmask | (dmask << SHIFT),
+                      remaining - above, out, cap, sh.cnt[0]);
         remaining = 0;
         return true;
     }
@@ -336,6 +380,10 @@ __device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t p
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (remaining == 0) return;
+    if (m <= 64) { // the callers' barrier has published the list and the output count
+        if (tid < 64) rank_take(src, m, nullptr, prefix, pmask, remaining, out, cap, sh.cnt[0]);
+        return;
+    }
     if (!digit_level<T, Src, U, 9, 2048>(src, m, prefix, pmask, remaining, out, cap, sh.hist, sh)) return;
     if (remaining == 0) return;
     if (!digit_level<T, Src, U, 0, 512>(src, m, prefix, pmask, remaining, out, cap, sh.hist2, sh)) return;
