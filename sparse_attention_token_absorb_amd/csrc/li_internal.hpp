@@ -20,6 +20,9 @@ enum {
     kSlotN = kHistBins + 2,    // the query's row count, recorded by the scoring kernel
     kSlotUpI = kHistBins + 3,  // same two counters for the nested (inner) selection
     kSlotTieI = kHistBins + 4,
+    kSlotBins = kHistBins + 5,   // threshold digits found by the filter: outer | inner << 16 (-1: none)
+    kSlotAboveO = kHistBins + 6, // rows in digits above the outer threshold digit
+    kSlotAboveI = kHistBins + 7, // the same for the inner one
 };
 
 // Rows to score for one call.

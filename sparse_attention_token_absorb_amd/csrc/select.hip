@@ -735,6 +735,11 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
     find_bins<T, kHistBins, 2>(h0, rem, sh);
     const int bin = sh.res[0];
     const int bin_i = Ki > 0 ? sh.res[2] : -1;
+    if (blockIdx.x == 0 && tid == 0) { // every workgroup finds the same digits; the final kernel reads them here
+        hq[kSlotBins] = (int32_t)(((uint32_t)sh.res[0] & 0xFFFFu) | ((uint32_t)sh.res[2] << 16));
+        hq[kSlotAboveO] = sh.res[1];
+        hq[kSlotAboveI] = sh.res[3];
+    }
     if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
     const bool inner = Ki > 0;
     const bool sep = inner && bin_i != bin; // inner ties need a list of their own
@@ -811,7 +816,6 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
 __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
 {
     __shared__ Scratch<NT> sh;
-    __shared__ uint32_t h0[kHistBins];
     __shared__ uint32_t ck[kCandCap];
     __shared__ int32_t ci[kCandCap];
     constexpr int E = kCandCap / NT;
@@ -822,9 +826,10 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     const int kout = inner ? c.k_inner : c.k;
     int32_t *out = (inner ? c.idx_inner : c.idx) + (int64_t)q * kout;
     sh.clear_levels();
-    // Loaded up front: the histogram, the counters, and the head of this
-    // part's tie list (the nested part's list is the likely one; the outer
-    // list is read later only when the two threshold digits coincide).
+    // Loaded up front: the threshold digits the filter found, the counters,
+    // and the head of this part's tie list (the nested part's list is the
+    // likely one; the outer list is read later only when the two threshold
+    // digits coincide).
     const int lim = (int)(ws.cap < kCandCap ? ws.cap : kCandCap);
     const uint2 *list = (inner ? ws.cand2 : ws.cand) + (int64_t)q * ws.cap;
     uint2 p[E];
@@ -833,21 +838,18 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
         const int i = e * NT + tid;
         p[e] = i < lim ? list[i] : make_uint2(0u, 0u);
     }
-    HistRegs<NT> hr;
-    hr.load(hq);
     const int n = clamp_n(hq[kSlotN], c.max_n);
     const int tie_o = hq[kSlotTieO];
     const int tie_i = hq[kSlotTieI];
+    const int bins = hq[kSlotBins];
+    const int above_o = hq[kSlotAboveO];
+    const int above_i = hq[kSlotAboveI];
     const int K = min(n, c.k);
     const int Kp = inner ? min(n, c.k_inner) : K;
     if (Kp > 0) {
-        hr.store(h0);
-        __syncthreads();
-        const uint32_t rem[2] = {(uint32_t)K, (uint32_t)Kp};
-        find_bins<NT, kHistBins, 2>(h0, rem, sh);
-        const int bin_o = sh.res[0];
-        const int bin = inner ? sh.res[2] : bin_o;
-        const int above = inner ? sh.res[3] : sh.res[1];
+        const int bin_o = (int)(int16_t)(bins & 0xFFFF);
+        const int bin = inner ? (int)(int16_t)(bins >> 16) : bin_o;
+        const int above = inner ? above_i : above_o;
         if (bin >= 0 && bin_o >= 0) {
             const bool shared_list = inner && bin == bin_o;
             const int nc = inner && !shared_list ? tie_i : tie_o;
@@ -877,8 +879,10 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
             } else if (nc <= ws.cap) {
                 // every tie is in the global list: rank it instead of the row
                 const uint2 *lst = (inner && !shared_list ? ws.cand2 : ws.cand) + (int64_t)q * ws.cap;
+                __syncthreads(); // the level histograms' clear and the output count
                 finish_levels<NT>(CandGlobal{lst, c.row, q}, nc, prefix, pmask, need, out, kout, sh);
             } else {
+                __syncthreads();
                 finish_levels<NT>(RowGlobal{c.row, q}, n, prefix, pmask, need, out, kout, sh);
             }
         }
