@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--no-model", action="store_true")
@@ -101,7 +101,7 @@ def main() -> int:
     # ------------------------------------------------------------------
     N, Bn = args.context, args.batch
     log(f"generating inputs B={Bn} N={N}")
-    g = synth.config4(N=N, B=Bn)
+    g = synth.long_context_b4(N=N, B=Bn)
     H, d, r, k, M, G = g.H, g.d, g.r, g.k, g.M, g.G
 
     def make_cache(latent, width):
@@ -349,14 +349,14 @@ def main() -> int:
         log(f"sweep {sweep}")
 
     # ------------------------------------------------------------------
-    # The two other decode workloads: a single 8K sequence (config 2, full
+    # The two other decode workloads: a single 8K sequence (full
     # LatentIndex on all four layers) and 16 ragged paged sequences of
-    # 16K-32K rows (config 3, full LatentIndex and HS); each layer absorbs
+    # 16K-32K rows (full LatentIndex and HS); each layer absorbs
     # its decoder, scores and selects, as one captured graph per mode
     # ------------------------------------------------------------------
-    configs = {}
-    if not args.no_configs:
-        for cname, gc in (("config2_decode_b1_n8192", synth.config2()), ("config3_ragged_b16_n16k_32k", synth.config3())):
+    workloads = {}
+    if not args.no_workloads:
+        for cname, gc in (("decode_b1_n8192", synth.decode_b1_n8192()), ("ragged_paged_b16_n16k_32k", synth.ragged_paged_b16())):
             log(f"{cname} inputs")
             Bc = gc.B
             pool_c = torch.zeros((gc.num_pages, 64, gc.r), dtype=bf, device=dev)
@@ -408,10 +408,10 @@ def main() -> int:
                 entry["hs_rows_per_s"] = round((sum(n_q) + (gc.G - 1) * sum(min(gc.M, n) for n in n_q)) /
                                                (ms_h * 1e-3), 1)
                 entry["hs_speedup_over_full_group"] = round(ms_f / ms_h, 3)
-            configs[cname] = entry
+            workloads[cname] = entry
             del cache_c, pool_c, ws_c, ws_hc, gc
             torch.cuda.empty_cache()
-        log(f"configs {configs}")
+        log(f"workloads {workloads}")
 
     # ------------------------------------------------------------------
     # Segmented FP8 cache (same latent, rotated and quantized on append):
@@ -579,7 +579,7 @@ def main() -> int:
                                f"+ HS (M={M}) + per-layer baseline indexer x{G}",
                    "batch": Bn, "context": N, "heads": H, "d": d, "r": r, "k": k, "M": M, "group": G,
                    "parallelism": "single GPU"},
-        "modes": modes, "roofline": roofline, "sweep": sweep, "configs": configs, "fp8": fp8, "rope": rope,
+        "modes": modes, "roofline": roofline, "sweep": sweep, "workloads": workloads, "fp8": fp8, "rope": rope,
         "model": model,
         "prefill": prefill, "cpu_baseline": cpu,
     }

@@ -202,31 +202,31 @@ def make_prefill(name: str, seed: int, *, N: int, Qn: int, r: int, H: int, d: in
 # The five workloads.  ``scale`` < 1 shrinks the row counts for quick runs
 # while keeping every other property (shapes of heads, widths, budgets).
 # ----------------------------------------------------------------------------
-def config1(seed: int = 1) -> DecodeGroup:
+def tiny_fp32_n512(seed: int = 1) -> DecodeGroup:
     """Tiny fp32 group: N=512, r=64, H=4, d=32, k=64, M=128, 8 heavy rows."""
     return make_decode("tiny-fp32-N512", seed, B=1, lens=[512], r=64, H=4, d=32, k=64, M=128,
                        dtype="fp32", n_heavy=8, structure=False, w_dist="uniform", paged=False)
 
 
-def config2(seed: int = 2) -> DecodeGroup:
+def decode_b1_n8192(seed: int = 2) -> DecodeGroup:
     """DSA-scale single decode: N=8192, H=64, d=128, r=256, bf16, k=2048."""
     return make_decode("decode-B1-N8192", seed, B=1, lens=[8192], r=256, H=64, d=128, k=2048, M=8192,
                        paged=False)
 
 
-def config3(seed: int = 3, lo: int = 16384, hi: int = 32768, B: int = 16) -> DecodeGroup:
+def ragged_paged_b16(seed: int = 3, lo: int = 16384, hi: int = 32768, B: int = 16) -> DecodeGroup:
     """Ragged paged HS decode: B=16, lens ~ U{16384..32768}, M=8192, k=2048."""
     return make_decode(f"hs-ragged-B{B}-N{lo}-{hi}", seed, B=B, lens=(lo, hi), r=256, H=64, d=128,
                        k=2048, M=8192, paged=True)
 
 
-def config4(seed: int = 4, N: int = 131072, B: int = 4, keys_a: bool = True) -> DecodeGroup:
+def long_context_b4(seed: int = 4, N: int = 131072, B: int = 4, keys_a: bool = True) -> DecodeGroup:
     """Long-context decode: B=4, N=131072, r=256 (plus [N][128] per-layer keys)."""
     return make_decode(f"decode-B{B}-N{N}", seed, B=B, lens=[N] * B, r=256, H=64, d=128, k=2048, M=8192,
                        paged=True, keys_a=keys_a)
 
 
-def config5(seed: int = 5, N: int = 65536, Qn: int = 4096) -> DecodeGroup:
+def chunked_prefill_q4096(seed: int = 5, N: int = 65536, Qn: int = 4096) -> DecodeGroup:
     """Chunked prefill: 4096 queries at positions N-4096..N-1 of a 65536-row cache."""
     return make_prefill(f"prefill-Q{Qn}-N{N}", seed, N=N, Qn=Qn, r=256, H=64, d=128, k=2048)
 

@@ -19,5 +19,5 @@ def test_help_lists_the_workload_switches():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--gpus", "--no-cpu-baseline", "--no-prefill", "--no-configs", "--counters"):
+    for flag in ("--steps", "--warmup", "--gpus", "--no-cpu-baseline", "--no-prefill", "--no-workloads", "--counters"):
         assert flag in r.stdout

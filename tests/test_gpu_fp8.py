@@ -136,7 +136,7 @@ def verify_fp8_full(h, g, l, out, k=None, codes=None, tag="", queries=None):
 def test_fp8_decode_8k_full_layers():
     h = _gpu()
     say("fp8 decode 8K, 4 layers")
-    g = synth.config2()
+    g = synth.decode_b1_n8192()
     cache = fp8_cache(h, g)
     qs = h.Queries(g)
     codes = oracle_codes(g)
@@ -197,7 +197,7 @@ def test_fp8_short_empty_and_r128():
 def test_fp8_prefill_sampled_rows():
     """4096 queries of one 65536-row sequence: the many-query kernel."""
     h = _gpu()
-    g = synth.config5()
+    g = synth.chunked_prefill_q4096()
     say("fp8 prefill Q=4096 N=65536: cache")
     cache = fp8_cache(h, g)
     qs = h.Queries(g)

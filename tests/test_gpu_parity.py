@@ -133,98 +133,98 @@ def test_absorb_parity(dtype, d, r, Q, Hh):
 # ----------------------------------------------------------------------------
 # The five workloads
 # ----------------------------------------------------------------------------
-def test_config1_tiny_fp32_full_and_hs():
+def test_tiny_fp32_n512_full_and_hs():
     h = H()
-    g = synth.config1()
-    say("config1 fp32 N=512: cache")
+    g = synth.tiny_fp32_n512()
+    say("tiny fp32 N=512: cache")
     cache = h.build_cache(g)
     qs = h.Queries(g)
     for l in range(g.G):
-        say(f"config1 full layer {l}")
+        say(f"tiny fp32 full layer {l}")
         res = h.full_layer(g, cache, qs, l)
-        verify_full(g, l, res, tag="config1")
-    say("config1 HS")
+        verify_full(g, l, res, tag="tiny fp32")
+    say("tiny fp32 HS")
     anchor, followers = h.hs_group(g, cache, qs)
-    verify_hs(g, anchor, followers, tag="config1")
+    verify_hs(g, anchor, followers, tag="tiny fp32")
 
 
-def test_config2_decode_8k_bf16():
+def test_decode_b1_n8192_bf16():
     h = H()
-    g = synth.config2()
-    say("config2 bf16 N=8192: cache")
+    g = synth.decode_b1_n8192()
+    say("decode B=1 N=8192 bf16: cache")
     cache = h.build_cache(g)
     qs = h.Queries(g)
     full = []
     for l in range(g.G):
-        say(f"config2 full layer {l}")
+        say(f"decode 8K full layer {l}")
         res = h.full_layer(g, cache, qs, l)
-        verify_full(g, l, res, tag="config2")
+        verify_full(g, l, res, tag="decode 8K")
         full.append(h.host(res.idx))
     # M = n: HS is full LatentIndex (up to exact-tie / tolerance swaps)
-    say("config2 HS with M = N")
+    say("decode 8K HS with M = N")
     anchor, followers = h.hs_group(g, cache, qs, M=8192)
-    verify_hs(g, anchor, followers, M=8192, tag="config2 M=N")
+    verify_hs(g, anchor, followers, M=8192, tag="decode 8K M=N")
 
 
-def test_config3_ragged_paged_hs_and_full():
+def test_ragged_paged_b16_hs_and_full():
     h = H()
-    g = synth.config3()
-    say(f"config3 B={g.B} lens {int(g.lens.min())}..{int(g.lens.max())}: cache")
+    g = synth.ragged_paged_b16()
+    say(f"ragged paged B={g.B} lens {int(g.lens.min())}..{int(g.lens.max())}: cache")
     cache = h.build_cache(g)
     qs = h.Queries(g)
-    say("config3 HS")
+    say("ragged paged HS")
     anchor, followers = h.hs_group(g, cache, qs)
-    verify_hs(g, anchor, followers, tag="config3")
+    verify_hs(g, anchor, followers, tag="ragged paged")
     ov = []
     for l in range(g.G):
-        say(f"config3 full layer {l}")
+        say(f"ragged paged full layer {l}")
         res = h.full_layer(g, cache, qs, l)
-        verify_full(g, l, res, tag="config3")
+        verify_full(g, l, res, tag="ragged paged")
         hs_sel = h.host(anchor.idx_inner) if l == 0 else h.host(followers[l - 1].idx)
         full_sel = h.host(res.idx)
         ov += [overlap(hs_sel[i][hs_sel[i] >= 0], full_sel[i][full_sel[i] >= 0]) for i in range(g.Q)]
-    say(f"config3 HS-vs-full top-k overlap mean {np.mean(ov):.4f} (reported, not pinned)")
+    say(f"ragged paged HS-vs-full top-k overlap mean {np.mean(ov):.4f} (reported, not pinned)")
 
 
-def test_config4_long_context_all_three_ways():
+def test_long_context_b4_n131072_all_three_ways():
     h = H()
-    g = synth.config4()
-    say("config4 B=4 N=131072: cache")
+    g = synth.long_context_b4()
+    say("long context B=4 N=131072: cache")
     cache = h.build_cache(g)
     qs = h.Queries(g)
     for l in range(g.G):
-        say(f"config4 (b) full layer {l}")
-        verify_full(g, l, h.full_layer(g, cache, qs, l), tag="config4b")
-    say("config4 (c) HS M=8192")
+        say(f"long context (b) full layer {l}")
+        verify_full(g, l, h.full_layer(g, cache, qs, l), tag="long context (b)")
+    say("long context (c) HS M=8192")
     anchor, followers = h.hs_group(g, cache, qs)
-    verify_hs(g, anchor, followers, tag="config4c")
+    verify_hs(g, anchor, followers, tag="long context (c)")
     del cache
     torch.cuda.empty_cache()
     from sparse_attention_token_absorb_amd import binding as B
     for l in range(g.G):
-        say(f"config4 (a) per-layer key cache layer {l}")
+        say(f"long context (a) per-layer key cache layer {l}")
         kc = h.build_cache(g, latent=g.keys_a[l], r=g.d)
         q = h.to_dev(g.q[l], torch.bfloat16)
         res = B.score_topk(kc, qs.seq, qs.pos, qs.max_valid, q, h.head_weights(g, l), g.k, keep_scores=True)
         sel, cnt, sc = h.host(res.idx), h.host(res.count), h.host(res.scores)
         for i in range(g.Q):
             s = oracle.score_explicit(g.q[l][i], None, g.w[l][i], g.keys_a[l][i])
-            check_scores(sc[i, :len(s)], s, f"config4a layer {l} q{i}")
-            check_topk(sel[i], int(cnt[i]), oracle.topk(s, g.k), s, None, g.k, rms(s), f"config4a layer {l} q{i}")
+            check_scores(sc[i, :len(s)], s, f"long context (a) layer {l} q{i}")
+            check_topk(sel[i], int(cnt[i]), oracle.topk(s, g.k), s, None, g.k, rms(s), f"long context (a) layer {l} q{i}")
         del kc
 
 
-def test_config5_prefill_sampled_rows():
+def test_chunked_prefill_q4096_sampled_rows():
     h = H()
-    g = synth.config5()
-    say("config5 prefill Q=4096 N=65536: cache")
+    g = synth.chunked_prefill_q4096()
+    say("chunked prefill Q=4096 N=65536: cache")
     cache = h.build_cache(g)
     qs = h.Queries(g)
     sample = sorted(set(np.linspace(0, g.Q - 1, 6).astype(int).tolist()))
     for l in range(g.G):
-        say(f"config5 layer {l}")
+        say(f"chunked prefill layer {l}")
         res = h.full_layer(g, cache, qs, l)
-        verify_full(g, l, res, queries=sample, tag="config5")
+        verify_full(g, l, res, queries=sample, tag="chunked prefill")
         cnt = h.host(res.count)
         exp = np.minimum(g.k, np.minimum(g.qpos + 1, g.lens[0]))
         assert np.array_equal(cnt, exp)

@@ -14,9 +14,9 @@ def test_round_bf16_matches_torch():
     assert np.array_equal(synth.round_bf16(x).view(np.uint32), ref.view(np.uint32))
 
 
-def test_config1_shapes_and_determinism():
-    a = synth.config1()
-    b = synth.config1()
+def test_tiny_fp32_n512_shapes_and_determinism():
+    a = synth.tiny_fp32_n512()
+    b = synth.tiny_fp32_n512()
     assert a.dtype == "fp32" and a.B == 1 and a.Q == 1 and a.G == 4
     assert a.latent[0].shape == (512, 64)
     assert a.q[0].shape == (1, 4, 32) and a.W[0].shape == (32, 64) and a.w[0].shape == (1, 4)
