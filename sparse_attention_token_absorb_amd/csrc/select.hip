@@ -506,7 +506,12 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
             n = query_n(c, q);
         }
         K = min(n, c.k);
-        if (K > 0) {
+        if (K > 0 && K == n) {
+            // the budget covers the whole row: every element is taken
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (e * NT + tid < n) out[e * NT + tid] = id[e];
+        } else if (K > 0) {
             if constexpr (HIST) {
                 hr.store(h0);
             } else {
@@ -579,7 +584,9 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
         K = min(n, c.k);
         const bool cached = MODE == kCached && n <= kKeyCache;
         constexpr int64_t ROUND = (int64_t)NT * KB * 4;
-        if (K > 0) {
+        if (K > 0 && K == n) {
+            for (int i = tid; i < n; i += NT) out[i] = out_id(c.row, q, i); // the budget covers the whole row
+        } else if (K > 0) {
             if constexpr (HIST) {
                 HistRegs<NT> hr;
                 hr.load(hq);
