@@ -103,6 +103,7 @@ def _check_full(out, n_q, k, what, k_inner=0):
     ([8192], 30, 2048),               # ~270 copies per value: equal run across all digits
     ([8192, 5000], 200, 2048),        # ~40 copies per value: threshold digit of <= 64 equal keys
     ([8192, 8191, 4097], 8192, 2048),  # mostly distinct: a few elements left after the first digit
+    ([40, 64, 65, 8192], 50, 8192),   # the budget covers every row: all taken without a radix pass
 ])
 def test_short_rows_exact(lens, distinct, k):
     cache, seq, pos, mv, qt, w, n_q = _setup(11 + distinct, lens, distinct)
@@ -138,6 +139,7 @@ def test_many_queries_stream_exact():
     ([5000, 3000], 100, 2048, 512),    # short anchor rows: nested selection over the outer winners
     ([20000, 30000], 100, 8192, 2048),  # long anchor rows: nested selection in the filter
     ([20000, 900], 9, 8192, 2048),     # a sequence shorter than M, massive ties
+    ([5000, 3000, 8192], 40, 8192, 2048),  # M covers every row: the anchor keeps all, its top-k nested
 ])
 def test_hs_exact(lens, distinct, M, k):
     cache, seq, pos, mv, qt, w, n_q = _setup(41 + M, lens, distinct)
