@@ -260,6 +260,11 @@ void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const do
                    const float *cs, const int32_t *rows, int64_t m, int64_t H, int64_t r, double *s)
 {
     const int64_t nseg = r / 128;
+    /* the value of every code, as lio_e4m3_decode gives it, looked up instead
+     * of recomputed per product (the same values in the same order) */
+    double dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = lio_e4m3_decode((uint8_t)c);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i) {
         const int64_t row = rows ? (int64_t)rows[i] : i;
@@ -269,7 +274,7 @@ void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const do
             for (int64_t g = 0; g < nseg; ++g) {
                 double seg = 0.0;
                 for (int t = 0; t < 128; ++t)
-                    seg += lio_e4m3_decode(qc[h * r + g * 128 + t]) * lio_e4m3_decode(cc[row * r + g * 128 + t]);
+                    seg += dec[qc[h * r + g * 128 + t]] * dec[cc[row * r + g * 128 + t]];
                 dot += (double)qs[h * nseg + g] * (double)cs[row * nseg + g] * seg;
             }
             if (bias) dot += bias[h];

@@ -81,6 +81,22 @@ def pin_worked_causal():
         assert sorted(res[0].sel.tolist()) == sorted(case["selected"]), (case, res[0].sel)
 
 
+def pin_worked_baseline_layer():
+    """The per-layer indexer on its own cached keys (no decoder): with the
+    keys rebuilt by hand from the worked latent it gives the latent path's
+    scores and selection, causal prefix included."""
+    g = _golden("worked_score_topk.json")
+    q = np.array(g["q"], float)[None]
+    w = np.array(g["w"], float)[None]
+    K = np.array(g["keys"], float)
+    res = oracle.baseline_layer(q, w, [K], np.array([0]), np.array([4]), np.array([5]), 3)
+    assert np.array_equal(res[0].scores, np.array(g["scores"], float)), res[0].scores
+    assert list(res[0].sel) == g["topk_order"][:3], res[0].sel
+    for case in g["causal"]:
+        res = oracle.baseline_layer(q, w, [K], np.array([0]), np.array([case["pos"]]), np.array([5]), case["k"])
+        assert len(res[0].scores) == case["n_valid"] and sorted(res[0].sel) == case["selected"], (case, res[0].sel)
+
+
 def pin_worked_hs():
     g = _golden("worked_hs.json")
     C = np.array(g["latent"], float)
@@ -433,6 +449,35 @@ def pin_quantize_worked_examples():
     two[0, 0], two[0, 128] = 1.0, 4.0
     c2, s2 = oracle.quantize_rows(two)
     assert s2[0, 0] == 2.0 ** -12 and s2[0, 1] == 2.0 ** -10 and np.all(c2 == 123)
+
+
+def worked_absorb_fp8_operands(r=128):
+    """q [1][1][32] and W [32][r] of the worked FP8 absorption case."""
+    g = _golden("worked_fp8.json")["absorb_case"]
+    q = np.zeros((1, 1, 32), np.float32)
+    q[0, 0, :len(g["q_terms"])] = g["q_terms"]
+    W = np.zeros((32, r), np.float32)
+    W[:len(g["w_column0"]), 0] = g["w_column0"]
+    return q, W
+
+
+def pin_worked_absorb_fp8():
+    """The absorbed query is the exact product rounded once to fp32 before the
+    rotation: here that one rounding decides every code of the segment."""
+    g = _golden("worked_fp8.json")["absorb_case"]
+    for r in (128, 256):
+        q, W = worked_absorb_fp8_operands(r)
+        codes, scales = oracle.absorb_fp8(q, W)
+        assert codes.shape == (1, 1, r) and scales.shape == (1, 1, r // 128)
+        assert scales[0, 0, 0] == g["scale"] == 2.0 ** g["exponent"], scales
+        assert np.all(codes[0, 0, :128] == g["code"]), codes[0, 0, :8]
+        if r == 256:  # an all-zero segment: exponent 0, zero codes
+            assert scales[0, 0, 1] == 1.0 and not codes[0, 0, 128:].any()
+    # the next float32 below x (any rounding of x other than to nearest)
+    row = np.zeros((1, 128), np.float32)
+    row[0, 0] = np.float32(8526734 * 2.0 ** -23)
+    c, s = oracle.quantize_rows(row)
+    assert s[0, 0] == g["scale"] and np.all(c == g["code_if_x_rounded_down"]), c[0, :4]
 
 
 def pin_quantization_error_bound():

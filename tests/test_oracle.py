@@ -119,10 +119,38 @@ def _mut_hs_follower_uncapped(q, W, w, latents, qseq, qpos, lens, k, M):
 
 _orig_hs = oracle.hs_group
 
+
+def _mut_absorb_fp8_fp32_accumulation(q, W):
+    """Sums the products in float32, in order, instead of rounding the exact sum once."""
+    q = np.asarray(q, np.float32)
+    W = np.asarray(W, np.float32)
+    acc = np.zeros(q.shape[:-1] + (W.shape[1],), np.float32)
+    for e in range(W.shape[0]):
+        acc = (acc + q[..., e:e + 1] * W[e]).astype(np.float32)
+    return oracle.quantize_rows(acc)
+
+
+def _mut_absorb_fp8_truncates(q, W):
+    """Rounds the exact sum toward zero instead of to nearest."""
+    x = oracle.absorb(q, W)
+    f = x.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(x)
+    f[over] = np.nextafter(f[over], np.float32(0))
+    return oracle.quantize_rows(f)
+
+
+def _mut_absorb_fp8_bf16(q, W):
+    """Rounds the absorbed query to bfloat16 (the plain path's precision) before quantizing."""
+    from sparse_attention_token_absorb_amd import synth
+    return oracle.quantize_rows(synth.round_bf16(oracle.absorb(q, W).astype(np.float32)))
+
 PY_MUTANTS = {
     "valid_rows_exclusive": ("valid_rows", _mut_valid_rows_exclusive),
     "hs_follower_scores_full_prefix": ("hs_group", _mut_hs_follower_full_prefix),
     "hs_follower_budget_uncapped": ("hs_group", _mut_hs_follower_uncapped),
+    "absorb_fp8_fp32_accumulation": ("absorb_fp8", _mut_absorb_fp8_fp32_accumulation),
+    "absorb_fp8_truncates": ("absorb_fp8", _mut_absorb_fp8_truncates),
+    "absorb_fp8_bf16": ("absorb_fp8", _mut_absorb_fp8_bf16),
 }
 
 
