@@ -56,8 +56,9 @@ class DecodeGroup:
     latent[b] holds the logical rows 0..lens[b]-1 of sequence b (float32
     values, bf16-exact when dtype == "bf16").  Query i belongs to sequence
     qseq[i] at position qpos[i]; layer l has q[l] [Q][H][d], W[l] [d][r] and
-    w[l] [Q][H].  keys_a[l][b] (optional) is an independent per-layer key
-    cache [lens[b]][d] for the per-layer (DSA-style) baseline indexer.
+    w[l] [Q][H].  keys_a[l][b] (optional) is the per-layer key cache
+    [lens[b]][d] of the per-layer (DSA-style) baseline indexer: layer l's
+    decoder applied to the latent rows, rounded once to the dtype.
     """
     name: str
     dtype: str
@@ -159,13 +160,15 @@ def make_decode(name: str, seed: int, *, B: int, lens, r: int, H: int, d: int, G
             wl = rng.random((B, H), dtype=np.float32)
         ws.append(np.ascontiguousarray(wl, dtype=np.float32))
         if keys_a:
-            # Per-layer key caches of the DSA-style baseline: independent draws
-            # with the latent's recipe, at key width d.
-            kl = []
-            for b in range(B):
-                kz = rng.standard_normal((int(lens[b]), d), dtype=np.float32)
-                kl.append(_cast(kz, dtype))
-            ka.append(kl)
+            # Per-layer key caches of the DSA-style baseline: the keys the layer
+            # would cache natively for the same tokens, its decoder applied to
+            # the latent rows (K_j = W_dec c_j, computed in float64 and rounded
+            # once to the cache dtype), so the baseline and the latent path
+            # score the same effective keys up to that one rounding.  These
+            # keys are an input of the baseline (what it has cached), not a
+            # step of either path; no random number is drawn for them.
+            W64 = Ws[-1].astype(np.float64)
+            ka.append([_cast(latent[b].astype(np.float64) @ W64.T, dtype) for b in range(B)])
     rng_perm = np.random.Generator(np.random.PCG64(s_perm)) if paged else None
     bt, npages = _paging(lens, rng_perm)
     return DecodeGroup(name=name, dtype=dtype, H=H, d=d, r=r, G=G, k=k, M=M, lens=lens.astype(np.int32),

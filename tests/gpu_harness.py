@@ -83,5 +83,10 @@ def hs_group(g, cache, qs: Queries, M: int | None = None, k: int | None = None, 
     return anchor, followers
 
 
+def prefill_sample(Q: int, n: int = 64) -> list:
+    """n evenly spaced query rows of a chunk, the first and the last included."""
+    return sorted(set(np.linspace(0, Q - 1, n).round().astype(int).tolist()))
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()

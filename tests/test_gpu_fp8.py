@@ -202,8 +202,9 @@ def test_fp8_prefill_sampled_rows():
     cache = fp8_cache(h, g)
     qs = h.Queries(g)
     codes = oracle_codes(g)
-    sample = sorted(set(np.linspace(0, g.Q - 1, 5).astype(int).tolist()))
-    for l in (0, 1):
+    sample = h.prefill_sample(g.Q)
+    assert len(sample) == 64 and sample[0] == 0 and sample[-1] == g.Q - 1
+    for l in range(g.G):
         say(f"fp8 prefill layer {l}")
         _, out = fp8_layer(h, g, cache, qs, l)
         verify_fp8_full(h, g, l, out, codes=codes, tag="fp8-prefill", queries=sample)

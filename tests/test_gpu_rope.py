@@ -226,18 +226,30 @@ def test_rope_decode_full_and_hs(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_rope_prefill_sampled(dtype):
+    """The chunked-prefill workload (4096 queries at the end of a 65536-row
+    cache, 4 layers) through the structured decoder: 64 evenly spaced query
+    rows of every layer against the oracle; on the bf16 path the first and
+    last sampled rows of layer 0 also against rebuilt post-RoPE keys."""
     h = _gpu()
     rg = synth.make_rope(74)
-    g = synth.make_prefill(f"rope-pf-{dtype}", 74, N=16384, Qn=512, r=256, H=64, d=128, G=1, k=2048)
+    g = synth.make_prefill(f"rope-pf-{dtype}", 74, N=65536, Qn=4096, r=256, H=64, d=128, G=4, k=2048)
     say(f"prefill {dtype}: cache")
     cache = rope_cache(h, g, rg, dtype)
     qs = h.Queries(g)
     stored = _stored(g, rg, dtype)
-    qt, bias = layer_operands(h, g, rg, 0, fp8=(dtype == "fp8"))
-    out = B.score_topk(cache, qs.seq, qs.pos, qs.max_valid, qt, h.head_weights(g, 0), g.k, keep_scores=True,
-                       bias=bias)
-    sample = sorted(set(np.linspace(0, g.Q - 1, 5).astype(int).tolist()))
-    _verify(h, g, rg, 0, out, stored, dtype, queries=sample, explicit=(dtype == "bf16"), tag=f"rope-pf-{dtype}")
+    sample = h.prefill_sample(g.Q)
+    assert len(sample) == 64 and sample[0] == 0 and sample[-1] == g.Q - 1
+    for l in range(g.G):
+        say(f"prefill {dtype}: layer {l}")
+        qt, bias = layer_operands(h, g, rg, l, fp8=(dtype == "fp8"))
+        out = B.score_topk(cache, qs.seq, qs.pos, qs.max_valid, qt, h.head_weights(g, l), g.k, keep_scores=True,
+                           bias=bias)
+        _verify(h, g, rg, l, out, stored, dtype, queries=sample, tag=f"rope-pf-{dtype}")
+        if dtype == "bf16" and l == 0:
+            _verify(h, g, rg, l, out, stored, dtype, queries=[sample[0], sample[-1]], explicit=True,
+                    tag=f"rope-pf-{dtype}")
+        del out
+        torch.cuda.empty_cache()
 
 
 def test_bias_on_the_register_staged_and_fp32_paths():

@@ -47,3 +47,16 @@ def test_heavy_rows_planted():
     assert len(h) == 20
     norms = np.linalg.norm(g.latent[0], axis=1)
     assert norms[h].mean() > 2.0 * np.delete(norms, h).mean()
+
+
+def test_baseline_keys_are_the_decoded_latent():
+    """The per-layer baseline caches each layer's decoder applied to the same
+    latent rows, rounded once to bf16."""
+    g = synth.make_decode("t", 8, B=2, lens=[70, 33], r=64, H=4, d=32, k=16, M=32, keys_a=True)
+    for l in range(g.G):
+        for b in range(g.B):
+            k = g.keys_a[l][b]
+            assert k.shape == (int(g.lens[b]), g.d)
+            assert np.array_equal(synth.round_bf16(k), k)
+            exact = g.latent[b].astype(np.float64) @ g.W[l].astype(np.float64).T
+            assert np.all(np.abs(k - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30)
