@@ -595,16 +595,15 @@ def model_step(B, dev, i32, capture, time_graph, reps):
     """Indexer work of one decode step (batch 1) over a 61-layer map shaped
     like the pages' DeepSeek-V3.2 setting (§C.3, §C.4, §B.3): layer 0 keeps
     its own indexer, layers 1-60 form 15 groups of G = 4 (and, as the pages'
-    G = 8 variant of §4.4 and §A.5, 7 groups of 8 plus one of 4).  Every cache is
-    segmented FP8 as in the pages' inference (§B.2, §C.1): native per-layer
+    G = 8 variant of §4.4 and §A.5, 7 groups of 8 plus one of 4).  Every cache
+    is segmented FP8 as in the pages' inference (§B.2, §C.1): native per-layer
     keys 128 wide (128 code bytes + one scale: the 132 B per token and layer
-    of §B.1), group latents 256 wide.  Each layer's work is what its indexer
-    does per step: append its new key (or the anchor its latent row), turn its
-    query into the FP8 operand (absorbing the decoder for LatentIndex), score
-    and select.  Methods:
+    of §B.1), group latents 256 wide.  The step is the package's
+    IndexerModel.step (append, query absorption or quantization, scoring and
+    selection for every layer) under each method:
       dsa         every layer scores its own keys over the whole prefix
-      latentindex layer 0 as dsa; each group caches one latent, all 4 layers
-                  score it with their absorbed queries and select top-2048
+      latentindex layer 0 as dsa; each group caches one latent, every layer
+                  scores it with its absorbed query and selects top-2048
       hs          as latentindex, but the anchor proposes its top-8192 and the
                   group's followers rescore only those (§3.2, §C.4)
       indexcache  layer 0 and every group's anchor as dsa; followers reuse
@@ -612,10 +611,11 @@ def model_step(B, dev, i32, capture, time_graph, reps):
     Inputs are seeded device-side normals; only timing is reported."""
     import numpy as np
     import torch
+    from sparse_attention_token_absorb_amd.model import IndexerModel, LayerMap
     L_max, H, d, r, k, M = 131072, 64, 128, 256, 2048, 8192
-    maps = {"G4": [4] * 15, "G8": [8] * 7 + [4]}
-    n_layers = 1 + 60
-    n_groups = max(len(m) for m in maps.values())
+    maps = {"G4": LayerMap.grouped(61, 4), "G8": LayerMap.grouped(61, 8)}
+    n_layers = 61
+    n_groups = max(len(m.groups) for m in maps.values())
     bf = torch.bfloat16
     gen = torch.Generator(device=dev)
     gen.manual_seed(61)
@@ -632,58 +632,31 @@ def model_step(B, dev, i32, capture, time_graph, reps):
         B.append_latent(c, rows, i32(np.zeros(L_max)), i32(np.arange(L_max)))
         return c
 
-    keys = [fp8_cache(d) for _ in range(n_layers)]
+    keys = {l: fp8_cache(d) for l in range(n_layers)}
     lat = [fp8_cache(r) for _ in range(n_groups)]
     q = [torch.randn((1, H, d), generator=gen, device=dev).to(bf) for _ in range(n_layers)]
     W = [(torch.randn((d, r), generator=gen, device=dev) / 16.0).to(bf) for _ in range(n_layers)]
     w = [torch.nn.functional.softplus(torch.randn((1, H), generator=gen, device=dev)) for _ in range(n_layers)]
     new_key = torch.randn((1, d), generator=gen, device=dev).to(bf)
     new_lat = torch.randn((1, r), generator=gen, device=dev).to(bf)
-    qk = [B.Fp8Query.empty(1, H, d, dev) for _ in range(n_layers)]
-    ql = [B.Fp8Query.empty(1, H, r, dev) for _ in range(n_layers)]
-    ws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, 1, L_max, H, r, M, 0), dtype=torch.uint8, device=dev)
-    ws_hs = torch.empty(B.workspace_bytes(B.LI_OP_HS_SELECT, 1, 0, H, r, k, M), dtype=torch.uint8, device=dev)
-    out = B.TopK(torch.empty((1, k), dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
-    outM = B.TopK(torch.empty((1, M), dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
-                  torch.empty((1, k), dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    models = {name: IndexerModel(lm, keys, lat[:len(lm.groups)], q, W, w, k, M, L_max, fp8=True)
+              for name, lm in maps.items()}
     torch.cuda.synchronize()
 
-    def dsa_layer(l, Lc, pos):
-        B.append_latent(keys[l], new_key, seq0, pos)
-        B.absorb_query(q[l], None, out=qk[l], fp8=True)  # a native query: quantized, no decoder
-        B.score_topk(keys[l], seq0, pos, Lc, qk[l], w[l], k, ws=ws, out=out)
-
-    def run(method, Lc, pos, groups):
-        dsa_layer(0, Lc, pos)
-        l0 = 1
-        for gi, G in enumerate(groups):
-            if method == "dsa":
-                for l in range(l0, l0 + G):
-                    dsa_layer(l, Lc, pos)
-            elif method == "indexcache":
-                dsa_layer(l0, Lc, pos)
-            else:
-                B.append_latent(lat[gi], new_lat, seq0, pos)
-                for j, l in enumerate(range(l0, l0 + G)):
-                    B.absorb_query(q[l], W[l], out=ql[l], fp8=True)
-                    if method == "latentindex":
-                        B.score_topk(lat[gi], seq0, pos, Lc, ql[l], w[l], k, ws=ws, out=out)
-                    elif j == 0:
-                        B.score_topk(lat[gi], seq0, pos, Lc, ql[l], w[l], M, k_inner=k, ws=ws, out=outM)
-                    else:
-                        B.hs_select(lat[gi], seq0, pos, Lc, outM.idx, outM.count, ql[l], w[l], k, ws=ws_hs, out=out)
-            l0 += G
+    def run(model, method, Lc, pos):
+        model.step(method, seq0, pos, Lc, new_keys={l: new_key for l in range(n_layers)},
+                   new_latents={gi: new_lat for gi in range(len(model.lmap.groups))}, new_seq=seq0, new_pos=pos)
 
     res, res8 = {}, {}
     for Lc in (8192, 32768, 131072):
         pos = i32([Lc - 1])
         ms, ms8 = {}, {}
         for method in ("dsa", "latentindex", "hs", "indexcache"):
-            gr = capture(lambda: run(method, Lc, pos, maps["G4"]))
+            gr = capture(lambda: run(models["G4"], method, Lc, pos))
             ms[method] = time_graph(gr, reps)
             del gr
             if method != "dsa":  # the same work under either map
-                gr = capture(lambda: run(method, Lc, pos, maps["G8"]))
+                gr = capture(lambda: run(models["G8"], method, Lc, pos))
                 ms8[method] = time_graph(gr, reps)
                 del gr
         res[str(Lc)] = {f"{m}_ms": round(v, 4) for m, v in ms.items()}
@@ -691,7 +664,7 @@ def model_step(B, dev, i32, capture, time_graph, reps):
         for m in ("latentindex", "hs", "indexcache"):
             res[str(Lc)][f"{m}_speedup_vs_dsa"] = round(ms["dsa"] / ms[m], 3)
             res8[str(Lc)][f"{m}_speedup_vs_dsa"] = round(ms["dsa"] / ms8[m], 3)
-    del keys, lat
+    del keys, lat, models
     torch.cuda.empty_cache()
     return {"layer_map": f"{n_layers} layers: layer 0 independent + 15 groups of 4 (FP8 caches; native "
                          f"keys {d} wide, latents {r} wide; H={H}, k={k}, M={M}, batch 1)",
