@@ -3,6 +3,7 @@
 // then enqueues work on the caller's stream; nothing here allocates, frees
 // or synchronizes.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -99,6 +100,26 @@ li_status rope_args(const li_rope *rope, int32_t r, li::RopeArgs *out)
     return LI_OK;
 }
 
+// Whether a decode scoring launch reads its latent rows with the
+// non-temporal policy.  A group's layers score the same latent one after the
+// other, so while the rows fit the 256 MB last-level cache (Infinity Cache)
+// with room to spare, letting them stay there serves the next layer; a launch
+// that streams more than kStreamNtBytes would only churn that cache.
+// LI_STREAM_NT=0|1 overrides (read once).
+constexpr int64_t kStreamNtBytes = 160ll << 20;
+
+bool stream_nt(int64_t bytes)
+{
+    static const int over = [] {
+        const char *e = getenv("LI_STREAM_NT");
+        if (e && strcmp(e, "0") == 0) return 0;
+        if (e && strcmp(e, "1") == 0) return 1;
+        return -1;
+    }();
+    if (over >= 0) return over == 1;
+    return bytes > kStreamNtBytes;
+}
+
 li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt, const float *w, int32_t H)
 {
     li::ScoreArgs a{};
@@ -106,6 +127,7 @@ li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt
     a.bt = c->block_table;
     a.max_pages = c->max_pages;
     a.num_pages = c->num_pages;
+    a.batch = c->batch;
     a.seq_lens = c->seq_lens;
     a.qseq = qs->seq;
     a.qpos = qs->pos;
@@ -331,6 +353,8 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
         a.out_ld = sld;
         a.max_rows = queries->max_valid;
         a.hist = fused_hist ? sw.hist : nullptr;
+        const int64_t row_bytes = fp8 ? cache->r + cache->r / 128 * 4 : (int64_t)cache->r * (cache->dtype == LI_BF16 ? 2 : 4);
+        a.stream_nt = !many && stream_nt((int64_t)Q * queries->max_valid * row_bytes);
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
         if (fp8)
             e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, many,

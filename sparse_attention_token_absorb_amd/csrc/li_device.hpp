@@ -48,6 +48,34 @@ __device__ __forceinline__ void dma16(const void *g, lds_u8 *lds_uniform)
                  : "memory");
 }
 
+// dma16 with the non-temporal policy: the bytes are streamed through without
+// being kept in L2 or the Infinity Cache, so a long one-pass read does not
+// evict the lines that other data (the scores being written, the query)
+// still needs.
+__device__ __forceinline__ void dma16_nt(const void *g, lds_u8 *lds_uniform)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[addr], off nt\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [addr] "v"(g), [lds] "s"(lds)
+                 : "memory");
+}
+
+template <bool NT>
+__device__ __forceinline__ void dma16p(const void *g, lds_u8 *lds_uniform)
+{
+    if constexpr (NT)
+        dma16_nt(g, lds_uniform);
+    else
+        dma16(g, lds_uniform);
+}
+
 // Workgroup barrier without the global-memory fences of __syncthreads():
 // outstanding DMA loads stay in flight across it.  This wave's LDS reads are
 // complete before it arrives.
@@ -78,6 +106,30 @@ __device__ __forceinline__ void wait_after(int after)
     case 5: wait_vmcnt<(MAXA >= 5 ? 5 : 1) * PER>(); break;
     case 6: wait_vmcnt<(MAXA >= 6 ? 6 : 1) * PER>(); break;
     default: wait_vmcnt<(MAXA >= 7 ? 7 : 1) * PER>(); break;
+    }
+}
+
+// Wait until at most n (wave-uniform, 0 <= n <= 15) vector-memory
+// operations of this wave are in flight.
+__device__ __forceinline__ void wait_vmcnt_upto(int n)
+{
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
     }
 }
 

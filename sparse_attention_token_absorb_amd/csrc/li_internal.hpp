@@ -35,6 +35,7 @@ struct ScoreArgs {
     const int32_t *bt;
     int32_t max_pages;
     int32_t num_pages; // pages in the pool (page ids read ahead of the row count are clamped to it)
+    int32_t batch;     // sequences in the block table
     const int32_t *seq_lens;
     const int32_t *qseq;
     const int32_t *qpos;
@@ -51,6 +52,7 @@ struct ScoreArgs {
     int64_t max_rows; // bound on every query's row count (rows past it are not scored)
     int32_t *hist;    // optional [Q][kHistStride]: first-digit counts of the keys written
                       // (accumulated) and the query's row count in slot kSlotN
+    bool stream_nt;   // latent rows are read with the non-temporal policy (not kept in the caches)
 };
 
 // Scoring.  `max_rows` bounds every query's row count (grid sizing).

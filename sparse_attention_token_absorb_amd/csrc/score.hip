@@ -30,6 +30,7 @@ namespace li {
 namespace {
 
 constexpr int kGatherTiles = 16; // max tiles per wave in gather mode (row offsets kept in LDS)
+constexpr int kMaxTilesPerWave = 64; // max tiles per wave of the contiguous LDS-ring decode kernel
 constexpr int kVrMaxTiles = 32;  // max tiles per wave of the register-staged decode kernel
 constexpr int kPrefillMaxTiles = 2048; // max tiles per prefill split (their page ids sit in LDS)
 
@@ -155,7 +156,7 @@ __device__ __forceinline__ void mfma_tile_prefetch(const lds_u8 *buf, const Quer
 // Copy `NIC` KiB of a 32-row tile (CH pieces of 16 B per row, starting at
 // column `col0`) into LDS: instruction ii moves 64/CH rows.  rowoff(nr)
 // gives the pool element offset of tile row nr.
-template <int R, int CH, int NIC, class RowOff>
+template <int R, int CH, int NIC, bool NT = false, class RowOff>
 __device__ __forceinline__ void issue_rows(const u16 *pool, const RowOff &rowoff, int col0, lds_u8 *buf, int ii0,
                                            int nii)
 {
@@ -167,7 +168,7 @@ __device__ __forceinline__ void issue_rows(const u16 *pool, const RowOff &rowoff
             const int p = ii * 64 + lane;
             const int nr = p / CH, cs = p % CH;
             const int c = cs ^ (nr % CH);
-            dma16(pool + rowoff(nr) + col0 + c * 8, buf + ii * 1024);
+            dma16p<NT>(pool + rowoff(nr) + col0 + c * 8, buf + ii * 1024);
         }
     }
 }
@@ -213,12 +214,20 @@ __device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const
 
 // ---------------------------------------------------------------------------
 // Decode: few queries, long rows.  Workgroup = 4 waves of one query; wave w
-// streams tiles row0 + (w + 4 i) * 32.  Each tile moves as CPT chunks of
-// 32 rows x r/CPT columns (two half-width chunks at r = 256, where a whole
-// tile is 16 KiB; whole tiles at r <= 128) through a per-wave ring of NB
-// chunk buffers, so NB-1 chunks stay in flight while the wave computes.
+// streams tiles row0 + (w + 4 i) * 32, so the workgroup covers a contiguous
+// range of rows.  Each tile moves as CPT chunks of 32 rows x r/CPT columns
+// (two half-width chunks at r = 256, where a whole tile is 16 KiB; whole
+// tiles at r <= 128) through a per-wave ring of NB chunk buffers, so NB-1
+// chunks stay in flight while the wave computes.
+//
+// Scores stay in LDS until the stream is done and leave in one coalesced
+// burst per workgroup: score stores spread through the stream interleave
+// writes with the HBM read stream, which measured 7% slower on a 1 GiB pool.
+// NT: the latent rows are read with the non-temporal policy, for launches
+// that stream more than the last-level cache can keep (a pool read once
+// per launch gains nothing from allocating in it, and evicts everything else).
 // ---------------------------------------------------------------------------
-template <int R, int HB, bool GATHER, int NB, int CPT>
+template <int R, int HB, bool GATHER, int NB, int CPT, bool NT>
 __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per_wave)
 {
     static_assert(CPT == 1 || CPT == 2, "chunks per tile");
@@ -227,9 +236,12 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     constexpr int NIC = CHUNK / 1024;           // DMA instructions per chunk
     constexpr int CH = WC / 8;                  // 16-byte pieces per chunk row
     constexpr int KSH = WC / 16;                // MFMA k-steps per chunk
+    constexpr int MAXT = GATHER ? kGatherTiles : kMaxTilesPerWave; // tiles per wave (scores kept in LDS)
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * CHUNK];
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTiles * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
+    __shared__ float s_out[4 * MAXT * kTile];
+    __shared__ int32_t s_pg[GATHER ? 1 : 4 * 64];
     __shared__ float s_w[64];
     __shared__ float s_b[64];
 
@@ -245,25 +257,43 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         first < a.max_rows ? (int)min64(tiles_per_wave, (a.max_rows - first + 4 * kTile - 1) / (4 * kTile)) : 0;
 
     // Start-up is a chain of dependent loads (sequence id, then page ids and
-    // the row count).  The query's rows, weights and biases do not depend on
-    // it and go first (into LDS, read back once all have landed); the first
-    // chunks are issued as soon as the page ids arrive, before the row count:
-    // a page id that is not in use is clamped into the pool, and what such a
-    // chunk brings in is never scored.
+    // the row count).  In contiguous mode lane i of a wave holds the page id
+    // of the wave's tile i (the launcher keeps tiles_per_wave <= 64), so the
+    // stream reads page ids from a register.  A decode batch usually has
+    // query q in sequence q: that block-table row is requested first, by LDS
+    // DMA, before the sequence id is known and ahead of the query staging,
+    // and used if the guess was right.  The query's rows, weights and biases
+    // go next (into LDS, read back once all have landed).  The first chunks
+    // are issued as soon as the page ids are in, before the query and the
+    // row count: a page id that is not in use is clamped into the pool, and
+    // what such a chunk brings in is never scored.
+    const int b_guess = q < a.batch ? q : 0;
+    if constexpr (!GATHER) {
+        const int pidx = (int)min64(tile_row0(lane < nt_max ? lane : 0) >> 6, a.max_pages - 1);
+        dma4(a.bt + (int64_t)b_guess * a.max_pages + pidx, (lds_u8 *)(s_pg + wv * 64));
+    }
     lds_u8 *const ring_all = (lds_u8 *)ring_raw;
-    stage_query<R, HB, NB, CHUNK>((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H,
-                                  a.bias ? a.bias + (int64_t)q * a.H : nullptr, a.H, ring_all, (lds_f32 *)s_w,
-                                  (lds_f32 *)s_b);
-    // Scalar loads (constant address space): waited on with lgkmcnt, so
-    // waiting for them never waits for the chunk loads below.
+    const int staged = stage_query<R, HB, NB, CHUNK>((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H,
+                                                     a.bias ? a.bias + (int64_t)q * a.H : nullptr, a.H, ring_all,
+                                                     (lds_f32 *)s_w, (lds_f32 *)s_b);
+    auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
+    // Scalar loads (constant address space): waited on with lgkmcnt.
     const int b = ((const_i32_t *)a.qseq)[q];
     int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
                    : valid_rows(((const_i32_t *)a.qpos)[q], ((const_i32_t *)a.seq_lens)[b]);
     n = (int)min64(n, a.max_rows);
     const u16 *pool = (const u16 *)a.pool;
-    const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
     lds_u8 *const ring = (lds_u8 *)ring_raw + wv * NB * CHUNK;
-    auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
+    int tile_page = 0;
+    if constexpr (!GATHER) {
+        wait_vmcnt_upto(staged); // the page ids have landed (vector loads complete in issue order)
+        if (b == b_guess) {
+            tile_page = ((const __attribute__((address_space(3))) int32_t *)s_pg)[wv * 64 + lane];
+        } else if (lane < nt_max) {
+            tile_page = a.bt[(int64_t)b * a.max_pages + (tile_row0(lane) >> 6)];
+        }
+        tile_page = clamp_page(tile_page);
+    }
 
     if constexpr (GATHER) {
         // Physical rows of every tile of this wave, resolved once up front
@@ -300,11 +330,14 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         if constexpr (GATHER) {
             const __attribute__((address_space(3))) int32_t *rows =
                 (const __attribute__((address_space(3))) int32_t *)s_row + (wv * kGatherTiles + i) * kTile;
-            issue_rows<R, CH, NIC>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c % CPT) * WC, buf, 0, NIC);
+            issue_rows<R, CH, NIC, NT>(pool, [&](int nr) { return (int64_t)rows[nr] * R; }, (c % CPT) * WC, buf, 0,
+                                       NIC);
         } else {
             const int64_t t0 = tile_row0(i);
-            const int64_t base = ((int64_t)clamp_page(bt[t0 >> 6]) * kPage + (t0 & 63)) * R;
-            issue_rows<R, CH, NIC>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c % CPT) * WC, buf, 0, NIC);
+            const int page = __builtin_amdgcn_readlane(tile_page, i);
+            const int64_t base = ((int64_t)page * kPage + (t0 & 63)) * R;
+            issue_rows<R, CH, NIC, NT>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c % CPT) * WC, buf, 0,
+                                       NIC);
         }
     };
     const int npro = min(NB - 1, CPT * nt_max);
@@ -328,7 +361,8 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     wait_lds();
     wg_barrier(); // no wave overwrites a staging slot before every wave has read it
 
-    float *out = a.out + (int64_t)q * a.out_ld;
+    __attribute__((address_space(3))) float *const outw =
+        (__attribute__((address_space(3))) float *)s_out + wv * kTile;
     f32x16 acc[HB];
     for (int c = 0; c < nchunks; ++c) {
         if (c + NB - 1 < nchunks) {
@@ -346,17 +380,27 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         }
         if (c % CPT == CPT - 1) {
             const float p = epilogue<HB>(acc, qr.w);
-            const int64_t j = tile_row0(c / CPT) + lane;
-            if (lane < 32 && j < n) {
-                out[j] = p;
-                if (a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
-            }
+            const int i = c / CPT;
+            if (lane < 32 && tile_row0(i) + lane < n)
+                outw[i * 4 * kTile + lane] = p; // workgroup-local row (i * 4 + wv) * 32 + lane
         }
     }
     wait_vmcnt<0>(); // chunks issued ahead of the row count and never used
+    __syncthreads(); // every wave's scores are in LDS
+    // The scores leave in one pass over the workgroup's rows, which also
+    // counts their first radix digit (kept out of the stream above).
+    float *out = a.out + (int64_t)q * a.out_ld;
+    const int rows = (int)min64(4 * (int64_t)tiles_per_wave * kTile, n - row0);
     if (a.hist) {
+        for (int j = threadIdx.x; j < rows; j += 256) {
+            const float p = ((const lds_f32 *)s_out)[j];
+            out[row0 + j] = p;
+            atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+        }
         __syncthreads();
         hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
+    } else {
+        for (int j = threadIdx.x; j < rows; j += 256) out[row0 + j] = ((const lds_f32 *)s_out)[j];
     }
 }
 
@@ -790,15 +834,22 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
                                (int)tpw);
         return hipGetLastError();
     }
-    // chunk ring depth: as deep as LDS allows next to the histogram
+    if (!a.cand && tpw > kMaxTilesPerWave) {
+        tpw = kMaxTilesPerWave; // one page id per lane of the wave
+        wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    }
+    // chunk ring: 96 KiB next to the histogram and the staged scores
     constexpr int CPT = R == 256 ? 2 : 1;
-    constexpr int NB = R == 128 ? 4 : (R == 256 ? 4 : 8);
+    constexpr int NB = R == 64 ? 6 : 3;
     if (a.cand)
-        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                           (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
+                           a, (int)tpw);
+    else if (a.stream_nt)
+        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
+                           a, (int)tpw);
     else
-        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                           (int)tpw);
+        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
+                           a, (int)tpw);
     return hipGetLastError();
 }
 
