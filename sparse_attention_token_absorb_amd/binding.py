@@ -377,6 +377,42 @@ class TopK:
         self.scores = scores
 
 
+def topk_out_problem(out: TopK, Q: int, k: int, k_inner: int, max_valid: int) -> Optional[str]:
+    """Why the output buffers of a score_topk call do not fit what the
+    kernels write (dtype and shape; device placement is checked apart), or
+    None when they do.  A buffer that is too small would be written past."""
+    need = [("idx", out.idx, (Q, k)), ("count", out.count, (Q,))]
+    if k_inner:
+        if out.idx_inner is None or out.count_inner is None:
+            return "k_inner > 0 needs idx_inner [Q][k_inner] and count_inner [Q]"
+        need += [("idx_inner", out.idx_inner, (Q, k_inner)), ("count_inner", out.count_inner, (Q,))]
+    for name, t, shape in need:
+        if not isinstance(t, torch.Tensor):
+            return f"{name} must be a torch tensor"
+        if t.dtype != torch.int32:
+            return f"{name} must be int32 (got {t.dtype})"
+        if tuple(t.shape) != shape:
+            return f"{name} has shape {tuple(t.shape)}, expected {shape}"
+    if out.scores is not None:
+        t = out.scores
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            return "scores must be a float32 tensor"
+        if t.dim() != 2 or t.shape[0] != Q or t.shape[1] < max(max_valid, 1):
+            return f"scores must be [Q={Q}][ld >= {max(max_valid, 1)}], got {tuple(t.shape)}"
+    return None
+
+
+def _check_topk_out(out: TopK, Q: int, k: int, k_inner: int, max_valid: int, dev) -> None:
+    """Every output buffer of a score_topk call has the shape the kernels write."""
+    problem = topk_out_problem(out, Q, k, k_inner, max_valid)
+    if problem:
+        raise ValueError(problem)
+    for name, t in (("idx", out.idx), ("count", out.count), ("idx_inner", out.idx_inner),
+                    ("count_inner", out.count_inner), ("scores", out.scores)):
+        if t is not None:
+            _need(t, name, t.dtype, dev)
+
+
 def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int, q_tilde: torch.Tensor,
                w: torch.Tensor, k: int, k_inner: int = 0, keep_scores: bool = False,
                ws: Optional[torch.Tensor] = None, out: Optional[TopK] = None,
@@ -396,12 +432,8 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
             out.count_inner = torch.empty(Q, dtype=torch.int32, device=dev)
         if keep_scores:
             out.scores = torch.empty((Q, max(max_valid, 1)), dtype=torch.float32, device=dev)
-    _need(out.idx, "idx", torch.int32, dev, (Q, k))
-    _need(out.count, "count", torch.int32, dev, (Q,))
-    ld = 0
-    if out.scores is not None:
-        _need(out.scores, "scores", torch.float32, dev)
-        ld = int(out.scores.shape[1])
+    _check_topk_out(out, Q, k, k_inner, max_valid, dev)
+    ld = int(out.scores.shape[1]) if out.scores is not None else 0
     op = LI_OP_SCORE_TOPK_EXT_SCORES if out.scores is not None else LI_OP_SCORE_TOPK
     nb = workspace_bytes(op, Q, max_valid, H, cache.r, k, 0)
     ws = _workspace(dev, nb, ws)
