@@ -242,6 +242,23 @@ LI_API li_status li_score_topk(const li_cache *cache, const li_queries *queries,
                         int64_t ld, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * score_topk_noalloc — li_score_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results without the workspace.
+ * The library keeps one scratch array of 32 MiB per GPU (a static device
+ * array, held until the process ends) in its place; no call allocates or
+ * frees anything.  Calls whose workspace (li_workspace_bytes of
+ * LI_OP_SCORE_TOPK, or LI_OP_SCORE_TOPK_EXT_SCORES when scores is given)
+ * exceeds 32 MiB return LI_ERR_WORKSPACE without enqueueing anything.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (concurrent streams, threads) race and must be ordered by the caller.
+ */
+LI_API li_status li_score_topk_noalloc(const li_cache *cache, const li_queries *queries, const void *q_tilde,
+                                const float *w, const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count,
+                                int32_t k_inner, int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld,
+                                hipStream_t stream);
+
+/*
  * hs_select — HS follower step (§3.2, §3.4, §C.4): rescore only the anchor's
  * candidates with this layer's query and select this layer's top-k of them.
  *   cand       [Q][M] candidate positions (the anchor's idx output with

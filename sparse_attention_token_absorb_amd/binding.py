@@ -23,7 +23,7 @@ LI_BF16, LI_FP32, LI_FP8 = 0, 1, 2
 LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
 EXPORTED = ["li_append_latent", "li_append_latent_rope", "li_rope_decoder", "li_query_bias", "li_absorb_query",
-            "li_score_topk", "li_hs_select", "li_workspace_bytes", "li_fp8_query_bytes", "li_fp8_query_scale_offset",
+            "li_score_topk", "li_score_topk_noalloc", "li_hs_select", "li_workspace_bytes", "li_fp8_query_bytes", "li_fp8_query_scale_offset",
             "li_timing_enable", "li_timing_read", "li_status_str", "li_last_error", "li_abi_version"]
 (LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
  LI_KERNEL_APPEND) = range(6)
@@ -70,6 +70,7 @@ def lib():
         L.li_query_bias.argtypes = [vp, vp, i32, i32, i32, i32, vp, ctypes.c_int, vp]
         L.li_absorb_query.argtypes = [vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
         L.li_score_topk.argtypes = [cp, qp, vp, vp, vp, i32, i32, vp, vp, i32, vp, vp, vp, i64, vp, sz, vp]
+        L.li_score_topk_noalloc.argtypes = [cp, qp, vp, vp, vp, i32, i32, vp, vp, i32, vp, vp, vp, i64, vp]
         L.li_hs_select.argtypes = [cp, qp, vp, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.li_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32]
         L.li_workspace_bytes.restype = sz
@@ -441,6 +442,29 @@ def score_topk(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_val
     _check(lib().li_score_topk(ctypes.byref(c), ctypes.byref(qs), _ptr(qbuf), _ptr(w), _ptr(bias), H, k, _ptr(out.idx),
                                _ptr(out.count), k_inner, _ptr(out.idx_inner), _ptr(out.count_inner),
                                _ptr(out.scores), ld, _ptr(ws), ws.numel(), _stream(dev)), "li_score_topk")
+    return out
+
+
+def score_topk_noalloc(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid: int,
+                       q_tilde: torch.Tensor, w: torch.Tensor, k: int, out: TopK, k_inner: int = 0,
+                       bias: Optional[torch.Tensor] = None) -> TopK:
+    """li_score_topk_noalloc: li_score_topk on the library's per-GPU scratch
+    instead of a workspace.  `out` is required (the call allocates nothing);
+    out.scores, when set, receives the scores."""
+    dev = cache.device
+    qs = _queries(cache, seq, pos, max_valid)
+    Q = qs.Q
+    H, qbuf = _query_operand(cache, q_tilde, Q)
+    _need(w, "w", torch.float32, dev, (Q, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (Q, H))
+    _check_topk_out(out, Q, k, k_inner, max_valid, dev)
+    ld = int(out.scores.shape[1]) if out.scores is not None else 0
+    c = cache.desc()
+    _check(lib().li_score_topk_noalloc(ctypes.byref(c), ctypes.byref(qs), _ptr(qbuf), _ptr(w), _ptr(bias), H, k,
+                                       _ptr(out.idx), _ptr(out.count), k_inner, _ptr(out.idx_inner),
+                                       _ptr(out.count_inner), _ptr(out.scores), ld, _stream(dev)),
+           "li_score_topk_noalloc")
     return out
 
 

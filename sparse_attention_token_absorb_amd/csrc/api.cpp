@@ -10,11 +10,20 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/latentindex.h"
 #include "li_internal.hpp"
 #include "li_timing.hpp"
+
+// Scratch of li_score_topk_noalloc (the workspace of li_score_topk): one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory; the device address of each GPU's
+// copy comes from hipGetSymbolAddress and is the only form of it that is
+// passed to kernels.
+static constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -281,10 +290,12 @@ li_status li_absorb_query(const void *q, const void *w_dec, void *q_tilde, int32
     return ok();
 }
 
-li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
-                        const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner,
-                        int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld, void *ws,
-                        size_t ws_bytes, hipStream_t stream)
+namespace {
+
+li_status score_topk_impl(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
+                          const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner,
+                          int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld, void *ws,
+                          size_t ws_bytes, hipStream_t stream)
 {
     li_status st = check_cache(cache);
     if (st != LI_OK) return st;
@@ -370,6 +381,65 @@ li_status li_score_topk(const li_cache *cache, const li_queries *queries, const 
     if (e != hipSuccess) return hip_fail(e, "select launch");
 
     return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array (resolved on the first call
+// on that device, with the device current).
+li_status scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LI_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(LI_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LI_OK;
+}
+
+} // namespace
+
+li_status li_score_topk(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
+                        const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count, int32_t k_inner,
+                        int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld, void *ws,
+                        size_t ws_bytes, hipStream_t stream)
+{
+    return score_topk_impl(cache, queries, q_tilde, w, bias, H, k, idx, count, k_inner, idx_inner, count_inner,
+                           scores, ld, ws, ws_bytes, stream);
+}
+
+li_status li_score_topk_noalloc(const li_cache *cache, const li_queries *queries, const void *q_tilde, const float *w,
+                                const float *bias, int32_t H, int32_t k, int32_t *idx, int32_t *count,
+                                int32_t k_inner, int32_t *idx_inner, int32_t *count_inner, float *scores, int64_t ld,
+                                hipStream_t stream)
+{
+    li_status st = check_cache(cache);
+    if (st != LI_OK) return st;
+    st = check_queries(queries, cache);
+    if (st != LI_OK) return st;
+    if (k <= 0 || k > LI_MAX_TOPK) return fail(LI_ERR_SHAPE, "k=%d outside [1, %d]", k, LI_MAX_TOPK);
+    if (queries->Q == 0) return ok();
+    const int op = scores ? LI_OP_SCORE_TOPK_EXT_SCORES : LI_OP_SCORE_TOPK;
+    const size_t need = li_workspace_bytes(op, queries->Q, queries->max_valid, H, cache->r, k, 0);
+    if (need > kScratchBytes)
+        return fail(LI_ERR_WORKSPACE,
+                    "li_score_topk_noalloc needs %zu bytes of scratch at Q=%d, max_valid=%d, more than its %zu%s", need,
+                    queries->Q, queries->max_valid, kScratchBytes, scores ? "" : " (a caller score buffer needs less)");
+    void *ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != LI_OK) return st;
+    return score_topk_impl(cache, queries, q_tilde, w, bias, H, k, idx, count, k_inner, idx_inner, count_inner, scores,
+                           ld, ws, kScratchBytes, stream);
 }
 
 li_status li_hs_select(const li_cache *cache, const li_queries *queries, const int32_t *cand,
