@@ -31,9 +31,12 @@
  *   - Row-major layouts; int32 indices; `bf16` means IEEE bfloat16 bits.
  *   - Host-side validation happens before anything is enqueued: a failing
  *     call returns a status, enqueues nothing and never aborts.  Values that
- *     live in device memory (seq_lens, block-table entries, positions,
- *     candidates) cannot be checked on the host; out-of-range values there
- *     are undefined behaviour.  NaN/Inf inputs are undefined.
+ *     live in device memory (sequence ids, seq_lens, block-table entries,
+ *     positions, candidates) cannot be checked on the host; the kernels bound
+ *     them where they use them (an append whose sequence, position or page
+ *     lies outside the cache writes nothing; other indices are clamped into
+ *     range), so out-of-range values give meaningless results but never an
+ *     access outside the caller's buffers.  NaN/Inf inputs are undefined.
  *   - LI_ERR_HIP reports a failed launch (detail in li_last_error()).
  *   - Calls on different streams are independent; calls that share output
  *     or workspace buffers must be ordered by the caller.

@@ -206,15 +206,15 @@ li_status append_common(const li_cache *cache, const void *rows, const int32_t *
     hipError_t e;
     {
         li::TimedScope ts(LI_KERNEL_APPEND, stream);
+        const li::PoolGeom geo{cache->batch, cache->max_pages, cache->num_pages};
         if (cache->dtype == LI_FP8)
-            e = li::launch_append_fp8(cache->pool, cache->scales, cache->block_table, cache->max_pages, cache->r, rows,
-                                      seq, pos, T, ra, stream);
+            e = li::launch_append_fp8(cache->pool, cache->scales, cache->block_table, geo, cache->r, rows, seq, pos, T,
+                                      ra, stream);
         else if (rope)
-            e = li::launch_append_rope(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq,
-                                       pos, T, ra, stream);
+            e = li::launch_append_rope(cache->pool, cache->block_table, geo, cache->r, esize, rows, seq, pos, T, ra,
+                                       stream);
         else
-            e = li::launch_append(cache->pool, cache->block_table, cache->max_pages, cache->r, esize, rows, seq, pos,
-                                  T, stream);
+            e = li::launch_append(cache->pool, cache->block_table, geo, cache->r, esize, rows, seq, pos, T, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "append_latent launch");
     return ok();
@@ -331,6 +331,7 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
     sc.qseq = queries->seq;
     sc.qpos = queries->pos;
     sc.seq_lens = cache->seq_lens;
+    sc.batch = cache->batch;
     sc.Q = Q;
     sc.k = k;
     sc.max_n = queries->max_valid; // rows past the caller's bound are never scored
@@ -465,8 +466,57 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
 
     uint8_t *p = (uint8_t *)ws;
     float *S = cand_scores ? cand_scores : (float *)p;
+    float *S_pos = (float *)p; // by-position scores (see below)
     p += align256((size_t)Q * M * 4);
     li::SelWorkspace sw = li::sel_workspace_carve(p, Q, M);
+
+    // When M >= max_valid, no query has more valid rows than M, so scoring a
+    // query's whole valid prefix reads no more rows than its candidates may
+    // number, and reads them as contiguous tiles instead of through the
+    // candidate -> page -> row chain.  The scores are then kept by position
+    // (S_pos[q][row], stride M) and the selection reads each candidate's
+    // score through the candidate list, which is exact for any list of
+    // valid rows.
+    if (queries->max_valid <= M) {
+        hipError_t e = hipSuccess;
+        li::ScoreArgs a = score_args(cache, queries, q_tilde, w, H);
+        a.bias = bias;
+        a.out = S_pos;
+        a.out_ld = M;
+        a.max_rows = queries->max_valid;
+        a.hist = nullptr;
+        const bool fp8 = cache->dtype == LI_FP8;
+        const int64_t row_bytes =
+            fp8 ? cache->r + cache->r / 128 * 4 : (int64_t)cache->r * (cache->dtype == LI_BF16 ? 2 : 4);
+        a.stream_nt = stream_nt((int64_t)Q * queries->max_valid * row_bytes);
+        if (queries->max_valid > 0) {
+            li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
+            if (fp8)
+                e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r,
+                                         false, queries->max_valid, stream);
+            else
+                e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, queries->max_valid, stream);
+            if (e == hipSuccess && cand_scores)
+                e = li::launch_gather_scores(S_pos, M, cand, cand_count, M, cand_scores, Q, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "hs score launch");
+        li::SelCall sc{};
+        sc.row = li::SelRow{S_pos, M, cand, M, cand, M};
+        sc.src_mode = li::kSrcCount;
+        sc.cnt = cand_count;
+        sc.cnt_cap = M;
+        sc.Q = Q;
+        sc.k = k;
+        sc.max_n = M;
+        sc.idx = idx;
+        sc.count = count;
+        {
+            li::TimedScope ts(LI_KERNEL_SELECT, stream);
+            e = li::launch_select(sc, sw, false, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "hs select launch");
+        return ok();
+    }
 
     li::SelCall sc{};
     sc.row = li::SelRow{S, M, nullptr, 0, cand, M};

@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kSeg = 128;               // elements per quantization segment
 constexpr int kGatherTilesF8 = 16;      // max tiles per wave in gather mode
+constexpr int kMaxTilesPerWaveF8 = 64;  // max tiles per wave in contiguous mode (one page id per lane)
 
 // 2^k as an fp32 (k in [-126, 127]).
 __device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
@@ -164,7 +165,7 @@ __device__ __forceinline__ void rotate_quantize(float (&x)[NR][4], int l32, int 
 // their page slots.  One half-wave per (row, segment).
 // ---------------------------------------------------------------------------
 template <int R>
-__global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales, const int32_t *bt, int max_pages,
+__global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales, const int32_t *bt, PoolGeom geo,
                                                     const u16 *rows, const int32_t *seq, const int32_t *pos, int T,
                                                     const RopeArgs rope)
 {
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(256) void k_append_fp8(uint8_t *pool, float *scales
     const uint32_t codes = cw[0];
     const int e = ee[0];
     if (!live) return;
-    const int p = pos[t];
-    const int64_t slot = (int64_t)bt[(int64_t)seq[t] * max_pages + (p >> 6)] * kPage + (p & 63);
+    const int64_t slot = geo.slot(bt, seq[t], pos[t]);
+    if (slot < 0) return; // a sequence, position or page outside the cache: the row is not written
     *(uint32_t *)(pool + slot * R + g * kSeg + 4 * l32) = codes;
     if (l32 == 0) scales[slot * NSEG + g] = exp2i(e);
 }
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(256) void k_absorb_fp8_row(const u16 *q, const u16 
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int R, int HB, bool GATHER, int NB>
+template <int R, int HB, bool GATHER, int NB, bool NT>
 __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *pool_scales, int64_t qscale_off,
                                                    int tiles_per_wave)
 {
@@ -419,9 +420,11 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     constexpr int NIT = NIC + 1;               // + the scales
     constexpr int CH = R / 16;                 // 16-byte pieces per row
     constexpr int KS = R / 64;                 // MFMA k-steps
+    constexpr int MAXT = GATHER ? kGatherTilesF8 : kMaxTilesPerWaveF8; // tiles per wave (scores kept in LDS)
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * SLOT];
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTilesF8 * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
+    __shared__ float s_out[4 * MAXT * kTile];
 
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -467,14 +470,29 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             }
         }
     }
-    const int b = ((const_i32_t *)a.qseq)[q];
+    // Contiguous mode: lane i holds the page id of this wave's tile i (at
+    // most 64 tiles per wave); query q usually sits in sequence q, so that
+    // block-table row is requested before the sequence id arrives.
+    const int b_guess = q < a.batch ? q : 0;
+    int page_guess = 0;
+    if constexpr (!GATHER) {
+        if (lane < nt_max) page_guess = a.bt[(int64_t)b_guess * a.max_pages + (tile_row0(lane) >> 6)];
+    }
+    const int b = clamp_index(((const_i32_t *)a.qseq)[q], a.batch);
     int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
                    : valid_rows(((const_i32_t *)a.qpos)[q], ((const_i32_t *)a.seq_lens)[b]);
     n = (int)min64(n, a.max_rows);
     const uint8_t *pool = (const uint8_t *)a.pool;
-    const_i32_t *bt = (const_i32_t *)(a.bt + (int64_t)b * a.max_pages);
     lds_u8 *const ring = (lds_u8 *)ring_raw + wv * NB * SLOT;
     auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
+    int tile_page = 0;
+    if constexpr (!GATHER) {
+        if (b == b_guess)
+            tile_page = page_guess;
+        else if (lane < nt_max)
+            tile_page = a.bt[(int64_t)b * a.max_pages + (tile_row0(lane) >> 6)];
+        tile_page = clamp_page(tile_page);
+    }
 
     if constexpr (GATHER) {
         // physical slots of every tile row of this wave, two batched rounds
@@ -509,7 +527,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         int64_t base = 0;
         if constexpr (!GATHER) {
             const int64_t t0 = tile_row0(i);
-            base = (int64_t)clamp_page(bt[t0 >> 6]) * kPage + (t0 & 63);
+            base = (int64_t)__builtin_amdgcn_readlane(tile_page, i) * kPage + (t0 & 63);
         }
         auto slot_of = [&](int nr) -> int64_t {
             if constexpr (GATHER) return (int64_t)rows[nr];
@@ -520,7 +538,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             const int p = ii * 64 + lane;
             const int nr = p / CH, cs = p % CH;
             const int c = cs ^ (nr % CH);
-            dma16(pool + slot_of(nr) * R + c * 16, slot + ii * 1024);
+            dma16p<NT>(pool + slot_of(nr) * R + c * 16, slot + ii * 1024);
         }
         // scales: lane l carries (row l / NSEG, segment l % NSEG); lanes past
         // the tile's 32 rows repeat its last row
@@ -541,7 +559,8 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     if (first < n) nt = (int)min64(tiles_per_wave, (n - first + 4 * kTile - 1) / (4 * kTile));
     if (a.hist) wg_barrier(); // histogram cleared before any wave counts into it
 
-    float *out = a.out + (int64_t)q * a.out_ld;
+    __attribute__((address_space(3))) float *const outw =
+        (__attribute__((address_space(3))) float *)s_out + wv * kTile;
     const int nr = lane & 31, gk = lane >> 5;
     for (int i = 0; i < nt; ++i) {
         if (i + NB - 1 < nt) {
@@ -571,16 +590,26 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
                                                                           sb[g]);
         }
         const float p = epilogue<HB>(acc, wr);
-        const int64_t j = tile_row0(i) + lane;
-        if (lane < 32 && j < n) {
-            out[j] = p;
-            if (a.hist) atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
-        }
+        if (lane < 32 && tile_row0(i) + lane < n) outw[i * 4 * kTile + lane] = p; // local row (i * 4 + wv) * 32 + lane
     }
     wait_vmcnt<0>(); // tiles issued ahead of the row count and never used
+    __syncthreads(); // every wave's scores are in LDS (and the histogram is cleared)
+    // The scores leave in one coalesced pass over the workgroup's rows (score
+    // stores among the stream's loads interleave DRAM writes with the read
+    // stream), which also counts their first radix digit.
+    float *out = a.out + (int64_t)q * a.out_ld;
+    const int rows = (int)min64(4 * (int64_t)tiles_per_wave * kTile, n - row0);
     if (a.hist) {
+        for (int j = threadIdx.x; j < rows; j += 256) {
+            const float p = ((const __attribute__((address_space(3))) float *)s_out)[j];
+            out[row0 + j] = p;
+            atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+        }
         __syncthreads();
         hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
+    } else {
+        for (int j = threadIdx.x; j < rows; j += 256)
+            out[row0 + j] = ((const __attribute__((address_space(3))) float *)s_out)[j];
     }
 }
 
@@ -621,7 +650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int qq = qbase + u;
-        sb[u] = qq < a.Q ? qseq[qq] : -1;
+        sb[u] = qq < a.Q ? clamp_index(qseq[qq], a.batch) : -1;
         sn[u] = qq < a.Q ? (int)min64(valid_rows(qpos[qq], slen[sb[u]]), a.max_rows) : 0;
     }
     const int q = qbase + wv;
@@ -693,7 +722,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int p0 = ts >> 1;
         const int np = ((te - 1) >> 1) - p0 + 1;
         __syncthreads(); // the previous pass is done with the ring and the page ids
-        for (int pi = threadIdx.x; pi < np; pi += 256) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
+        for (int pi = threadIdx.x; pi < np; pi += 256)
+            s_page[pi] = clamp_index(a.bt[(int64_t)b * a.max_pages + p0 + pi], a.num_pages);
         __syncthreads();
         auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
         auto issue = [&](int i, int page) {
@@ -785,19 +815,24 @@ template <int R, int HB>
 hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
                                hipStream_t s)
 {
-    constexpr int NB = R == 256 ? 4 : 7;
+    // ring next to the histogram and the staged scores: 3 slots at r = 256, 5 at r = 128
+    constexpr int NB = R == 256 ? 3 : 5;
     const int64_t tiles = (max_rows + kTile - 1) / kTile;
     const int64_t per_q = (256 + a.Q - 1) / a.Q;
     int64_t tpw = (tiles + 4 * per_q - 1) / (4 * per_q);
     if (tpw < 1) tpw = 1;
     if (a.cand && tpw > kGatherTilesF8) tpw = kGatherTilesF8;
+    if (!a.cand && tpw > kMaxTilesPerWaveF8) tpw = kMaxTilesPerWaveF8;
     const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
     if (a.cand)
-        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, pool_scales,
-                           qscale_off, (int)tpw);
+        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NB, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                           pool_scales, qscale_off, (int)tpw);
+    else if (a.stream_nt)
+        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                           pool_scales, qscale_off, (int)tpw);
     else
-        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a, pool_scales,
-                           qscale_off, (int)tpw);
+        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                           pool_scales, qscale_off, (int)tpw);
     return hipGetLastError();
 }
 
@@ -852,17 +887,17 @@ hipError_t launch_absorb_fp8_r(const u16 *q, const u16 *W, uint8_t *codes, float
 
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r) { return (Q * H * r + 255) / 256 * 256; }
 
-hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
+hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, const PoolGeom &geo, int r, const void *rows,
                              const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
     const int64_t halves = (int64_t)T * (r / kSeg);
     const unsigned blocks = (unsigned)((halves * 32 + 255) / 256);
     if (r == 256)
-        hipLaunchKernelGGL((k_append_fp8<256>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
+        hipLaunchKernelGGL((k_append_fp8<256>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, geo,
                            (const u16 *)rows, seq, pos, T, rope);
     else if (r == 128)
-        hipLaunchKernelGGL((k_append_fp8<128>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, max_pages,
+        hipLaunchKernelGGL((k_append_fp8<128>), dim3(blocks), dim3(256), 0, s, (uint8_t *)pool, scales, bt, geo,
                            (const u16 *)rows, seq, pos, T, rope);
     else
         return hipErrorInvalidValue;

@@ -27,6 +27,12 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Device-resident indices (sequence ids, page ids, positions, candidates)
+// come from the caller's buffers and cannot be checked on the host; every
+// kernel bounds them where it uses them, so an out-of-range value gives
+// meaningless results but never an access outside the buffers.
+__device__ __forceinline__ int clamp_index(int v, int n) { return v < 0 ? 0 : (v < n ? v : n - 1); }
+
 // Rows a query scores: the causal prefix, inclusive of its own position,
 // capped by the rows present in its sequence.
 __device__ __forceinline__ int valid_rows(int pos, int seq_len)

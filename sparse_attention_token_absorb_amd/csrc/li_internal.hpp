@@ -25,6 +25,22 @@ enum {
     kSlotAboveI = kHistBins + 7, // the same for the inner one
 };
 
+// Geometry of a paged pool, for bounding device-resident indices.
+struct PoolGeom {
+    int32_t batch;
+    int32_t max_pages;
+    int32_t num_pages;
+    // Physical row of position p of sequence s, or -1 when s, p or the page
+    // they map to lies outside the cache.
+    __device__ __forceinline__ int64_t slot(const int32_t *bt, int s, int p) const
+    {
+        if (s < 0 || s >= batch || p < 0 || (int64_t)p >= (int64_t)max_pages * 64) return -1;
+        const int page = bt[(int64_t)s * max_pages + (p >> 6)];
+        if (page < 0 || page >= num_pages) return -1;
+        return (int64_t)page * 64 + (p & 63);
+    }
+};
+
 // Rows to score for one call.
 //   contiguous mode (cand == nullptr): query i scores its causal prefix
 //     rows 0..n_i-1, n_i = min(qpos[i] + 1, seq_lens[qseq[i]]);
@@ -59,6 +75,11 @@ struct ScoreArgs {
 hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq,
                         int64_t max_rows, hipStream_t s);
 
+// out[q][j] = S[q][cand[q][j]] for j < min(cand_count[q], M) (candidates
+// clamped into [0, ld)); entries past the count are left untouched.
+hipError_t launch_gather_scores(const float *S, int64_t ld, const int32_t *cand, const int32_t *cand_count, int64_t M,
+                                float *out, int32_t Q, hipStream_t s);
+
 // Absorption qt = q W (see li_absorb_query).
 hipError_t launch_absorb(const void *q, const void *W, void *qt, int64_t QH, int d, int r, bool bf16,
                          hipStream_t s);
@@ -76,19 +97,19 @@ struct RopeArgs {
     double theta[kMaxRopeFreqs];
 };
 
-hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, int max_pages, int r, const void *rows,
+hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, const PoolGeom &geo, int r, const void *rows,
                              const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s);
 hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH, int d, int r, hipStream_t s);
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
                             bool many_queries_per_seq, int64_t max_rows, hipStream_t s);
 
 // Append rows into the paged pool.
-hipError_t launch_append(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
+hipError_t launch_append(void *pool, const int32_t *bt, const PoolGeom &geo, int r, int esize, const void *rows,
                          const int32_t *seq, const int32_t *pos, int T, hipStream_t s);
 
 // RoPE-compatible structured decoder: rotated append (bf16 / fp32 pools),
 // lowering of the decoder to a dense W, and the absorbed bias.
-hipError_t launch_append_rope(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
+hipError_t launch_append_rope(void *pool, const int32_t *bt, const PoolGeom &geo, int r, int esize, const void *rows,
                               const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s);
 hipError_t launch_rope_decoder(const void *D, const void *Wn, int F, int S, int d_nope, int r_nope, void *W, int esize,
                                hipStream_t s);
@@ -114,6 +135,7 @@ struct SelCall {
     SelRow row;
     int src_mode;
     const int32_t *qseq, *qpos, *seq_lens;  // kSrcCausal
+    int32_t batch;                           // sequences (qseq entries are clamped below it)
     const int32_t *cnt;                      // kSrcCount
     int32_t cnt_cap;
     int32_t Q;

@@ -46,7 +46,7 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, double v)
 // One thread per element pair of a row (a last unpaired element of an odd
 // fp32 row is copied).
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_append_rope(void *pool, const int32_t *bt, int max_pages, int r,
+__global__ __launch_bounds__(256) void k_append_rope(void *pool, const int32_t *bt, PoolGeom geo, int r,
                                                      const void *rows, const int32_t *seq, const int32_t *pos, int T,
                                                      const RopeArgs rope)
 {
@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256) void k_append_rope(void *pool, const int32_t *
     const int t = (int)(i / pairs);
     const int j = (int)(i % pairs);
     const int p = pos[t];
-    const int64_t dst = ((int64_t)bt[(int64_t)seq[t] * max_pages + (p >> 6)] * kPage + (p & 63)) * r;
+    const int64_t slot = geo.slot(bt, seq[t], p);
+    if (slot < 0) return; // a sequence, position or page outside the cache: the row is not written
+    const int64_t dst = slot * r;
     const int64_t src = (int64_t)t * r;
     double re = load_elem<BF16>(rows, src + 2 * j);
     if (2 * j + 1 >= r) {
@@ -118,17 +120,17 @@ __global__ __launch_bounds__(256) void k_query_bias(const void *q, const float *
 
 } // namespace
 
-hipError_t launch_append_rope(void *pool, const int32_t *bt, int max_pages, int r, int esize, const void *rows,
+hipError_t launch_append_rope(void *pool, const int32_t *bt, const PoolGeom &geo, int r, int esize, const void *rows,
                               const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
     const int64_t n = (int64_t)T * ((r + 1) / 2);
     const dim3 grid((unsigned)((n + 255) / 256));
     if (esize == 2)
-        hipLaunchKernelGGL(k_append_rope<true>, grid, dim3(256), 0, s, pool, bt, max_pages, r, rows, seq, pos, T,
+        hipLaunchKernelGGL(k_append_rope<true>, grid, dim3(256), 0, s, pool, bt, geo, r, rows, seq, pos, T,
                            rope);
     else
-        hipLaunchKernelGGL(k_append_rope<false>, grid, dim3(256), 0, s, pool, bt, max_pages, r, rows, seq, pos, T,
+        hipLaunchKernelGGL(k_append_rope<false>, grid, dim3(256), 0, s, pool, bt, geo, r, rows, seq, pos, T,
                            rope);
     return hipGetLastError();
 }

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
                                                      (lds_f32 *)s_w, (lds_f32 *)s_b);
     auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
     // Scalar loads (constant address space): waited on with lgkmcnt.
-    const int b = ((const_i32_t *)a.qseq)[q];
+    const int b = clamp_index(((const_i32_t *)a.qseq)[q], a.batch);
     int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
                    : valid_rows(((const_i32_t *)a.qpos)[q], ((const_i32_t *)a.seq_lens)[b]);
     n = (int)min64(n, a.max_rows);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int b = a.qseq[q];
+    const int b = clamp_index(a.qseq[q], a.batch);
     int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
@@ -445,8 +445,8 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
         for (int i = 0; i < nt; ++i) {
             int64_t j = tile_row0(i) + nr;
             j = j < n ? j : n - 1;
-            const int pos = a.cand[(int64_t)q * a.cand_ld + j];
-            const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
+            const int pos = clamp_index(a.cand[(int64_t)q * a.cand_ld + j], a.max_pages * kPage);
+            const int page = clamp_index(a.bt[(int64_t)b * a.max_pages + (pos >> 6)], a.num_pages);
             if (lane < 32) s_row[(wv * kGatherTiles + i) * kTile + lane] = page * kPage + (pos & 63);
         }
         wait_lds();
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
             const int64_t t0 = tile_row0(i);
             int64_t j = nr;
             if (t0 + j >= n) j = n - 1 - t0; // stay inside the sequence's last page
-            off = ((int64_t)bt[t0 >> 6] * kPage + (t0 & 63) + j) * R;
+            off = ((int64_t)clamp_index(bt[t0 >> 6], a.num_pages) * kPage + (t0 & 63) + j) * R;
         }
         return pool + off + (lane >> 5) * 8;
     };
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
         const int qq = qbase + u;
-        sb[u] = qq < a.Q ? qseq[qq] : -1;
+        sb[u] = qq < a.Q ? clamp_index(qseq[qq], a.batch) : -1;
         sn[u] = qq < a.Q ? (int)min64(valid_rows(qpos[qq], slen[sb[u]]), a.max_rows) : 0;
     }
     const int q = qbase + wv;
@@ -668,7 +668,8 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int p0 = ts >> 1;
         const int np = ((te - 1) >> 1) - p0 + 1;
         __syncthreads(); // the previous pass is done with the ring and the page ids
-        for (int pi = threadIdx.x; pi < np; pi += NT) s_page[pi] = a.bt[(int64_t)b * a.max_pages + p0 + pi];
+        for (int pi = threadIdx.x; pi < np; pi += NT)
+            s_page[pi] = clamp_index(a.bt[(int64_t)b * a.max_pages + p0 + pi], a.num_pages);
         __syncthreads();
         auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
         auto issue = [&](int i, int page) {
@@ -733,7 +734,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     __shared__ float sb[64];
     __shared__ uint32_t s_hist[kHistBins];
     const int q = blockIdx.y;
-    const int b = a.qseq[q];
+    const int b = clamp_index(a.qseq[q], a.batch);
     int n = a.cand ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
@@ -749,8 +750,8 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
     __syncthreads();
     for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
-        const int pos = a.cand ? a.cand[(int64_t)q * a.cand_ld + j] : (int)j;
-        const int page = a.bt[(int64_t)b * a.max_pages + (pos >> 6)];
+        const int pos = a.cand ? clamp_index(a.cand[(int64_t)q * a.cand_ld + j], a.max_pages * kPage) : (int)j;
+        const int page = clamp_index(a.bt[(int64_t)b * a.max_pages + (pos >> 6)], a.num_pages);
         const float *row = (const float *)a.pool + ((int64_t)page * kPage + (pos & 63)) * R;
         float sc = 0.0f;
         for (int h = 0; h < a.H; ++h) {
@@ -860,7 +861,29 @@ hipError_t launch_r(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStrea
     return launch_bf16<R, 2>(a, prefill, max_rows, s);
 }
 
+// Candidate scores from scores kept by position.
+__global__ __launch_bounds__(256) void k_gather_scores(const float *S, int64_t ld, const int32_t *cand,
+                                                       const int32_t *cand_count, int64_t M, float *out)
+{
+    const int q = blockIdx.y;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = min64(max(cand_count[q], 0), M);
+    if (j >= n) return;
+    int64_t c = cand[(int64_t)q * M + j];
+    c = c < 0 ? 0 : (c < ld ? c : ld - 1);
+    out[(int64_t)q * M + j] = S[(int64_t)q * ld + c];
+}
+
 } // namespace
+
+hipError_t launch_gather_scores(const float *S, int64_t ld, const int32_t *cand, const int32_t *cand_count, int64_t M,
+                                float *out, int32_t Q, hipStream_t s)
+{
+    if (Q <= 0 || M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gather_scores, dim3((unsigned)((M + 255) / 256), Q), dim3(256), 0, s, S, ld, cand, cand_count,
+                       M, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq, int64_t max_rows,
                         hipStream_t s)

@@ -45,7 +45,11 @@ constexpr int kFilterChunk = kFilterThreads * kB * 4; // rows per filter workgro
 
 __device__ __forceinline__ uint32_t key_at(const SelRow &r, int q, int64_t i)
 {
-    const int64_t j = r.gmap ? (int64_t)r.gmap[(int64_t)q * r.gld + i] : i;
+    int64_t j = i;
+    if (r.gmap) { // a mapped index stays inside the row
+        j = r.gmap[(int64_t)q * r.gld + i];
+        j = j < 0 ? 0 : (j < r.ld ? j : r.ld - 1);
+    }
     return score_key(r.S[(int64_t)q * r.ld + j]);
 }
 
@@ -81,7 +85,7 @@ __device__ __forceinline__ int query_n(const SelCall &c, int q)
 {
     int n;
     if (c.src_mode == kSrcCausal) {
-        n = valid_rows(c.qpos[q], c.seq_lens[c.qseq[q]]);
+        n = valid_rows(c.qpos[q], c.seq_lens[clamp_index(c.qseq[q], c.batch)]);
     } else {
         n = c.cnt[q] < c.cnt_cap ? c.cnt[q] : c.cnt_cap;
     }
