@@ -28,36 +28,54 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+# Host-side AddressSanitizer build (variant "asan"): the host code of every
+# source is instrumented; device code is built as usual (GPU sanitizers are
+# not used).  Each -fsanitize flag applies to the host pass only.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+BUILD_ASAN = os.path.join(HERE, "_build_asan")
+LIB_ASAN = os.path.join(BUILD_ASAN, "liblatentindex_asan.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _flags(variant=None):
+    f = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+    if variant == "asan":
+        f += ASAN_HOST
+    return f
+
+
+def _compile(src: str, variant=None) -> str:
+    out_dir = BUILD_ASAN if variant == "asan" else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *_flags(variant), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, variant=None) -> str:
+    """Build liblatentindex.so (variant None) or the host-ASan library
+    _build_asan/liblatentindex_asan.so (variant "asan")."""
+    out_dir = BUILD_ASAN if variant == "asan" else BUILD
+    lib = LIB_ASAN if variant == "asan" else LIB
+    os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, variant), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if variant == "asan":
+        cmd += ["-Xarch_host", "-fsanitize=address", "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, variant=sys.argv[1] if len(sys.argv) > 1 else None)
     sys.exit(0)
