@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--no-model", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the roofline kernel's cold launches (a 1 GiB scrub before each), for a rocprofv3 "
+                         "kernel trace whose average duration is the line's roofline figure; prints their timing")
     ap.add_argument("--counters", choices=("decode", "prefill"), default=None,
                     help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
                          "then a plain 1 GiB copy whose counter readings scale the others to bytes; 'prefill' runs "
@@ -176,6 +179,30 @@ def main() -> int:
         log(f"counter pass done: 3 x {G} full-LatentIndex layers, 3 x copy of {src.numel() * 4} bytes")
         return 0
 
+    if args.roofline_only:
+        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        bytes_launch = Bn * N * 2 * r + Bn * (H * r * 2 + H * 4)
+        with torch.cuda.stream(stream):
+            B.score_topk(cache, seq, pos, N, qt[0], w[0], k, ws=ws, out=out_b[0])  # first launch, untimed
+        torch.cuda.synchronize()
+        B.timing_read(B.LI_KERNEL_SCORE_DECODE)
+        B.timing_enable(True)
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                for l in range(G):
+                    torch.sum(scrub, dim=0, keepdim=True, out=sink)
+                    B.absorb_query(q[l], W[l], out=qt[l])
+                    B.score_topk(cache, seq, pos, N, qt[l], w[l], k, ws=ws, out=out_b[l])
+        torch.cuda.synchronize()
+        B.timing_enable(False)
+        tot, n = B.timing_read(B.LI_KERNEL_SCORE_DECODE)
+        us = tot / max(n, 1) * 1e3
+        print(json.dumps({"kernel": "k_score_decode (r=256, 64 heads, B=4, N=131072, cold)", "launches": n,
+                          "avg_launch_us": round(us, 2), "bytes_per_launch": bytes_launch,
+                          "achieved_GBs": round(bytes_launch / us / 1e3, 1)}), flush=True)
+        return 0
+
     def capture(fn):
         with torch.cuda.stream(stream):
             fn()  # eager warm-up on the capture stream
@@ -271,17 +298,21 @@ def main() -> int:
     score_ms, n_launch = kernel_time(mode_b, B.LI_KERNEL_SCORE_DECODE, reps)
     sel_ms, _ = kernel_time(mode_b, B.LI_KERNEL_SELECT, reps)
     achieved = bytes_launch / (score_ms * 1e-3) / 1e9
-    # cold: reading 1 GiB of other data between launches evicts the 256 MB
-    # Infinity Cache (a read-only scrub leaves no dirty lines to write back)
+    # cold (the roofline figure): reading 1 GiB of other data between
+    # launches evicts the 256 MB Infinity Cache (a read-only scrub leaves no
+    # dirty lines to write back)
     scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty(1, dtype=torch.float32, device=dev)
 
     def cold_b():
+        # each layer as a decode step runs it: absorption, then scoring, with
+        # the latent evicted from every cache in between layers
         for l in range(G):
             torch.sum(scrub, dim=0, keepdim=True, out=sink)
+            B.absorb_query(q[l], W[l], out=qt[l])
             B.score_topk(cache, seq, pos, N, qt[l], w[l], k, ws=ws, out=out_b[l])
 
-    cold_ms, _ = kernel_time(cold_b, B.LI_KERNEL_SCORE_DECODE, max(reps // 2, 4))
+    cold_ms, n_cold = kernel_time(cold_b, B.LI_KERNEL_SCORE_DECODE, max(reps // 2, 4))
     del scrub
     # The 268 MB latent is about the size of the 256 MB last-level cache, so
     # warm repeats are partly served from it; the same kernel over pools of
@@ -310,15 +341,17 @@ def main() -> int:
     a_bytes = Bn * N * 2 * d + Bn * (H * d * 2 + H * 4)
     f_ms, _ = kernel_time(mode_c, B.LI_KERNEL_SCORE_GATHER, reps)
     f_bytes = Bn * min(M, N) * (bytes_row + 4) + Bn * bytes_query
+    cold_gbs = bytes_launch / (cold_ms * 1e-3) / 1e9
     roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "achieved": round(cold_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(os.path.join(ROOT, "profiles", "score_decode_r256_h64_b4_n131072.md"),
                                     os.path.join(ROOT, "sparse_attention_token_absorb_amd", "csrc", "score.hip")),
         "kernel": f"k_score_decode<r={r},64 heads> (full LatentIndex, B={Bn}, N={N})",
-        "avg_launch_us": round(score_ms * 1e3, 2), "launches": n_launch, "bytes_per_launch": bytes_launch,
-        "cold_avg_launch_us": round(cold_ms * 1e3, 2),
-        "cold_achieved_GBs": round(bytes_launch / (cold_ms * 1e-3) / 1e9, 1),
+        "timing": "cold: a 1 GiB read-only scrub before every launch evicts the 256 MB last-level cache",
+        "avg_launch_us": round(cold_ms * 1e3, 2), "launches": n_cold, "bytes_per_launch": bytes_launch,
+        "warm_avg_launch_us": round(score_ms * 1e3, 2), "warm_launches": n_launch,
+        "warm_achieved_GBs": round(achieved, 1), "warm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "beyond_llc": large,
         "select_us_per_layer": round(sel_ms * 1e3, 2),
         "baseline_r128_score_us": round(a_score_ms * 1e3, 2),
@@ -445,6 +478,16 @@ def main() -> int:
         f8_ms_full = time_graph(capture(f8_full), reps)
         f8_ms_hs = time_graph(capture(f8_hs), reps)
         f8_score_ms, _ = kernel_time(f8_full, B.LI_KERNEL_SCORE_DECODE, reps)
+        scrub8 = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+        def f8_cold():
+            for l in range(G):
+                torch.sum(scrub8, dim=0, keepdim=True, out=sink)
+                B.absorb_query(q[l], W[l], out=f8q[l], fp8=True)
+                B.score_topk(f8cache, seq, pos, N, f8q[l], w[l], k, ws=ws, out=out_b[l])
+
+        f8_cold_ms, _ = kernel_time(f8_cold, B.LI_KERNEL_SCORE_DECODE, max(reps // 2, 4))
+        del scrub8
         f8_bytes_row = r + (r // 128) * 4
         f8_bytes = Bn * N * f8_bytes_row + Bn * (H * r + H * (r // 128) * 4 + H * 4)
         f8_gbs = f8_bytes / (f8_score_ms * 1e-3) / 1e9
@@ -453,6 +496,8 @@ def main() -> int:
                "hs_us_per_group": round(f8_ms_hs * 1e3, 2),
                "score_kernel_us": round(f8_score_ms * 1e3, 2), "bytes_per_launch": f8_bytes,
                "score_GBs": round(f8_gbs, 1), "score_frac_hbm": round(f8_gbs / HBM_PEAK_GBS, 4),
+               "cold_score_kernel_us": round(f8_cold_ms * 1e3, 2),
+               "cold_score_frac_hbm": round(f8_bytes / (f8_cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "rows_per_s_full": round(G * Bn * N / (f8_ms_full * 1e-3), 1)}
         log(f"fp8 {fp8}")
         del f8pool, f8sc, f8cache, f8q
@@ -524,6 +569,25 @@ def main() -> int:
                "sample": f"full LatentIndex (mode b) at B={Bn}, N={N}: {layers_done} layer passes (the group's "
                          f"{G} layers in turn) x {Bn} queries x {N} rows, each absorb + fp64 scoring + top-{k} "
                          f"sort; {el:.1f} s on {cpu_model()}"}
+        if not args.no_prefill:
+            # the chunked-prefill layer: 64 evenly spaced query rows (first and
+            # last included), each absorb + fp64 scoring of its causal prefix +
+            # top-k; extrapolated to the chunk's 4096 rows
+            pf = synth.make_prefill("prefill", 5, N=N // 2, Qn=4096, r=256, H=H, d=d, G=1, k=k)
+            rows = sorted(set(np.linspace(0, pf.Q - 1, 64).round().astype(int).tolist()))
+            t0 = time.perf_counter()
+            oracle.full_layer(pf.q[0], pf.W[0], pf.w[0], pf.latent, pf.qseq, pf.qpos, pf.lens, pf.k, rows)
+            el_p = time.perf_counter() - t0
+            pairs_s = sum(min(int(pf.qpos[i]) + 1, int(pf.lens[0])) for i in rows)
+            pairs_all = sum(min(int(p_) + 1, int(pf.lens[0])) for p_ in pf.qpos)
+            cpu["prefill"] = {"value": round(pairs_s / el_p, 1), "unit": "query-row pairs scored/s",
+                              "extrapolated_ms_per_layer": round(el_p * pairs_all / pairs_s * 1e3, 1),
+                              "extrapolated": True, "cores": oracle.num_threads(), "kind": "oracle",
+                              "sample": f"{len(rows)} of {pf.Q} query rows (evenly spaced, first and last included) "
+                                        f"of one chunked-prefill layer ({pf.Q} queries at positions "
+                                        f"{int(pf.qpos[0])}..{int(pf.qpos[-1])} of a {int(pf.lens[0])}-row cache): "
+                                        f"{el_p:.1f} s; the layer time is that x {pairs_all}/{pairs_s} valid pairs"}
+            del pf
         log(f"cpu baseline {cpu}")
 
     # ------------------------------------------------------------------
