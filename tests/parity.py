@@ -2,8 +2,11 @@
 
 Scores (fp32 accumulation on the GPU, fp64 in the oracle): for query row q
 let rho = RMS of the oracle's scores over the valid rows; every valid score
-must satisfy |g - o| <= 1e-2 * max(|o|, rho).  The floor keeps exact-zero
-scores (a row whose every head is cut by the ReLU) well defined.
+must satisfy |g - o| <= 1e-2 * max(|o|, f rho), f = 1 in general and 1e-3
+for layers of at least 32 heads whose head weights are all non-negative.  The floor keeps
+exact-zero scores (a row whose every head is cut by the ReLU) well defined;
+with mixed-sign weights, heads can cancel a score to near zero, which only
+an absolute bound can judge.
 
 Top-k sets: the GPU set has the right size, no duplicates and only valid
 positions; every position the oracle picked that the GPU left out, and every
@@ -25,22 +28,37 @@ def rms(x: np.ndarray) -> float:
     return float(np.sqrt(np.mean(x * x))) if x.size else 0.0
 
 
-def check_scores(g: np.ndarray, o: np.ndarray, what: str = "scores") -> float:
-    """Assert the score rule; returns the worst |g - o| / max(|o|, rho)."""
+# Stricter floor for layers of many heads whose head weights are all
+# non-negative: there every head adds a non-negative term, a score is small
+# only when every head is small, and its error stays relative to it; the
+# RMS floor then only covers near-zero scores (every head cut or nearly so
+# by the ReLU).
+STRICT_FLOOR = 1e-3
+
+
+def check_scores(g: np.ndarray, o: np.ndarray, what: str = "scores", floor_frac: float = 1.0) -> float:
+    """Assert |g - o| <= 1e-2 max(|o|, floor_frac rho) for every row; returns
+    the worst purely relative error |g - o| / |o| over the rows with
+    |o| >= 1e-3 rho (reported by the tests).  floor_frac = 1 is the general
+    rule (mixed-sign head weights can cancel a score to near zero, where only
+    an absolute bound is meaningful); STRICT_FLOOR is used for non-negative
+    head weights."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     assert g.shape == o.shape, (what, g.shape, o.shape)
     if o.size == 0:
         return 0.0
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU scores"
-    floor = max(rms(o), 1e-30)
-    den = np.maximum(np.abs(o), floor)
+    rho = max(rms(o), 1e-30)
+    den = np.maximum(np.abs(o), floor_frac * rho)
     err = np.abs(g - o) / den
     worst = float(err.max())
     if worst > REL_TOL:
         i = int(err.argmax())
-        raise AssertionError(f"{what}: row {i} gpu={g[i]!r} oracle={o[i]!r} rel={worst:.3e} > {REL_TOL}")
-    return worst
+        raise AssertionError(f"{what}: row {i} gpu={g[i]!r} oracle={o[i]!r} rel={worst:.3e} > {REL_TOL} "
+                             f"(floor {floor_frac:g} x RMS)")
+    big = np.abs(o) >= STRICT_FLOOR * rho
+    return float((np.abs(g - o)[big] / np.abs(o[big])).max()) if big.any() else 0.0
 
 
 def check_topk(gsel: np.ndarray, gcount: int, oracle_sel: np.ndarray, o_scores_by_pos: dict | np.ndarray,
