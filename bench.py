@@ -736,7 +736,7 @@ def model_step(B, dev, i32, capture, time_graph, reps):
             "layer_map_g8": "layer 0 independent + 7 groups of 8 + 1 group of 4, otherwise the same",
             "per_step_g8": res8,
             "context_from_the_pages": "HS 2.30-2.72x over native DSA decode indexer time across 8K-128K, measured "
-                                      "on eight GPUs with tensor parallelism 8 (another machine; context only)"}
+                                      "by the pages on 8 GPUs (TP = 8; another machine; context only)"}
 
 
 def cpu_model() -> str:

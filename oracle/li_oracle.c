@@ -285,8 +285,9 @@ void lio_score_fp8(const uint8_t *qc, const float *qs, const double *w, const do
 }
 
 /*
- * RoPE-compatible structured decoder (§A.2, §A.4, §A.3; §3.1: the RoPE and
- * NoPE branches are concatenated and cached once per group).
+ * RoPE-compatible structured decoder (§A.2, §A.4, §A.3; §3.1: one latent
+ * row holds the rotary part followed by the NoPE part, and the group keeps
+ * a single copy of it).
  *
  * Latent row layout: the first 2*S*F elements are S shared complex sources
  * for each of F rotary frequencies, stored as (re, im) pairs; pair j holds

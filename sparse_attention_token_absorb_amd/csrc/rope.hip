@@ -5,8 +5,8 @@
 // is rotated once, when it is cached, and each layer's decoder is absorbed
 // into its post-RoPE query; §A.4: per rotary frequency, layer-specific
 // complex decoder coefficients over shared complex sources; §A.3: a dense
-// NoPE decoder with an output bias; §3.1: the RoPE and NoPE branches are
-// concatenated and cached once per group.
+// NoPE decoder with an output bias; §3.1: a latent row is its rotary part
+// followed by its NoPE part, kept once for the whole group.
 //
 //   append   rotary pair j of a row at position p turns by p * theta_(j % F)
 //            (fp64), the row is rounded once to the pool dtype;

@@ -7,7 +7,7 @@ the two sides share.
 
 Workload shapes follow the LatentIndex paper (paperlayer.ai summary):
   * a layer group of G = 4 layers with one shared latent cache (§3.1, §4.1);
-  * up to 2048 selected tokens per query (§4.1), HS candidate budget 8192
+  * a top-k budget of k = 2048 rows per query (§4.1), HS candidate budget 8192
     (§C.4), decode contexts of 8K-128K (§4.5);
   * an indexer with 64 heads of width 128 over a 256-wide latent.
 The pages print no dataset items or worked inputs; every value here is drawn

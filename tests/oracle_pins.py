@@ -3,8 +3,8 @@
 Each ``pin_*`` function raises AssertionError when the oracle disagrees with
 something the LatentIndex paper (paperlayer.ai summary of arXiv:2610.04635)
 or plain mathematics fixes: hand-derived worked examples (tests/golden/),
-the absorption identity (§3.1: exact for the effective keys in exact
-arithmetic), special cases that reduce to a textbook dot product or a
+the absorption identity (§3.1: scores from the absorbed query equal scores
+through the explicitly decoded keys, up to rounding), special cases that reduce to a textbook dot product or a
 library sort, brute-force selection on tiny inputs, the HS reductions named
 for the method (M >= n gives full LatentIndex, M = k gives index reuse) and
 the closed forms of §3.4/§B.1/§B.3.
