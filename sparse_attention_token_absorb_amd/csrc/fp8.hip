@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kSeg = 128;               // elements per quantization segment
 constexpr int kGatherTilesF8 = 16;      // max tiles per wave in gather mode
-constexpr int kMaxTilesPerWaveF8 = 64;  // max tiles per wave in contiguous mode (one page id per lane)
+constexpr int kMaxTilesPerWaveF8 = 16;  // max tiles per wave in contiguous mode (their scores stay in LDS)
 
 // 2^k as an fp32 (k in [-126, 127]).
 __device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
@@ -421,6 +421,9 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     constexpr int CH = R / 16;                 // 16-byte pieces per row
     constexpr int KS = R / 64;                 // MFMA k-steps
     constexpr int MAXT = GATHER ? kGatherTilesF8 : kMaxTilesPerWaveF8; // tiles per wave (scores kept in LDS)
+    static_assert(4 * NB * SLOT + (GATHER ? 4 * kGatherTilesF8 * kTile * 4 : 0) + kHistBins * 4 +
+                          4 * MAXT * kTile * 4 <= 160 * 1024,
+                  "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[4 * NB * SLOT];
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTilesF8 * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
@@ -435,41 +438,6 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     const int nt_max =
         first < a.max_rows ? (int)min64(tiles_per_wave, (a.max_rows - first + 4 * kTile - 1) / (4 * kTile)) : 0;
 
-    // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
-    // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
-    i32x8 qa[HB][KS];
-    int sa[HB][NSEG];
-    float wr[HB][16];
-    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
-    {
-        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
-        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const int h = hb * 32 + (lane & 31);
-            const int hc = h < a.H ? h : a.H - 1;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
-                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
-                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                if (h >= a.H) {
-                    i32x8 z = {};
-                    v = z;
-                }
-                qa[hb][s] = v;
-            }
-#pragma unroll
-            for (int g = 0; g < NSEG; ++g)
-                sa[hb][g] = h < a.H ? (int)((__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu) : 127;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                wr[hb][r] = hh < a.H ? a.w[(int64_t)q * a.H + hh] : 0.0f;
-                br[hb][r] = a.bias && hh < a.H ? a.bias[(int64_t)q * a.H + hh] : 0.0f;
-            }
-        }
-    }
     // Contiguous mode: lane i holds the page id of this wave's tile i (at
     // most 64 tiles per wave); query q usually sits in sequence q, so that
     // block-table row is requested before the sequence id arrives.
@@ -549,6 +517,51 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     const int npro = min(NB - 1, nt_max);
     for (int i = 0; i < npro; ++i) issue(i);
 
+    // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
+    // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
+    // Loaded after the first tiles are in flight: its loads then overlap
+    // theirs instead of delaying their issue.
+    i32x8 qa[HB][KS];
+    int sa[HB][NSEG];
+    float wr[HB][16];
+    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
+    {
+        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
+        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const int hc = h < a.H ? h : a.H - 1;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
+                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
+                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (h >= a.H) {
+                    i32x8 z = {};
+                    v = z;
+                }
+                qa[hb][s] = v;
+            }
+            // every load is unconditional (indices clamped into the query),
+            // so they are all in flight together; heads past H are zeroed after
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g) {
+                const uint32_t e = (__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu;
+                sa[hb][g] = h < a.H ? (int)e : 127;
+            }
+            const float *wq = a.w + (int64_t)q * a.H;
+            const float *bq = a.bias ? a.bias + (int64_t)q * a.H : a.w + (int64_t)q * a.H;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int hcl = hh < a.H ? hh : a.H - 1;
+                const float wv_ = wq[hcl], bv_ = bq[hcl];
+                wr[hb][r] = hh < a.H ? wv_ : 0.0f;
+                br[hb][r] = a.bias && hh < a.H ? bv_ : 0.0f;
+            }
+        }
+    }
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     if (row0 >= n) {
         wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
@@ -815,8 +828,11 @@ template <int R, int HB>
 hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
                                hipStream_t s)
 {
-    // ring next to the histogram and the staged scores: 3 slots at r = 256, 5 at r = 128
-    constexpr int NB = R == 256 ? 3 : 5;
+    // ring next to the histogram, the staged scores (16 tiles per wave) and,
+    // in gather mode, the row table: 4 slots at r = 256 (3 in gather mode),
+    // 7 at r = 128
+    constexpr int NB = R == 256 ? 4 : 7;
+    constexpr int NBG = R == 256 ? 3 : 7;
     const int64_t tiles = (max_rows + kTile - 1) / kTile;
     const int64_t per_q = (256 + a.Q - 1) / a.Q;
     int64_t tpw = (tiles + 4 * per_q - 1) / (4 * per_q);
@@ -825,7 +841,7 @@ hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int
     if (!a.cand && tpw > kMaxTilesPerWaveF8) tpw = kMaxTilesPerWaveF8;
     const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
     if (a.cand)
-        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NB, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NBG, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
                            pool_scales, qscale_off, (int)tpw);
     else if (a.stream_nt)
         hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
