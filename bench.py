@@ -60,10 +60,10 @@ def parse():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the roofline kernel's cold launches (a 1 GiB scrub before each), for a rocprofv3 "
                          "kernel trace whose average duration is the line's roofline figure; prints their timing")
-    ap.add_argument("--counters", choices=("decode", "prefill"), default=None,
+    ap.add_argument("--counters", choices=("decode", "prefill", "prefill-fp8"), default=None,
                     help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
-                         "then a plain 1 GiB copy whose counter readings scale the others to bytes; 'prefill' runs "
-                         "a few eager chunked-prefill layers")
+                         "then a plain 1 GiB copy whose counter readings scale the others to bytes; 'prefill' "
+                         "('prefill-fp8') runs a few eager chunked-prefill layers on a bf16 (FP8) cache")
     return ap.parse_args()
 
 
@@ -91,12 +91,12 @@ def main() -> int:
     def tdev(x, dt):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dt).to(dev)
 
-    if args.counters == "prefill":
-        pl = setup_prefill(B, synth, dev, bf, i32, tdev, args.context // 2)
+    if args.counters in ("prefill", "prefill-fp8"):
+        pl = setup_prefill(B, synth, dev, bf, i32, tdev, args.context // 2, fp8=args.counters == "prefill-fp8")
         for _ in range(3):
             pl.layer()
         torch.cuda.synchronize()
-        log("counter pass done: 3 chunked-prefill layers")
+        log(f"counter pass done: 3 chunked-prefill layers ({args.counters})")
         return 0
 
     # ------------------------------------------------------------------
