@@ -379,7 +379,7 @@ __device__ __forceinline__ bool digit_level(const Src &src, int m, uint32_t &pre
 // left equal on all 32 bits are taken in element order, so two calls over
 // the same elements with budgets a <= b take nested sets.
 template <int T, class Src, int U = 8>
-__device__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
+__device__ __forceinline__ void finish_levels(const Src &src, int m, uint32_t prefix, uint32_t pmask, uint32_t remaining,
                               int32_t *out, int cap, Scratch<T> &sh)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;

@@ -111,6 +111,7 @@ class IndexerModel:
                                   scores=f32(Q, nv) if keep_scores else None) for _ in lmap.groups]
         self.out_follower = [B.TopK(i32(Q, self.k), i32(Q), scores=f32(Q, self.M) if keep_scores else None)
                              for _ in range(lmap.n_layers)]
+        self._have_cand = [False] * len(lmap.groups)
 
     # -- one layer's pieces ------------------------------------------------
     def _native(self, l: int, seq, pos, max_valid, new_key, new_seq, new_pos) -> B.TopK:
@@ -139,6 +140,13 @@ class IndexerModel:
         appends first, at (new_seq, new_pos).  Returns each layer's selection
         (for an HS anchor its nested top-k; for an index-reuse follower the
         anchor's selection object itself).
+
+        Under "hs", when max_valid <= M every query's candidate budget
+        min(M, n) covers its whole prefix, so the candidates are every valid
+        row and hierarchical selection is full LatentIndex on the group
+        (§3.2): the group then runs as "latentindex" (same selections, no
+        candidate list; candidates() refuses until an "hs" step with
+        max_valid > M).
         """
         if method not in METHODS:
             raise ValueError(f"method must be one of {METHODS}")
@@ -164,9 +172,12 @@ class IndexerModel:
             lat = self.latents[gi]
             if gi in nl:
                 B.append_latent(lat, nl[gi], new_seq, new_pos)
+            full = method == "latentindex" or mv <= self.M
+            if method == "hs":
+                self._have_cand[gi] = not full
             for j, l in enumerate(layers):
                 self._absorb(l)
-                if method == "latentindex":
+                if full:
                     B.score_topk(lat, seq, pos, mv, self.q_lat[l], self.w[l], self.k, ws=self.ws, out=self.out[l])
                     sel[l] = self.out[l]
                 elif j == 0:
@@ -182,5 +193,9 @@ class IndexerModel:
         return sel
 
     def candidates(self, group: int) -> B.TopK:
-        """The HS anchor's top-M candidates of group `group` (after an "hs" step)."""
+        """The HS anchor's top-M candidates of group `group` (after an "hs"
+        step whose max_valid exceeded M; with a smaller bound the candidates
+        were every valid row and no list was made)."""
+        if not self._have_cand[group]:
+            raise ValueError("no candidate list: the last hs step's budget M covered every row, or none ran")
         return self.out_anchor[group]

@@ -287,3 +287,33 @@ def test_small_model_maps_and_scored_positions():
             say(f"map {lmap.group_sizes()} {method}: rows scored per query {list(total)}")
         del m
         torch.cuda.empty_cache()
+
+
+def test_hs_with_budget_covering_every_row_runs_as_full_latentindex():
+    """When max_valid <= M every candidate set is the whole prefix, so HS is
+    full LatentIndex on the group (§3.2, §C.4): the step's selections equal
+    the full method's and the oracle's, and no candidate list is claimed."""
+    h = _gpu()
+    g = synth.make_decode("model-covered", 84, B=2, lens=[1500, 900], r=256, H=64, d=128, k=256, M=2048, G=4,
+                          keys_a=True)
+    lmap = LayerMap(4, (), ((0, 1, 2, 3),))
+    m, qs = _model(h, g, lmap)
+    assert qs.max_valid <= g.M
+    om = OracleModel(g, False)
+    full = m.step("latentindex", qs.seq, qs.pos)
+    torch.cuda.synchronize()
+    want = {l: (full[l].idx.cpu().numpy().copy(), full[l].count.cpu().numpy().copy()) for l in range(4)}
+    _poison(m)
+    sel = m.step("hs", qs.seq, qs.pos)
+    torch.cuda.synchronize()
+    _verify(m, g, om, "latentindex", sel)
+    for l in range(4):
+        gi, gc = sel[l].idx.cpu().numpy(), sel[l].count.cpu().numpy()
+        assert np.array_equal(gc, want[l][1])
+        for i in range(g.Q):
+            assert set(gi[i, :gc[i]].tolist()) == set(want[l][0][i, :gc[i]].tolist()), (l, i)
+    with pytest.raises(ValueError):
+        m.candidates(0)
+    _, groups = _rows_scored(m, "latentindex", sel)
+    n = [om._n(i) for i in range(g.Q)]
+    assert list(groups[0]) == [oracle.rows_scored_hs(x, min(g.M, x), 4) for x in n]
