@@ -714,6 +714,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
     const uint8_t *pool = (const uint8_t *)a.pool;
     const int nr = lane & 31, gk = lane >> 5;
+    // Per-lane parts of every tile's addresses, the same for every tile:
+    // byte offsets of this lane's DMA sources inside a tile's codes and
+    // scales, and LDS offsets (inside a slot) of its MFMA B fragments (rows
+    // swizzled across the 16-byte columns) and of its row's scales.
+    uint32_t src_off[NIW];
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+        const int p = (wv * NIW + j) * 64 + lane;
+        const int rr = p / CH, cs = p % CH;
+        src_off[j] = (uint32_t)(rr * R + (cs ^ (rr % CH)) * 16);
+    }
+    uint32_t sc_src_off;
+    {
+        const int f = wv * 16 + (lane & 15);
+        const int row = f / NSEG < kTile ? f / NSEG : kTile - 1;
+        sc_src_off = (uint32_t)((row * NSEG + f % NSEG) * 4);
+    }
+    uint32_t rd_off[KS][2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c = 4 * s + 2 * gk;
+        rd_off[s][0] = (uint32_t)((nr * CH + (c ^ (nr % CH))) * 16);
+        rd_off[s][1] = (uint32_t)((nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+    }
+    uint32_t sc_rd_off[NSEG];
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g) sc_rd_off[g] = (uint32_t)(CODE_BYTES + (nr * NSEG + g) * 4);
 
 #pragma unroll 1
     for (int u = 0; u < 4; ++u) {
@@ -738,39 +765,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int pi = threadIdx.x; pi < np; pi += 256)
             s_page[pi] = clamp_index(a.bt[(int64_t)b * a.max_pages + p0 + pi], a.num_pages);
         __syncthreads();
-        auto page_of = [&](int i) { return s_page[((ts + i) >> 1) - p0]; };
-        auto issue = [&](int i, int page) {
-            const int64_t base = (int64_t)page * kPage + ((ts + i) & 1) * kTile; // first slot of the tile
-            lds_u8 *slot = ring + (i % NBUF) * SLOT;
+        // page ids are wave-uniform: read once into scalar registers
+        auto page_of = [&](int i) { return __builtin_amdgcn_readfirstlane(s_page[((ts + i) >> 1) - p0]); };
+        auto issue = [&](int i, int page, int slot_idx) {
+            const int64_t base = (int64_t)page * kPage + ((ts + i) & 1) * kTile; // first row of the tile
+            const uint8_t *gcode = pool + base * R;
+            const uint8_t *gscale = (const uint8_t *)(pool_scales + base * NSEG);
+            lds_u8 *slot = ring + slot_idx * SLOT;
 #pragma unroll
-            for (int j = 0; j < NIW; ++j) {
-                const int ii = wv * NIW + j;
-                const int p = ii * 64 + lane;
-                const int rr = p / CH, cs = p % CH;
-                const int c = cs ^ (rr % CH);
-                dma16(pool + (base + rr) * R + c * 16, slot + ii * 1024);
-            }
+            for (int j = 0; j < NIW; ++j) dma16s(gcode, src_off[j], slot + (wv * NIW + j) * 1024);
             // scales: this wave's quarter (16 lanes x 4 bytes) of the tile's 32 x NSEG
-            const int f = wv * 16 + (lane & 15);
-            const int row = f / NSEG < kTile ? f / NSEG : kTile - 1;
-            if (lane < 16) dma4(pool_scales + (base + row) * NSEG + (f % NSEG), slot + CODE_BYTES + wv * 64);
+            if (lane < 16) dma4s(gscale, sc_src_off, slot + CODE_BYTES + wv * 64);
         };
-        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i));
-#pragma unroll 1
-        for (int i = 0; i < nt; ++i) {
+        // One tile; its ring slot SL (and that of the tile issued in its
+        // place) is a compile-time constant, so every LDS address below is a
+        // fixed per-lane offset plus an immediate.
+        auto tile = [&](auto SLc, int i) {
+            constexpr int SL = decltype(SLc)::value;
+            constexpr int NX = (SL + NBUF - 1) % NBUF; // slot of tile i + NBUF - 1 (tile i-1's)
             const int inext = i + NBUF - 1;
             const int pnext = inext < nt ? page_of(inext) : 0; // read before the barrier
             // tile i landed (this wave's part), tiles i+1..i+NBUF-2 may still fly
             wait_after<NIW + 1, NBUF - 2>(min(NBUF - 2, nt - 1 - i));
             wg_barrier(); // every part of tile i landed; every wave is done with tile i-1
-            if (inext < nt) issue(inext, pnext); // into tile i-1's slot
+            if (inext < nt) issue(inext, pnext, NX);
             if (active) {
-                const lds_u8 *slot = ring + (i % NBUF) * SLOT;
+                const lds_u8 *slot = ring + SL * SLOT;
                 int scb[NSEG];
 #pragma unroll
                 for (int g = 0; g < NSEG; ++g)
-                    scb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + CODE_BYTES +
-                                                                                       (nr * NSEG + g) * 4) >> 23) &
+                    scb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + sc_rd_off[g]) >> 23) &
                                    0xFFu);
                 // accumulators start from the heads' biases, or (no bias) the
                 // first step adds to a constant zero
@@ -781,9 +805,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    const int c = 4 * s + 2 * gk;
-                    const u32x4 lo = *(const lds_u32x4 *)(slot + (nr * CH + (c ^ (nr % CH))) * 16);
-                    const u32x4 hi = *(const lds_u32x4 *)(slot + (nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+                    const u32x4 lo = *(const lds_u32x4 *)(slot + rd_off[s][0]);
+                    const u32x4 hi = *(const lds_u32x4 *)(slot + rd_off[s][1]);
                     const i32x8 bv = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     const int g = (s * 64) / kSeg;
@@ -798,7 +821,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 const int j = (ts + i) * kTile + lane;
                 if (lane < 32 && j < my_n) out[j] = pv;
             }
-        }
+        };
+        for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i), i);
+#pragma unroll 1
+        for (int i0 = 0; i0 < nt; i0 += NBUF)
+            static_for<NBUF>([&](auto SLc) {
+                const int i = i0 + decltype(SLc)::value;
+                if (i < nt) tile(SLc, i);
+            });
     }
 }
 

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "li_common.hpp"
 #include "li_internal.hpp"
 
@@ -133,7 +136,6 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n)
     }
 }
 
-// Absorbed-query fragments (MFMA A operand) and per-lane head weights.
 // 4 bytes per lane from global memory straight into LDS at
 // lds_uniform + lane * 4 (global_load_lds_dword), issued like dma16.
 __device__ __forceinline__ void dma4(const void *g, lds_u8 *lds_uniform)
@@ -148,6 +150,62 @@ __device__ __forceinline__ void dma4(const void *g, lds_u8 *lds_uniform)
                  "s_mov_b32 m0, %[sv]"
                  : [sv] "=&s"(saved)
                  : [addr] "v"(g), [lds] "s"(lds)
+                 : "memory");
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1 in order: a loop
+// whose index is a compile-time constant in its body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A wave-uniform address held in an SGPR pair.
+__device__ __forceinline__ uint64_t uniform_addr(const void *p)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a) |
+           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32);
+}
+
+// dma16 and dma4 from a wave-uniform base address plus a per-lane 32-bit
+// byte offset: the load unit forms each lane's address, so a caller whose
+// lane offsets are fixed spends no vector instructions on addresses.
+__device__ __forceinline__ void dma16s(const void *base_uniform, uint32_t off, lds_u8 *lds_uniform)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    const uint64_t b = uniform_addr(base_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %[off], %[base]\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [off] "v"(off), [base] "s"(b), [lds] "s"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ void dma4s(const void *base_uniform, uint32_t off, lds_u8 *lds_uniform)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
+    const uint64_t b = uniform_addr(base_uniform);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_mov_b32 m0, %[lds]\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dword %[off], %[base]\n\t"
+                 "s_nop 0\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [off] "v"(off), [base] "s"(b), [lds] "s"(lds)
                  : "memory");
 }
 
