@@ -145,16 +145,9 @@ def test_fp8_decode_8k_full_layers():
         verify_fp8_full(h, g, l, out, codes=codes, tag="fp8-8k")
 
 
-def test_fp8_ragged_paged_full_and_hs():
-    h = _gpu()
-    say("fp8 ragged paged: full + HS")
-    g = synth.make_decode("f8rag", 61, B=5, lens=(3000, 20000), r=256, H=64, d=128, k=1024, M=4096)
-    cache = fp8_cache(h, g)
-    qs = h.Queries(g)
-    codes = oracle_codes(g)
-    _, out = fp8_layer(h, g, cache, qs, 1)
-    verify_fp8_full(h, g, 1, out, codes=codes, tag="fp8-rag")
-    # HS: the anchor's top-M with its own top-k nested, then every follower
+def verify_fp8_hs(h, g, cache, qs, codes, tag):
+    """The anchor's top-M with its own top-k nested, then every follower
+    rescoring the anchor's candidates, against the oracle on the same codes."""
     fq0, anchor = fp8_layer(h, g, cache, qs, 0, k=g.M, k_inner=g.k)
     a_idx, a_cnt = h.host(anchor.idx), h.host(anchor.count)
     a_in, a_in_cnt = h.host(anchor.idx_inner), h.host(anchor.count_inner)
@@ -172,16 +165,49 @@ def test_fp8_ragged_paged_full_and_hs():
             cc, cs = codes[b]
             if l == 1:
                 s0 = oracle.score_fp8(oq0[i], oqs0[i], g.w[0][i], cc, cs, n=n)
-                check_topk(a_idx[i], int(a_cnt[i]), oracle.topk(s0, Me), s0, None, Me, rms(s0), f"fp8 anchor q{i}")
+                check_topk(a_idx[i], int(a_cnt[i]), oracle.topk(s0, Me), s0, None, Me, rms(s0), f"{tag} anchor q{i}")
                 cand = a_idx[i, :Me].astype(np.int64)
                 sub = {int(p): s0[p] for p in cand}
                 check_topk(a_in[i], int(a_in_cnt[i]), oracle.topk(s0[cand], Ke, pos=cand), sub, cand, Ke, rms(s0),
-                           f"fp8 anchor nested q{i}")
+                           f"{tag} anchor nested q{i}")
             cand = a_idx[i, :Me].astype(np.int32)
             cs_l = oracle.score_fp8(oq[i], oqs[i], g.w[l][i], cc, cs, rows=cand)
-            check_scores(fs[i, :Me], cs_l, f"fp8 follower {l} q{i} scores")
+            check_scores(fs[i, :Me], cs_l, f"{tag} follower {l} q{i} scores")
             check_topk(fi[i], int(fc[i]), oracle.topk(cs_l, Ke, pos=cand), dict(zip(cand.tolist(), cs_l)), cand, Ke,
-                       rms(cs_l), f"fp8 follower {l} q{i} top-k")
+                       rms(cs_l), f"{tag} follower {l} q{i} top-k")
+
+
+def test_fp8_ragged_paged_full_and_hs():
+    h = _gpu()
+    say("fp8 ragged paged: full + HS")
+    g = synth.make_decode("f8rag", 61, B=5, lens=(3000, 20000), r=256, H=64, d=128, k=1024, M=4096)
+    cache = fp8_cache(h, g)
+    qs = h.Queries(g)
+    codes = oracle_codes(g)
+    _, out = fp8_layer(h, g, cache, qs, 1)
+    verify_fp8_full(h, g, 1, out, codes=codes, tag="fp8-rag")
+    verify_fp8_hs(h, g, cache, qs, codes, "fp8-rag")
+
+
+def test_fp8_long_context_b4_n131072_full_and_hs():
+    """The long-context workload (4 sequences of 131072 rows) on the FP8
+    cache, in the launch configuration the benchmark times: every layer's
+    full selection with every score, then the HS group (top-8192 anchor, 3
+    followers)."""
+    h = _gpu()
+    g = synth.long_context_b4()
+    say("fp8 long context B=4 N=131072: cache")
+    cache = fp8_cache(h, g)
+    qs = h.Queries(g)
+    codes = oracle_codes(g)
+    for l in range(g.G):
+        say(f"fp8 long context full layer {l}")
+        _, out = fp8_layer(h, g, cache, qs, l)
+        verify_fp8_full(h, g, l, out, codes=codes, tag="fp8-long")
+    say("fp8 long context HS M=8192")
+    verify_fp8_hs(h, g, cache, qs, codes, "fp8-long")
+    del cache
+    torch.cuda.empty_cache()
 
 
 def test_fp8_short_empty_and_r128():

@@ -225,6 +225,28 @@ def test_rope_decode_full_and_hs(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_rope_decode_long_context_b4_n131072(dtype):
+    """The long-context shape (4 sequences of 131072 rows) through the
+    structured decoder, in the launch configuration the benchmark times: a
+    rotated cache, one layer's absorbed query with its bias, every score and
+    the selection."""
+    h = _gpu()
+    rg = synth.make_rope(74)
+    g = synth.make_decode(f"rope-long-{dtype}", 74, B=4, lens=[131072] * 4, r=256, H=64, d=128, k=2048, M=8192)
+    say(f"long context {dtype}: cache")
+    cache = rope_cache(h, g, rg, dtype)
+    qs = h.Queries(g)
+    stored = _stored(g, rg, dtype)
+    qt, bias = layer_operands(h, g, rg, 2, fp8=(dtype == "fp8"))
+    say(f"long context {dtype}: full layer 2")
+    out = B.score_topk(cache, qs.seq, qs.pos, qs.max_valid, qt, h.head_weights(g, 2), g.k, keep_scores=True,
+                       bias=bias)
+    _verify(h, g, rg, 2, out, stored, dtype, tag=f"rope-long-{dtype}")
+    del cache
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_rope_prefill_sampled(dtype):
     """The chunked-prefill workload (4096 queries at the end of a 65536-row
     cache, 4 layers) through the structured decoder: 64 evenly spaced query
