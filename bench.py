@@ -645,7 +645,7 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "modes": modes, "roofline": roofline, "sweep": sweep, "workloads": workloads, "fp8": fp8, "rope": rope,
         "model": model,
-        "prefill": prefill, "cpu_baseline": cpu,
+        "prefill": prefill, "cpu_baseline": cpu, "device": device_facts(dev),
     }
     s = json.dumps(line)
     print(s, flush=True)
@@ -737,6 +737,17 @@ def model_step(B, dev, i32, capture, time_graph, reps):
             "per_step_g8": res8,
             "context_from_the_pages": "HS 2.30-2.72x over native DSA decode indexer time across 8K-128K, measured "
                                       "by the pages on 8 GPUs (TP = 8; another machine; context only)"}
+
+
+def device_facts(dev) -> dict:
+    """What the runtime reports about the GPU, and the published peaks every
+    fraction in the line is taken against."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1), "l2_bytes": getattr(p, "L2_cache_size", None),
+            "peaks_used": {"hbm_GBs": HBM_PEAK_GBS, "bf16_dense_TFLOPs": BF16_PEAK_TFLOPS,
+                           "fp8_dense_TFLOPs": FP8_PEAK_TFLOPS}}
 
 
 def cpu_model() -> str:

@@ -239,6 +239,25 @@ def test_long_context_b4_n131072_all_three_ways():
         del kc
 
 
+@pytest.mark.parametrize("seed", [40, 400])
+def test_long_context_b4_n131072_other_requests(seed):
+    """The timing protocol of the LatentIndex summary page (§C.4) runs three
+    requests per method and length; the long-context workload's other two
+    seeded requests: one full LatentIndex layer (every score) and the HS
+    group (anchor top-8192 with its nested top-2048, 3 followers)."""
+    h = H()
+    g = synth.long_context_b4(seed=seed, keys_a=False)
+    say(f"long context seed {seed}: cache")
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    verify_full(g, 1, h.full_layer(g, cache, qs, 1), tag=f"long context seed {seed} (b)")
+    say(f"long context seed {seed}: HS M=8192")
+    anchor, followers = h.hs_group(g, cache, qs)
+    verify_hs(g, anchor, followers, tag=f"long context seed {seed} (c)")
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_chunked_prefill_q4096_sampled_rows():
     h = H()
     g = synth.chunked_prefill_q4096()
