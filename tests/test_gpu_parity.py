@@ -160,6 +160,29 @@ def test_tiny_fp32_n512_full_and_hs():
     verify_hs(g, anchor, followers, tag="tiny fp32")
 
 
+def test_tiny_n512_through_the_bf16_kernels():
+    """The tiny configuration's cache is fp32 and runs on the fp32 kernel;
+    its inputs rounded once to bf16 also run through the bf16 MFMA kernels
+    (the register-staged one scores its contiguous r = 64 prefix, the LDS
+    ring the HS followers' gathered rows), against the oracle on the same
+    rounded values."""
+    import dataclasses
+    h = H()
+    g0 = synth.tiny_fp32_n512()
+    rb = synth.round_bf16
+    g = dataclasses.replace(g0, name=g0.name + "-bf16", dtype="bf16", latent=[rb(x) for x in g0.latent],
+                            q=[rb(x) for x in g0.q], W=[rb(x) for x in g0.W])
+    say("tiny N=512 on bf16 copies: cache")
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    for l in range(g.G):
+        say(f"tiny bf16 full layer {l}")
+        verify_full(g, l, h.full_layer(g, cache, qs, l), tag="tiny bf16")
+    say("tiny bf16 HS")
+    anchor, followers = h.hs_group(g, cache, qs)
+    verify_hs(g, anchor, followers, tag="tiny bf16")
+
+
 def test_decode_b1_n8192_bf16():
     h = H()
     g = synth.decode_b1_n8192()
