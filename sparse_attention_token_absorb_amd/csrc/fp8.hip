@@ -405,7 +405,11 @@ __global__ __launch_bounds__(256) void k_absorb_fp8_row(const u16 *q, const u16 
 // each the tile's codes (32 rows x R bytes, 16-byte pieces XOR-swizzled by
 // row) plus its rows' segment scales.  The query's codes are MFMA A
 // fragments for the whole stream; the tile is the B operand; both scales
-// enter as E8M0 exponents of v_mfma_scale_f32_32x32x64_f8f6f4.
+// enter as E8M0 exponents of v_mfma_scale_f32_32x32x64_f8f6f4.  With one
+// wave per SIMD, the vector work of a tile delays the next DMA issue: over
+// contiguous prefixes the DMA takes a scalar base plus fixed lane offsets,
+// and the tile loop is unrolled over the ring so that every LDS address is
+// a fixed lane offset plus an immediate.
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -487,9 +491,22 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
                 s_row[(wv * kGatherTilesF8 + i) * kTile + lane] = clamp_page(page[i]) * kPage + (pos[i] & 63);
         wait_lds();
     }
+    uint32_t src_off[NIC];
+#pragma unroll
+    for (int ii = 0; ii < NIC; ++ii) {
+        const int p = ii * 64 + lane;
+        const int nr = p / CH, cs = p % CH;
+        src_off[ii] = (uint32_t)(nr * R + (cs ^ (nr % CH)) * 16);
+    }
+    uint32_t sc_src_off;
+    {
+        int sl = lane / NSEG;
+        sl = sl < kTile ? sl : kTile - 1;
+        sc_src_off = (uint32_t)((sl * NSEG + lane % NSEG) * 4);
+    }
     // tile i -> slot (i % NB): the codes, then the scales of its 32 rows
-    auto issue = [&](int i) {
-        lds_u8 *slot = ring + (i % NB) * SLOT;
+    auto issue = [&](int i, int slot_idx) {
+        lds_u8 *slot = ring + slot_idx * SLOT;
         const __attribute__((address_space(3))) int32_t *rows =
             (const __attribute__((address_space(3))) int32_t *)s_row + (wv * kGatherTilesF8 + i) * kTile;
         int64_t base = 0;
@@ -501,21 +518,27 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             if constexpr (GATHER) return (int64_t)rows[nr];
             else return base + nr;
         };
+        if constexpr (GATHER) {
 #pragma unroll
-        for (int ii = 0; ii < NIC; ++ii) {
-            const int p = ii * 64 + lane;
-            const int nr = p / CH, cs = p % CH;
-            const int c = cs ^ (nr % CH);
-            dma16p<NT>(pool + slot_of(nr) * R + c * 16, slot + ii * 1024);
+            for (int ii = 0; ii < NIC; ++ii) {
+                const int p = ii * 64 + lane;
+                const int nr = p / CH, cs = p % CH;
+                const int c = cs ^ (nr % CH);
+                dma16p<NT>(pool + slot_of(nr) * R + c * 16, slot + ii * 1024);
+            }
+            int sl = lane / NSEG;
+            sl = sl < kTile ? sl : kTile - 1;
+            dma4(pool_scales + slot_of(sl) * NSEG + (lane % NSEG), slot + CODE_BYTES);
+        } else {
+            const uint8_t *gcode = pool + base * R;
+            const uint8_t *gscale = (const uint8_t *)(pool_scales + base * NSEG);
+#pragma unroll
+            for (int ii = 0; ii < NIC; ++ii) dma16s<NT>(gcode, src_off[ii], slot + ii * 1024);
+            dma4s(gscale, sc_src_off, slot + CODE_BYTES);
         }
-        // scales: lane l carries (row l / NSEG, segment l % NSEG); lanes past
-        // the tile's 32 rows repeat its last row
-        int sl = lane / NSEG;
-        sl = sl < kTile ? sl : kTile - 1;
-        dma4(pool_scales + slot_of(sl) * NSEG + (lane % NSEG), slot + CODE_BYTES);
     };
     const int npro = min(NB - 1, nt_max);
-    for (int i = 0; i < npro; ++i) issue(i);
+    for (int i = 0; i < npro; ++i) issue(i, i);
 
     // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
     // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
@@ -575,13 +598,22 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     __attribute__((address_space(3))) float *const outw =
         (__attribute__((address_space(3))) float *)s_out + wv * kTile;
     const int nr = lane & 31, gk = lane >> 5;
-    for (int i = 0; i < nt; ++i) {
+    uint32_t rd_off[KS][2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c = 4 * s + 2 * gk;
+        rd_off[s][0] = (uint32_t)((nr * CH + (c ^ (nr % CH))) * 16);
+        rd_off[s][1] = (uint32_t)((nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+    }
+    auto tile = [&](auto SLc, int i) {
+        constexpr int SL = decltype(SLc)::value;
+        constexpr int NX = (SL + NB - 1) % NB;
         if (i + NB - 1 < nt) {
             wait_lds(); // this wave's reads of that slot (tile i-1) are complete
-            issue(i + NB - 1);
+            issue(i + NB - 1, NX);
         }
         wait_after<NIT, NB - 1>(min(NB - 1, nt - 1 - i));
-        const lds_u8 *slot = ring + (i % NB) * SLOT;
+        const lds_u8 *slot = ring + SL * SLOT;
         int sb[NSEG];
 #pragma unroll
         for (int g = 0; g < NSEG; ++g)
@@ -592,9 +624,8 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const int c = 4 * s + 2 * gk;
-            const u32x4 lo = *(const lds_u32x4 *)(slot + (nr * CH + (c ^ (nr % CH))) * 16);
-            const u32x4 hi = *(const lds_u32x4 *)(slot + (nr * CH + ((c + 1) ^ (nr % CH))) * 16);
+            const u32x4 lo = *(const lds_u32x4 *)(slot + rd_off[s][0]);
+            const u32x4 hi = *(const lds_u32x4 *)(slot + rd_off[s][1]);
             const i32x8 bv = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             const int g = (s * 64) / kSeg;
 #pragma unroll
@@ -604,7 +635,13 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         }
         const float p = epilogue<HB>(acc, wr);
         if (lane < 32 && tile_row0(i) + lane < n) outw[i * 4 * kTile + lane] = p; // local row (i * 4 + wv) * 32 + lane
-    }
+    };
+#pragma unroll 1
+    for (int i0 = 0; i0 < nt; i0 += NB)
+        static_for<NB>([&](auto SLc) {
+            const int i = i0 + decltype(SLc)::value;
+            if (i < nt) tile(SLc, i);
+        });
     wait_vmcnt<0>(); // tiles issued ahead of the row count and never used
     __syncthreads(); // every wave's scores are in LDS (and the histogram is cleared)
     // The scores leave in one coalesced pass over the workgroup's rows (score

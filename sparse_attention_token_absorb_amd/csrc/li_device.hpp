@@ -176,21 +176,35 @@ __device__ __forceinline__ uint64_t uniform_addr(const void *p)
 
 // dma16 and dma4 from a wave-uniform base address plus a per-lane 32-bit
 // byte offset: the load unit forms each lane's address, so a caller whose
-// lane offsets are fixed spends no vector instructions on addresses.
+// lane offsets are fixed spends no vector instructions on addresses.  NT:
+// the non-temporal policy of dma16_nt.
+template <bool NT = false>
 __device__ __forceinline__ void dma16s(const void *base_uniform, uint32_t off, lds_u8 *lds_uniform)
 {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_uniform);
     const uint64_t b = uniform_addr(base_uniform);
     uint32_t saved;
-    asm volatile("s_mov_b32 %[sv], m0\n\t"
-                 "s_mov_b32 m0, %[lds]\n\t"
-                 "s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %[off], %[base]\n\t"
-                 "s_nop 0\n\t"
-                 "s_mov_b32 m0, %[sv]"
-                 : [sv] "=&s"(saved)
-                 : [off] "v"(off), [base] "s"(b), [lds] "s"(lds)
-                 : "memory");
+    if constexpr (NT) {
+        asm volatile("s_mov_b32 %[sv], m0\n\t"
+                     "s_mov_b32 m0, %[lds]\n\t"
+                     "s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %[off], %[base] nt\n\t"
+                     "s_nop 0\n\t"
+                     "s_mov_b32 m0, %[sv]"
+                     : [sv] "=&s"(saved)
+                     : [off] "v"(off), [base] "s"(b), [lds] "s"(lds)
+                     : "memory");
+    } else {
+        asm volatile("s_mov_b32 %[sv], m0\n\t"
+                     "s_mov_b32 m0, %[lds]\n\t"
+                     "s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %[off], %[base]\n\t"
+                     "s_nop 0\n\t"
+                     "s_mov_b32 m0, %[sv]"
+                     : [sv] "=&s"(saved)
+                     : [off] "v"(off), [base] "s"(b), [lds] "s"(lds)
+                     : "memory");
+    }
 }
 
 __device__ __forceinline__ void dma4s(const void *base_uniform, uint32_t off, lds_u8 *lds_uniform)
