@@ -96,23 +96,6 @@ struct QueryRegs {
     }
 };
 
-// MFMA steps over the LDS buffer holding columns [S0*16, (S0+KS)*16) of a
-// 32-row tile, `CH` 16-byte pieces per buffer row.
-template <int R, int HB, int S0, int KS, int CH>
-__device__ __forceinline__ void mfma_steps(const lds_u8 *buf, const QueryRegs<R, HB> &qr, f32x16 (&acc)[HB])
-{
-    const int lane = threadIdx.x & 63;
-    const int nr = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int c = 2 * s + g;
-        const bf16x8 b = *(lds_bf16x8 *)(buf + (nr * CH + (c ^ (nr % CH))) * 16);
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][S0 + s], b, acc[hb], 0, 0, 0);
-    }
-}
-
 // All R/16 MFMA steps over one full-width tile in LDS, with the B fragments
 // read D steps ahead of their use so LDS latency hides behind the MFMAs.
 // ZC: the accumulators start from zero (the first step takes a constant 0
@@ -226,6 +209,10 @@ __device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const
 // NT: the latent rows are read with the non-temporal policy, for launches
 // that stream more than the last-level cache can keep (a pool read once
 // per launch gains nothing from allocating in it, and evicts everything else).
+// With one wave per SIMD, a chunk's vector work delays the next DMA issue:
+// over contiguous prefixes the DMA takes a scalar base plus fixed lane
+// offsets, and the chunk loop is unrolled over the ring (and the chunks of
+// a tile) so that every LDS address is a fixed lane offset plus an immediate.
 // ---------------------------------------------------------------------------
 template <int R, int HB, bool GATHER, int NB, int CPT, bool NT>
 __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per_wave)
@@ -324,6 +311,14 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
                 s_row[(wv * kGatherTiles + i) * kTile + lane] = clamp_page(page[i]) * kPage + (pos[i] & 63);
         wait_lds();
     }
+    // per-lane byte offsets of the DMA sources inside a chunk (contiguous mode)
+    uint32_t src_off[NIC];
+#pragma unroll
+    for (int j = 0; j < NIC; ++j) {
+        const int p = j * 64 + lane;
+        const int nr = p / CH, cs = p % CH;
+        src_off[j] = (uint32_t)((nr * R + (cs ^ (nr % CH)) * 8) * 2);
+    }
     auto issue = [&](int c) {
         const int i = c / CPT;
         lds_u8 *buf = ring + (c % NB) * CHUNK;
@@ -335,9 +330,9 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         } else {
             const int64_t t0 = tile_row0(i);
             const int page = __builtin_amdgcn_readlane(tile_page, i);
-            const int64_t base = ((int64_t)page * kPage + (t0 & 63)) * R;
-            issue_rows<R, CH, NIC, NT>(pool, [&](int nr) { return base + (int64_t)nr * R; }, (c % CPT) * WC, buf, 0,
-                                       NIC);
+            const u16 *gbase = pool + ((int64_t)page * kPage + (t0 & 63)) * R + (c % CPT) * WC;
+#pragma unroll
+            for (int j = 0; j < NIC; ++j) dma16s<NT>(gbase, src_off[j], buf + j * 1024);
         }
     };
     const int npro = min(NB - 1, CPT * nt_max);
@@ -364,27 +359,49 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     __attribute__((address_space(3))) float *const outw =
         (__attribute__((address_space(3))) float *)s_out + wv * kTile;
     f32x16 acc[HB];
-    for (int c = 0; c < nchunks; ++c) {
+    // LDS offsets of this lane's B fragments inside a chunk, one per k-step
+    uint32_t rd_off[KSH];
+    {
+        const int nr = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) rd_off[s] = (uint32_t)((nr * CH + ((2 * s + g) ^ (nr % CH))) * 16);
+    }
+    // chunk c of the stream; its ring slot and its place in the tile are
+    // compile-time constants (the loop runs UN chunks per round)
+    constexpr int UN = NB % CPT == 0 ? NB : NB * CPT;
+    auto chunk = [&](auto Uc, int c) {
+        constexpr int U = decltype(Uc)::value;
+        constexpr int SL = U % NB, PART = U % CPT;
         if (c + NB - 1 < nchunks) {
             wait_lds(); // this wave's reads of that buffer (chunk c-1) are complete
             issue(c + NB - 1);
         }
         wait_after<NIC, NB - 1>(min(NB - 1, nchunks - 1 - c));
-        const lds_u8 *buf = ring + (c % NB) * CHUNK;
-        if (CPT == 1 || c % CPT == 0) {
+        const lds_u8 *buf = ring + SL * CHUNK;
+        if constexpr (PART == 0) {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) acc[hb] = qr.b[hb];
-            mfma_steps<R, HB, 0, KSH, CH>(buf, qr, acc);
-        } else {
-            if constexpr (CPT == 2) mfma_steps<R, HB, KSH, KSH, CH>(buf, qr, acc);
         }
-        if (c % CPT == CPT - 1) {
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) {
+            const bf16x8 bfr = *(const lds_bf16x8 *)(buf + rd_off[s]);
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][PART * KSH + s], bfr, acc[hb], 0, 0, 0);
+        }
+        if constexpr (PART == CPT - 1) {
             const float p = epilogue<HB>(acc, qr.w);
             const int i = c / CPT;
             if (lane < 32 && tile_row0(i) + lane < n)
                 outw[i * 4 * kTile + lane] = p; // workgroup-local row (i * 4 + wv) * 32 + lane
         }
-    }
+    };
+#pragma unroll 1
+    for (int c0 = 0; c0 < nchunks; c0 += UN)
+        static_for<UN>([&](auto Uc) {
+            const int c = c0 + decltype(Uc)::value;
+            if (c < nchunks) chunk(Uc, c);
+        });
     wait_vmcnt<0>(); // chunks issued ahead of the row count and never used
     __syncthreads(); // every wave's scores are in LDS
     // The scores leave in one pass over the workgroup's rows, which also
