@@ -37,8 +37,12 @@ LIB_ASAN = os.path.join(BUILD_ASAN, "liblatentindex_asan.so")
 
 
 def _flags(variant=None):
+    # MFMA accumulators in VGPRs: the decode kernels' epilogue then reads them
+    # without a v_accvgpr_read per element (32 per tile), which a wave alone
+    # on its SIMD would otherwise spend before issuing its next loads.
     f = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
     if variant == "asan":
         f += ASAN_HOST

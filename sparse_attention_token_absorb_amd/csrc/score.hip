@@ -214,7 +214,7 @@ __device__ __forceinline__ int stage_query(const u16 *qt, const float *wq, const
 // offsets, and the chunk loop is unrolled over the ring (and the chunks of
 // a tile) so that every LDS address is a fixed lane offset plus an immediate.
 // ---------------------------------------------------------------------------
-template <int R, int HB, bool GATHER, int NB, int CPT, bool NT>
+template <int R, int HB, bool GATHER, int NB, int CPT, bool NT, bool BIAS>
 __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per_wave)
 {
     static_assert(CPT == 1 || CPT == 2, "chunks per tile");
@@ -378,7 +378,9 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         }
         wait_after<NIC, NB - 1>(min(NB - 1, nchunks - 1 - c));
         const lds_u8 *buf = ring + SL * CHUNK;
-        if constexpr (PART == 0) {
+        // a tile's accumulators start from the heads' biases, or (no bias)
+        // its first step adds to a constant zero
+        if constexpr (PART == 0 && BIAS) {
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) acc[hb] = qr.b[hb];
         }
@@ -386,8 +388,12 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
         for (int s = 0; s < KSH; ++s) {
             const bf16x8 bfr = *(const lds_bf16x8 *)(buf + rd_off[s]);
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb)
-                acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][PART * KSH + s], bfr, acc[hb], 0, 0, 0);
+            for (int hb = 0; hb < HB; ++hb) {
+                const f32x16 zero = {};
+                acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr.a[hb][PART * KSH + s], bfr,
+                                                                  !BIAS && PART == 0 && s == 0 ? zero : acc[hb], 0,
+                                                                  0, 0);
+            }
         }
         if constexpr (PART == CPT - 1) {
             const float p = epilogue<HB>(acc, qr.w);
@@ -859,15 +865,22 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     // chunk ring: 96 KiB next to the histogram and the staged scores
     constexpr int CPT = R == 256 ? 2 : 1;
     constexpr int NB = R == 64 ? 6 : 3;
-    if (a.cand)
-        hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
-                           a, (int)tpw);
-    else if (a.stream_nt)
-        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
-                           a, (int)tpw);
+    auto go = [&](auto BIASc) {
+        constexpr bool BI = decltype(BIASc)::value;
+        if (a.cand)
+            hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT, false, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
+                               0, s, a, (int)tpw);
+        else if (a.stream_nt)
+            hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, true, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
+                               0, s, a, (int)tpw);
+        else
+            hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, false, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
+                               0, s, a, (int)tpw);
+    };
+    if (a.bias)
+        go(std::true_type{});
     else
-        hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s,
-                           a, (int)tpw);
+        go(std::false_type{});
     return hipGetLastError();
 }
 
