@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kGatherTiles = 16; // max tiles per wave in gather mode (row offsets kept in LDS)
 constexpr int kMaxTilesPerWave = 64; // max tiles per wave of the contiguous LDS-ring decode kernel
+constexpr int kGatherBtLds = 4096;    // block-table row entries kept in LDS in gather mode (262144 rows)
 constexpr int kVrMaxTiles = 32;  // max tiles per wave of the register-staged decode kernel
 constexpr int kPrefillMaxTiles = 2048; // max tiles per prefill split (their page ids sit in LDS)
 
@@ -229,6 +230,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     __shared__ uint32_t s_hist[kHistBins];
     __shared__ float s_out[4 * MAXT * kTile];
     __shared__ int32_t s_pg[GATHER ? 1 : 4 * 64];
+    __shared__ int32_t s_bt[GATHER ? kGatherBtLds : 1];
     __shared__ float s_w[64];
     __shared__ float s_b[64];
 
@@ -258,6 +260,13 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     if constexpr (!GATHER) {
         const int pidx = (int)min64(tile_row0(lane < nt_max ? lane : 0) >> 6, a.max_pages - 1);
         dma4(a.bt + (int64_t)b_guess * a.max_pages + pidx, (lds_u8 *)(s_pg + wv * 64));
+    } else if (a.max_pages <= kGatherBtLds) {
+        // gather mode: the guessed sequence's whole block-table row, so that
+        // the candidates' page lookups read LDS instead of waiting on memory
+        for (int i = wv; i * 64 < a.max_pages; i += 4) {
+            const int pidx = min(i * 64 + lane, a.max_pages - 1);
+            dma4(a.bt + (int64_t)b_guess * a.max_pages + pidx, (lds_u8 *)(s_bt + i * 64));
+        }
     }
     lds_u8 *const ring_all = (lds_u8 *)ring_raw;
     const int staged = stage_query<R, HB, NB, CHUNK>((const u16 *)a.qt + (int64_t)q * a.H * R, a.w + (int64_t)q * a.H,
@@ -299,11 +308,23 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
                 pos[i] = a.cand[(int64_t)q * a.cand_ld + j];
             }
         }
+        if (b == b_guess && a.max_pages <= kGatherBtLds) { // uniform over the workgroup
+            // this wave's candidates have landed, and with them (vector loads
+            // complete in issue order) its part of the row; the barrier waits
+            // for the other waves' parts
+            wg_barrier();
 #pragma unroll
-        for (int i = 0; i < kGatherTiles; ++i) {
-            pos[i] = pos[i] < 0 ? 0 : (pos[i] > max_pos ? (int)max_pos : pos[i]);
-            page[i] = 0;
-            if (i < nt_max) page[i] = a.bt[(int64_t)b * a.max_pages + (pos[i] >> 6)];
+            for (int i = 0; i < kGatherTiles; ++i) {
+                pos[i] = pos[i] < 0 ? 0 : (pos[i] > max_pos ? (int)max_pos : pos[i]);
+                page[i] = i < nt_max ? ((const __attribute__((address_space(3))) int32_t *)s_bt)[pos[i] >> 6] : 0;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kGatherTiles; ++i) {
+                pos[i] = pos[i] < 0 ? 0 : (pos[i] > max_pos ? (int)max_pos : pos[i]);
+                page[i] = 0;
+                if (i < nt_max) page[i] = a.bt[(int64_t)b * a.max_pages + (pos[i] >> 6)];
+            }
         }
 #pragma unroll
         for (int i = 0; i < kGatherTiles; ++i)
