@@ -40,6 +40,12 @@
  *   - LI_ERR_HIP reports a failed launch (detail in li_last_error()).
  *   - Calls on different streams are independent; calls that share output
  *     or workspace buffers must be ordered by the caller.
+ *   - Two environment variables, read once per process, choose between
+ *     equivalent kernels (results are the same within rounding):
+ *     LI_DECODE_PATH=lds|vgpr forces the LDS-ring or the register-staged
+ *     decode scoring kernel; LI_STREAM_NT=0|1 forces the non-temporal read
+ *     policy of the decode latent stream off or on (default: on for
+ *     launches that read 128 MiB or more).
  */
 #ifndef LATENTINDEX_H
 #define LATENTINDEX_H
