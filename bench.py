@@ -274,7 +274,8 @@ def main() -> int:
     log(f"modes {modes}")
 
     # ------------------------------------------------------------------
-    # Roofline of the decode scoring kernel (HIP events around each launch)
+    # Roofline of the decode scoring kernel (HIP events bound to each launch's
+    # kernel start and end on its launch stream)
     # ------------------------------------------------------------------
     def kernel_time(fn, cls, reps_):
         B.timing_read(cls)
@@ -348,7 +349,8 @@ def main() -> int:
         "traffic": measured_traffic(os.path.join(ROOT, "profiles", "score_decode_r256_h64_b4_n131072.md"),
                                     os.path.join(ROOT, "sparse_attention_token_absorb_amd", "csrc", "score.hip")),
         "kernel": f"k_score_decode<r={r},64 heads> (full LatentIndex, B={Bn}, N={N})",
-        "timing": "cold: a 1 GiB read-only scrub before every launch evicts the 256 MB last-level cache",
+        "timing": "cold: a 1 GiB read-only scrub before every launch evicts the 256 MB last-level cache; "
+                  "HIP events bound to the kernel's own start and end on its launch stream",
         "avg_launch_us": round(cold_ms * 1e3, 2), "launches": n_cold, "bytes_per_launch": bytes_launch,
         "warm_avg_launch_us": round(score_ms * 1e3, 2), "warm_launches": n_launch,
         "warm_achieved_GBs": round(achieved, 1), "warm_frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -299,8 +299,13 @@ LI_API size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H
 
 /*
  * Kernel timing (instrumentation for benchmarks and profiling).  While
- * enabled, the library brackets each launch of a kernel class with a pair of
- * HIP events recorded on the call's stream.  li_timing_read waits for the
+ * enabled, the library times each launch of a kernel class with a pair of HIP
+ * events on the call's stream.  A scoring class launches one kernel per call,
+ * and its events are bound to that kernel's own start and end
+ * (hipExtLaunchKernel), as a kernel trace measures it; the other classes
+ * record their events on the stream before and after their kernels, so their
+ * interval also holds the dispatch of the first kernel after the stream's
+ * preceding work (a few microseconds).  li_timing_read waits for the
  * recorded events of one class, returns their summed milliseconds and the
  * number of bracketed launches since the previous read of that class, and
  * forgets them.  Enabling timing creates HIP events (host-side objects; no
@@ -308,7 +313,9 @@ LI_API size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H
  *   LI_KERNEL_SCORE_DECODE   full-prefix scoring, few queries per sequence
  *   LI_KERNEL_SCORE_PREFILL  full-prefix scoring, many queries per sequence
  *   LI_KERNEL_SCORE_GATHER   HS follower candidate scoring
- *   LI_KERNEL_SELECT         one top-k selection (all of its kernels)
+ *   LI_KERNEL_SELECT         one top-k selection (all of its kernels; in
+ *                            li_hs_select also the copy of candidate scores
+ *                            when they are asked for)
  *   LI_KERNEL_ABSORB, LI_KERNEL_APPEND
  */
 typedef enum {

@@ -371,7 +371,7 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
         a.hist = fused_hist ? sw.hist : nullptr;
         const int64_t row_bytes = fp8 ? cache->r + cache->r / 128 * 4 : (int64_t)cache->r * (cache->dtype == LI_BF16 ? 2 : 4);
         a.stream_nt = !many && stream_nt((int64_t)Q * queries->max_valid * row_bytes);
-        li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream);
+        li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream, true);
         if (fp8)
             e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, many,
                                      queries->max_valid, stream);
@@ -494,14 +494,18 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
             fp8 ? cache->r + cache->r / 128 * 4 : (int64_t)cache->r * (cache->dtype == LI_BF16 ? 2 : 4);
         a.stream_nt = stream_nt((int64_t)Q * queries->max_valid * row_bytes);
         if (queries->max_valid > 0) {
-            li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
-            if (fp8)
-                e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r,
-                                         false, queries->max_valid, stream);
-            else
-                e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, queries->max_valid, stream);
-            if (e == hipSuccess && cand_scores)
+            {
+                li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream, true);
+                if (fp8)
+                    e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r,
+                                             false, queries->max_valid, stream);
+                else
+                    e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, false, queries->max_valid, stream);
+            }
+            if (e == hipSuccess && cand_scores) {
+                li::TimedScope ts(LI_KERNEL_SELECT, stream);
                 e = li::launch_gather_scores(S_pos, M, cand, cand_count, M, cand_scores, Q, stream);
+            }
         }
         if (e != hipSuccess) return hip_fail(e, "hs score launch");
         li::SelCall sc{};
@@ -550,7 +554,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.max_rows = M;
     a.hist = fused_hist ? sw.hist : nullptr;
     {
-        li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream);
+        li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream, true);
         if (cache->dtype == LI_FP8)
             e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, false, M,
                                      stream);

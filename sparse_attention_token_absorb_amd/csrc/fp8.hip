@@ -24,6 +24,7 @@
 // byte offset li_fp8_query_scale_offset(Q, H, r), scales [Q][H][r/128] fp32.
 #include "li_device.hpp"
 #include "li_internal.hpp"
+#include "li_timing.hpp"
 
 #include <algorithm>
 
@@ -882,13 +883,12 @@ hipError_t launch_prefill_fp8_rh(const ScoreArgs &a, const float *pool_scales, i
     int64_t tps = (tiles + splits - 1) / splits;
     if (tps > kPrefillMaxTilesF8) tps = kPrefillMaxTilesF8;
     splits = (tiles + tps - 1) / tps;
+    const dim3 grid(qblocks, (unsigned)splits);
     if (a.bias)
-        hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF, true>), dim3(qblocks, (unsigned)splits), dim3(256), 0, s,
-                           a, pool_scales, qscale_off, (int)tps);
-    else
-        hipLaunchKernelGGL((k_score_prefill_fp8<R, HB, NBUF, false>), dim3(qblocks, (unsigned)splits), dim3(256), 0,
-                           s, a, pool_scales, qscale_off, (int)tps);
-    return hipGetLastError();
+        return launch_kernel(k_score_prefill_fp8<R, HB, NBUF, true>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+                             (int)tps);
+    return launch_kernel(k_score_prefill_fp8<R, HB, NBUF, false>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+                         (int)tps);
 }
 
 template <int R, int HB>
@@ -909,16 +909,15 @@ hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int
     if (a.cand && tpw > kGatherTilesF8) tpw = kGatherTilesF8;
     if (!a.cand && tpw > kMaxTilesPerWaveF8) tpw = kMaxTilesPerWaveF8;
     const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
+    const dim3 grid((unsigned)wgs, a.Q);
     if (a.cand)
-        hipLaunchKernelGGL((k_score_fp8<R, HB, true, NBG, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                           pool_scales, qscale_off, (int)tpw);
-    else if (a.stream_nt)
-        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB, true>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                           pool_scales, qscale_off, (int)tpw);
-    else
-        hipLaunchKernelGGL((k_score_fp8<R, HB, false, NB, false>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                           pool_scales, qscale_off, (int)tpw);
-    return hipGetLastError();
+        return launch_kernel(k_score_fp8<R, HB, true, NBG, false>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+                             (int)tpw);
+    if (a.stream_nt)
+        return launch_kernel(k_score_fp8<R, HB, false, NB, true>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+                             (int)tpw);
+    return launch_kernel(k_score_fp8<R, HB, false, NB, false>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+                         (int)tpw);
 }
 
 template <int R>

@@ -20,6 +20,7 @@
 // follows starts from a known threshold bin.
 #include "li_device.hpp"
 #include "li_internal.hpp"
+#include "li_timing.hpp"
 
 #include <stdlib.h>
 #include <string.h>
@@ -851,12 +852,10 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
         if (tps > kPrefillMaxTiles) tps = kPrefillMaxTiles;
         splits = (tiles + tps - 1) / tps;
         if (a.bias)
-            hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB, true>), dim3(qblocks, (unsigned)splits),
-                               dim3(64 * QW), 0, s, a, (int)tps);
-        else
-            hipLaunchKernelGGL((k_score_prefill<R, HB, NBUF, QW, TPB, false>), dim3(qblocks, (unsigned)splits),
-                               dim3(64 * QW), 0, s, a, (int)tps);
-        return hipGetLastError();
+            return launch_kernel(k_score_prefill<R, HB, NBUF, QW, TPB, true>, dim3(qblocks, (unsigned)splits),
+                                 dim3(64 * QW), 0, s, a, (int)tps);
+        return launch_kernel(k_score_prefill<R, HB, NBUF, QW, TPB, false>, dim3(qblocks, (unsigned)splits),
+                             dim3(64 * QW), 0, s, a, (int)tps);
     }
     // decode: about one round of one workgroup per CU
     const int64_t want_wgs = 256;
@@ -872,12 +871,10 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
             wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
         }
         if (a.cand)
-            hipLaunchKernelGGL((k_score_decode_vr<R, HB, true, DEPTH>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                               (int)tpw);
-        else
-            hipLaunchKernelGGL((k_score_decode_vr<R, HB, false, DEPTH>), dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
-                               (int)tpw);
-        return hipGetLastError();
+            return launch_kernel(k_score_decode_vr<R, HB, true, DEPTH>, dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                                 (int)tpw);
+        return launch_kernel(k_score_decode_vr<R, HB, false, DEPTH>, dim3((unsigned)wgs, a.Q), dim3(256), 0, s, a,
+                             (int)tpw);
     }
     if (!a.cand && tpw > kMaxTilesPerWave) {
         tpw = kMaxTilesPerWave; // one page id per lane of the wave
@@ -888,21 +885,13 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     constexpr int NB = R == 64 ? 6 : 3;
     auto go = [&](auto BIASc) {
         constexpr bool BI = decltype(BIASc)::value;
-        if (a.cand)
-            hipLaunchKernelGGL((k_score_decode<R, HB, true, NB, CPT, false, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
-                               0, s, a, (int)tpw);
-        else if (a.stream_nt)
-            hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, true, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
-                               0, s, a, (int)tpw);
-        else
-            hipLaunchKernelGGL((k_score_decode<R, HB, false, NB, CPT, false, BI>), dim3((unsigned)wgs, a.Q), dim3(256),
-                               0, s, a, (int)tpw);
+        const dim3 grid((unsigned)wgs, a.Q);
+        if (a.cand) return launch_kernel(k_score_decode<R, HB, true, NB, CPT, false, BI>, grid, dim3(256), 0, s, a, (int)tpw);
+        if (a.stream_nt)
+            return launch_kernel(k_score_decode<R, HB, false, NB, CPT, true, BI>, grid, dim3(256), 0, s, a, (int)tpw);
+        return launch_kernel(k_score_decode<R, HB, false, NB, CPT, false, BI>, grid, dim3(256), 0, s, a, (int)tpw);
     };
-    if (a.bias)
-        go(std::true_type{});
-    else
-        go(std::false_type{});
-    return hipGetLastError();
+    return a.bias ? go(std::true_type{}) : go(std::false_type{});
 }
 
 template <int R>
@@ -944,9 +933,8 @@ hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_
     if (!bf16) {
         const int64_t wgs = std::min<int64_t>((max_rows + 255) / 256, 1024);
         const int64_t per = ((max_rows + wgs - 1) / wgs + 255) / 256 * 256;
-        hipLaunchKernelGGL(k_score_f32, dim3((unsigned)((max_rows + per - 1) / per), a.Q), dim3(256), 0, s, a, r,
-                           (int)per);
-        return hipGetLastError();
+        return launch_kernel(k_score_f32, dim3((unsigned)((max_rows + per - 1) / per), a.Q), dim3(256), 0, s, a, r,
+                             (int)per);
     }
     switch (r) {
     case 64: return launch_r<64>(a, prefill, max_rows, s);

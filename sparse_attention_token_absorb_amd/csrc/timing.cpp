@@ -38,31 +38,53 @@ hipEvent_t take_event(Registry &r)
 
 } // namespace
 
-TimedScope::TimedScope(int cls, hipStream_t s) : cls_(cls), s_(s), a_(nullptr), b_(nullptr)
+static thread_local TimedScope *t_current = nullptr;
+
+TimedScope::TimedScope(int cls, hipStream_t s, bool one_kernel)
+    : cls_(cls), s_(s), a_(nullptr), b_(nullptr), one_(one_kernel), taken_(false), prev_(nullptr)
 {
     Registry &r = reg();
     std::lock_guard<std::mutex> g(r.m);
     if (!r.on || cls < 0 || cls >= LI_KERNEL_CLASSES) return;
     a_ = take_event(r);
     b_ = take_event(r);
-    if (!a_ || !b_ || hipEventRecord(a_, s_) != hipSuccess) {
+    if (!a_ || !b_ || (!one_ && hipEventRecord(a_, s_) != hipSuccess)) {
         if (a_) r.spare.push_back(a_);
         if (b_) r.spare.push_back(b_);
         a_ = b_ = nullptr;
+        return;
+    }
+    if (one_) {
+        prev_ = t_current;
+        t_current = this;
     }
 }
 
 TimedScope::~TimedScope()
 {
     if (!a_) return;
+    if (one_) t_current = prev_;
     Registry &r = reg();
     std::lock_guard<std::mutex> g(r.m);
-    if (hipEventRecord(b_, s_) == hipSuccess) {
+    const bool ok = one_ ? taken_ : hipEventRecord(b_, s_) == hipSuccess;
+    if (ok) {
         r.pending[cls_].push_back(Pair{a_, b_});
     } else {
         r.spare.push_back(a_);
         r.spare.push_back(b_);
     }
+}
+
+void kernel_events(hipEvent_t *start, hipEvent_t *stop)
+{
+    TimedScope *t = t_current;
+    if (!t || t->taken_) {
+        *start = *stop = nullptr;
+        return;
+    }
+    t->taken_ = true;
+    *start = t->a_;
+    *stop = t->b_;
 }
 
 void timing_enable(bool on)
