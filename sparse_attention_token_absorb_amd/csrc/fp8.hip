@@ -686,6 +686,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     constexpr int CH = R / 16;
     constexpr int KS = R / 64;
     static_assert(NIW >= 1, "tile must split over 4 waves");
+    static_assert(NBUF % 2 == 0, "a tile's accumulator set is its ring slot's parity");
     __shared__ __attribute__((aligned(1024))) uint8_t ring_raw[NBUF * SLOT];
     __shared__ int32_t s_page_raw[kPrefillMaxTilesF8 / 2 + 2];
     lds_u8 *ring = (lds_u8 *)ring_raw;
@@ -750,6 +751,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
     }
     float *out = a.out + (int64_t)(q < a.Q ? q : 0) * a.out_ld;
+    // this query's scores as a raw buffer of my_n floats (bounds-checked)
+    const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(out, 0, my_n * 4, kBufferWord3);
     const uint8_t *pool = (const uint8_t *)a.pool;
     const int nr = lane & 31, gk = lane >> 5;
     // Per-lane parts of every tile's addresses, the same for every tile:
@@ -815,6 +818,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             // scales: this wave's quarter (16 lanes x 4 bytes) of the tile's 32 x NSEG
             if (lane < 16) dma4s(gscale, sc_src_off, slot + CODE_BYTES + wv * 64);
         };
+        // The epilogue of a tile runs one tile late: the MFMAs of tile i
+        // issue first and the ReLU-weighted head sum of tile i-1 (registers
+        // only) follows while they execute, so the vector work overlaps the
+        // matrix core instead of waiting for it.  Tile i accumulates into
+        // accs[i & 1] (the ring depth is even, so that is the slot's parity).
+        f32x16 accs[2][HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) accs[0][hb] = accs[1][hb] = f32x16{};
+        auto finish = [&](const f32x16 (&acc)[HB], int i) {
+            const float pv = epilogue<HB>(acc, wr);
+            const int j = (ts + i) * kTile + lane;
+            if (lane < 32 && j < my_n) out[j] = pv;
+        };
         // One tile; its ring slot SL (and that of the tile issued in its
         // place) is a compile-time constant, so every LDS address below is a
         // fixed per-lane offset plus an immediate.
@@ -836,11 +852,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                    0xFFu);
                 // accumulators start from the heads' biases, or (no bias) the
                 // first step adds to a constant zero
-                f32x16 acc[HB];
-                if constexpr (BIAS) {
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
-                }
+                f32x16(&acc)[HB] = accs[SL & 1];
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const u32x4 lo = *(const lds_u32x4 *)(slot + rd_off[s][0]);
@@ -852,12 +864,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     for (int hb = 0; hb < HB; ++hb) {
                         const f32x16 zero = {};
                         acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            qa[hb][s], bv, !BIAS && s == 0 ? zero : acc[hb], 0, 0, 0, sa[hb][g], 0, scb[g]);
+                            qa[hb][s], bv, s == 0 ? (BIAS ? br[hb] : zero) : acc[hb], 0, 0, 0, sa[hb][g], 0, scb[g]);
                     }
                 }
-                const float pv = epilogue<HB>(acc, wr);
-                const int j = (ts + i) * kTile + lane;
-                if (lane < 32 && j < my_n) out[j] = pv;
+                // tile i-1's head sum (for i = 0 a discarded sum of zeros)
+                const float pv = epilogue<HB>(accs[(SL + 1) & 1], wr);
+                // issue order: the fragment reads, then each MFMA followed by
+                // a share of the head sum's vector instructions
+                __builtin_amdgcn_sched_group_barrier(0x100, KS * 2 + 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, NSEG, 0);
+                static_for<KS * HB>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 40 / KS, 0);
+                });
+                // a buffer store whose out-of-range offsets the hardware
+                // drops: no branch, so the MFMAs and the sum stay together
+                const int j = (ts + i - 1) * kTile + lane;
+                const bool ok = i > 0 && lane < 32 && j < my_n;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv), out_rsrc, ok ? j * 4 : kBufferDrop, 0, 0);
             }
         };
         for (int i = 0; i < NBUF - 1 && i < nt; ++i) issue(i, page_of(i), i);
@@ -867,6 +891,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 const int i = i0 + decltype(SLc)::value;
                 if (i < nt) tile(SLc, i);
             });
+        if (active) {
+            if ((nt - 1) & 1)
+                finish(accs[1], nt - 1);
+            else
+                finish(accs[0], nt - 1);
+        }
     }
 }
 

@@ -225,6 +225,14 @@ __device__ __forceinline__ void dma4s(const void *base_uniform, uint32_t off, ld
 
 // max(x, 0) in one integer max on the bit pattern (negative floats, -0.0
 // included, have the sign bit set and become +0.0).
+// Raw buffer resources (gfx9 family): the fourth descriptor word of an
+// untyped 32-bit buffer, and a byte offset past any buffer's record count.
+// A raw buffer access whose offset is at or beyond the record count is
+// dropped (a store writes nothing, a load returns 0), which lets a masked
+// store go without a branch.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferDrop = (int)0x80000000;
+
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // ReLU, head weights and head sum: the score of tile row (lane % 32).
