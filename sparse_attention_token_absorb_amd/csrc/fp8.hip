@@ -606,9 +606,21 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         rd_off[s][0] = (uint32_t)((nr * CH + (c ^ (nr % CH))) * 16);
         rd_off[s][1] = (uint32_t)((nr * CH + ((c + 1) ^ (nr % CH))) * 16);
     }
-    auto tile = [&](auto SLc, int i) {
-        constexpr int SL = decltype(SLc)::value;
+    // The head sum of a tile runs one tile late: tile i's MFMAs issue first
+    // and tile i-1's ReLU-weighted sum (registers only) follows while they
+    // execute.  Tile i accumulates into accs[i & 1]; the loop is unrolled
+    // over lcm(NB, 2) tiles so that both the ring slot and the set are
+    // compile-time constants.  Both lane halves end with the row's whole
+    // score, so lane l and lane l + 32 store the same value to the same LDS
+    // word and the store needs no branch (rows past n are never read back).
+    f32x16 accs[2][HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) accs[0][hb] = accs[1][hb] = f32x16{};
+    auto tile = [&](auto Uc, int i) {
+        constexpr int U = decltype(Uc)::value;
+        constexpr int SL = U % NB;
         constexpr int NX = (SL + NB - 1) % NB;
+        constexpr int PAR = U & 1;
         if (i + NB - 1 < nt) {
             wait_lds(); // this wave's reads of that slot (tile i-1) are complete
             issue(i + NB - 1, NX);
@@ -620,9 +632,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         for (int g = 0; g < NSEG; ++g)
             sb[g] = (int)((*(const __attribute__((address_space(3))) uint32_t *)(slot + CODE_BYTES +
                                                                                   (nr * NSEG + g) * 4) >> 23) & 0xFFu);
-        f32x16 acc[HB];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) acc[hb] = br[hb];
+        f32x16(&acc)[HB] = accs[PAR];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const u32x4 lo = *(const lds_u32x4 *)(slot + rd_off[s][0]);
@@ -631,18 +641,32 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             const int g = (s * 64) / kSeg;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
-                acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[hb][s], bv, acc[hb], 0, 0, 0, sa[hb][g], 0,
-                                                                          sb[g]);
+                acc[hb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[hb][s], bv, s == 0 ? br[hb] : acc[hb], 0, 0,
+                                                                          0, sa[hb][g], 0, sb[g]);
         }
-        const float p = epilogue<HB>(acc, wr);
-        if (lane < 32 && tile_row0(i) + lane < n) outw[i * 4 * kTile + lane] = p; // local row (i * 4 + wv) * 32 + lane
-    };
-#pragma unroll 1
-    for (int i0 = 0; i0 < nt; i0 += NB)
-        static_for<NB>([&](auto SLc) {
-            const int i = i0 + decltype(SLc)::value;
-            if (i < nt) tile(SLc, i);
+        // tile i-1's sum, interleaved with the MFMAs above (for i = 0 a sum
+        // over zeroed accumulators, written to tile 0's words, which tile 0's
+        // own score overwrites one tile later)
+        const float p = epilogue<HB>(accs[PAR ^ 1], wr);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS * 2 + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NSEG, 0);
+        static_for<KS * HB>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 40 / KS, 0);
         });
+        outw[(i > 0 ? i - 1 : 0) * 4 * kTile + (lane & 31)] = p; // local row ((i-1) * 4 + wv) * 32 + lane
+    };
+    constexpr int UN = NB % 2 == 0 ? NB : 2 * NB;
+#pragma unroll 1
+    for (int i0 = 0; i0 < nt; i0 += UN)
+        static_for<UN>([&](auto Uc) {
+            const int i = i0 + decltype(Uc)::value;
+            if (i < nt) tile(Uc, i);
+        });
+    if (nt > 0) {
+        const float p = (nt - 1) & 1 ? epilogue<HB>(accs[1], wr) : epilogue<HB>(accs[0], wr);
+        outw[(nt - 1) * 4 * kTile + (lane & 31)] = p;
+    }
     wait_vmcnt<0>(); // tiles issued ahead of the row count and never used
     __syncthreads(); // every wave's scores are in LDS (and the histogram is cleared)
     // The scores leave in one coalesced pass over the workgroup's rows (score
