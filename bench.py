@@ -64,7 +64,36 @@ def parse():
                     help="hardware-counter pass, no JSON line: 'decode' runs a few eager full-LatentIndex layers, "
                          "then a plain 1 GiB copy whose counter readings scale the others to bytes; 'prefill' "
                          "('prefill-fp8') runs a few eager chunked-prefill layers on a bf16 (FP8) cache")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-wave phase timestamps of the decode scoring kernels (bf16 and FP8, cold and warm "
+                         "launches) from the instrumented library variant (python -m "
+                         "sparse_attention_token_absorb_amd.build phases); prints one JSON line per case")
     return ap.parse_args()
+
+
+def phase_summary(rec, np):
+    """Per-wave phase records (li_phase_records) -> where one launch's time goes.
+
+    Times are microseconds from the earliest wave start (100 MHz clock).
+    'first_tile' is when a wave's first tile of rows has landed in LDS, 'loop_end'
+    when its stream is done, 'end' when the wave ends (after the score copy-out
+    and the histogram flush).  Each entry is [min, median, max] over waves."""
+    r = rec[rec[:, 0] != 0].astype(np.int64)
+    if len(r) == 0:
+        return {"waves": 0}
+    rel = (r[:, :5] - r[:, 0].min()) * 0.01
+    out = {"waves": int(len(r)), "span_us": round(float(rel[:, 4].max()), 2)}
+    for i, name in enumerate(("start", "first_tile", "loop_end", "after_barrier", "end")):
+        out[name] = [round(float(v), 2) for v in (rel[:, i].min(), np.median(rel[:, i]), rel[:, i].max())]
+    loop = rel[:, 2] - rel[:, 1]
+    out["stream_us_per_wave"] = [round(float(v), 2) for v in (loop.min(), np.median(loop), loop.max())]
+    out["startup_us_median"] = round(float(np.median(rel[:, 1] - rel[:, 0])), 2)
+    out["tail_us_median"] = round(float(np.median(rel[:, 4] - rel[:, 3])), 2)
+    xcc = (r[:, 5] >> 32) & 0xF
+    out["stream_us_median_by_xcc"] = {int(x): round(float(np.median(loop[xcc == x])), 2) for x in sorted(set(xcc.tolist()))}
+    out["loop_end_us_median_by_xcc"] = {int(x): round(float(np.median(rel[xcc == x, 2])), 2)
+                                         for x in sorted(set(xcc.tolist()))}
+    return out
 
 
 def main() -> int:
@@ -79,6 +108,13 @@ def main() -> int:
     from sparse_attention_token_absorb_amd import binding as B
     from sparse_attention_token_absorb_amd import synth
 
+    if args.phases:
+        from sparse_attention_token_absorb_amd import build as hip_build
+        if not os.path.exists(hip_build.LIB_PHASES):
+            print(f"{hip_build.LIB_PHASES} is not built: python -m sparse_attention_token_absorb_amd.build phases",
+                  file=sys.stderr, flush=True)
+            return 2
+        B.LIB_PATH = hip_build.LIB_PHASES
     B.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -201,6 +237,44 @@ def main() -> int:
         print(json.dumps({"kernel": "k_score_decode (r=256, 64 heads, B=4, N=131072, cold)", "launches": n,
                           "avg_launch_us": round(us, 2), "bytes_per_launch": bytes_launch,
                           "achieved_GBs": round(bytes_launch / us / 1e3, 1)}), flush=True)
+        return 0
+
+    if args.phases:
+        # the same launches as the roofline's (cold: a 1 GiB read-only scrub
+        # before each; warm: back to back), bf16 and FP8 caches of the latent
+        scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        f8pool = torch.zeros((g.num_pages, 64, r), dtype=torch.uint8, device=dev)
+        f8sc = torch.zeros((g.num_pages, 64, r // 128), dtype=torch.float32, device=dev)
+        f8cache = B.LatentCache(f8pool, i32(g.block_table), i32(g.lens), f8sc)
+        for b in range(Bn):
+            B.append_latent(f8cache, tdev(g.latent[b], bf), i32(np.full(N, b)), i32(np.arange(N)))
+        for l in range(G):
+            B.absorb_query(q[l], W[l], out=qt[l])
+        f8q = B.absorb_query(q[0], W[0], fp8=True)
+        cases = (("bf16", B.LI_PHASE_SCORE_DECODE_BF16, lambda: B.score_topk(cache, seq, pos, N, qt[0], w[0], k, ws=ws,
+                                                                               out=out_b[0])),
+                 ("fp8", B.LI_PHASE_SCORE_DECODE_FP8, lambda: B.score_topk(f8cache, seq, pos, N, f8q, w[0], k, ws=ws,
+                                                                             out=out_b[0])))
+        for name, which, run in cases:
+            for _ in range(3):
+                run()
+            for rep in range(args.steps):
+                for cold in (True, False):
+                    B.phase_clear(which)
+                    if cold:
+                        torch.sum(scrub, dim=0, keepdim=True, out=sink)
+                    torch.cuda.synchronize()
+                    B.timing_read(B.LI_KERNEL_SCORE_DECODE)
+                    B.timing_enable(True)
+                    run()
+                    torch.cuda.synchronize()
+                    B.timing_enable(False)
+                    ms, n = B.timing_read(B.LI_KERNEL_SCORE_DECODE)
+                    summary = phase_summary(B.phase_records(which), np)
+                    summary = {"kernel": f"{name} decode scoring, B={Bn}, N={N}", "launch": "cold" if cold else "warm",
+                               "rep": rep, "event_us": round(ms / max(n, 1) * 1e3, 2), **summary}
+                    print(json.dumps(summary), flush=True)
         return 0
 
     def capture(fn):

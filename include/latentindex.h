@@ -330,6 +330,24 @@ typedef enum {
 LI_API li_status li_timing_enable(int on);
 LI_API li_status li_timing_read(int kernel_class, double *total_ms, int64_t *launches);
 
+/*
+ * Phase records of the decode scoring kernels (instrumentation; only the
+ * library's "phases" build variant records them, every other build returns
+ * LI_ERR_UNSUPPORTED).  In that build each wave of a decode scoring launch
+ * writes one record of 8 little-endian uint64 words: five readings of the
+ * GPU's 100 MHz constant clock (its start, its first tile of latent rows
+ * landed in LDS, the end of its stream, the end of the workgroup barrier
+ * after the stream, its end), then (XCC id << 32 | hardware id), blockIdx.x
+ * and blockIdx.y.  Record (blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave;
+ * 16384 records, zero where no wave wrote.  Each launch overwrites the
+ * records its waves write, so read after one launch.
+ * li_phase_records(kernel, host, bytes): host != NULL copies the first
+ * `bytes` bytes (at most 16384 * 64) of that kernel's records on the current
+ * device to host memory (synchronous); host == NULL zeroes them.
+ */
+typedef enum { LI_PHASE_SCORE_DECODE_BF16 = 0, LI_PHASE_SCORE_DECODE_FP8 = 1 } li_phase_kernel;
+LI_API li_status li_phase_records(int kernel, void *host, size_t bytes);
+
 LI_API const char *li_status_str(li_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 LI_API const char *li_last_error(void);

@@ -24,7 +24,7 @@ LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
 EXPORTED = ["li_append_latent", "li_append_latent_rope", "li_rope_decoder", "li_query_bias", "li_absorb_query",
             "li_score_topk", "li_score_topk_noalloc", "li_hs_select", "li_workspace_bytes", "li_fp8_query_bytes", "li_fp8_query_scale_offset",
-            "li_timing_enable", "li_timing_read", "li_status_str", "li_last_error", "li_abi_version"]
+            "li_timing_enable", "li_timing_read", "li_phase_records", "li_status_str", "li_last_error", "li_abi_version"]
 (LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
  LI_KERNEL_APPEND) = range(6)
 
@@ -86,6 +86,8 @@ def lib():
         L.li_timing_enable.restype = ctypes.c_int
         L.li_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.li_timing_read.restype = ctypes.c_int
+        L.li_phase_records.argtypes = [ctypes.c_int, vp, sz]
+        L.li_phase_records.restype = ctypes.c_int
         for f in ("li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -231,6 +233,24 @@ def timing_read(kernel_class: int) -> Tuple[float, int]:
     n = ctypes.c_int64(0)
     _check(lib().li_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n)), "li_timing_read")
     return float(ms.value), int(n.value)
+
+
+LI_PHASE_SCORE_DECODE_BF16, LI_PHASE_SCORE_DECODE_FP8 = 0, 1
+PHASE_RECORDS, PHASE_WORDS = 16384, 8
+
+
+def phase_clear(kernel: int) -> None:
+    """li_phase_records(kernel, NULL, 0): zero one decode kernel's phase records
+    (instrumented "phases" build only; LIError otherwise)."""
+    _check(lib().li_phase_records(kernel, None, 0), "li_phase_records")
+
+
+def phase_records(kernel: int):
+    """li_phase_records: the phase records as a [16384, 8] uint64 numpy array."""
+    import numpy as np
+    buf = np.zeros((PHASE_RECORDS, PHASE_WORDS), dtype=np.uint64)
+    _check(lib().li_phase_records(kernel, buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes), "li_phase_records")
+    return buf
 
 
 def workspace_bytes(op: int, Q: int, max_valid: int, H: int, r: int, k: int, M: int = 0) -> int:

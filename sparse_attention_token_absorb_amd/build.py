@@ -34,6 +34,11 @@ def hipcc() -> str:
 ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 BUILD_ASAN = os.path.join(HERE, "_build_asan")
 LIB_ASAN = os.path.join(BUILD_ASAN, "liblatentindex_asan.so")
+# Instrumented build (variant "phases"): the decode scoring kernels record
+# per-wave phase timestamps (li_phase_records); everything else is the same.
+BUILD_PHASES = os.path.join(HERE, "_build_phases")
+LIB_PHASES = os.path.join(BUILD_PHASES, "liblatentindex_phases.so")
+_OUT = {None: (BUILD, LIB), "asan": (BUILD_ASAN, LIB_ASAN), "phases": (BUILD_PHASES, LIB_PHASES)}
 
 
 def _flags(variant=None):
@@ -46,11 +51,13 @@ def _flags(variant=None):
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
     if variant == "asan":
         f += ASAN_HOST
+    elif variant == "phases":
+        f += ["-DLI_PHASE_PROBE=1"]
     return f
 
 
 def _compile(src: str, variant=None) -> str:
-    out_dir = BUILD_ASAN if variant == "asan" else BUILD
+    out_dir = _OUT[variant][0]
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *_flags(variant), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,10 +67,12 @@ def _compile(src: str, variant=None) -> str:
 
 
 def build(verbose: bool = False, variant=None) -> str:
-    """Build liblatentindex.so (variant None) or the host-ASan library
-    _build_asan/liblatentindex_asan.so (variant "asan")."""
-    out_dir = BUILD_ASAN if variant == "asan" else BUILD
-    lib = LIB_ASAN if variant == "asan" else LIB
+    """Build liblatentindex.so (variant None), the host-ASan library
+    _build_asan/liblatentindex_asan.so (variant "asan") or the instrumented
+    _build_phases/liblatentindex_phases.so (variant "phases")."""
+    if variant not in _OUT:
+        raise ValueError(f"unknown build variant {variant!r}")
+    out_dir, lib = _OUT[variant]
     os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, variant), SOURCES))

@@ -16,6 +16,7 @@
 #include "../../include/latentindex.h"
 #include "li_internal.hpp"
 #include "li_timing.hpp"
+#include "li_probe.hpp"
 
 // Scratch of li_score_topk_noalloc (the workspace of li_score_topk): one copy
 // per GPU, held until the process ends.  In host code `scratch` names a
@@ -596,6 +597,27 @@ li_status li_timing_read(int kernel_class, double *total_ms, int64_t *launches)
     hipError_t e = li::timing_read(kernel_class, total_ms, launches);
     if (e != hipSuccess) return hip_fail(e, "timing read");
     return ok();
+}
+
+li_status li_phase_records(int kernel, void *host, size_t bytes)
+{
+    if (kernel != LI_PHASE_SCORE_DECODE_BF16 && kernel != LI_PHASE_SCORE_DECODE_FP8)
+        return fail(LI_ERR_SHAPE, "phase kernel %d is not LI_PHASE_SCORE_DECODE_BF16/FP8", kernel);
+    const size_t full = (size_t)li::kProbeWaves * li::kProbeWords * sizeof(uint64_t);
+#ifndef LI_PHASE_PROBE
+    (void)host;
+    (void)bytes;
+    (void)full;
+    return fail(LI_ERR_UNSUPPORTED, "phase records exist only in the instrumented (\"phases\") build");
+#else
+    if (bytes > full) return fail(LI_ERR_SHAPE, "%zu bytes > the %zu bytes of phase records", bytes, full);
+    void *dev = nullptr;
+    hipError_t e = kernel == LI_PHASE_SCORE_DECODE_BF16 ? li::phase_records_bf16(&dev) : li::phase_records_fp8(&dev);
+    if (e != hipSuccess) return hip_fail(e, "phase records address");
+    e = host ? hipMemcpy(host, dev, bytes, hipMemcpyDeviceToHost) : hipMemset(dev, 0, full);
+    if (e != hipSuccess) return hip_fail(e, host ? "phase records copy" : "phase records clear");
+    return ok();
+#endif
 }
 
 } // extern "C"

@@ -24,11 +24,16 @@
 // byte offset li_fp8_query_scale_offset(Q, H, r), scales [Q][H][r/128] fp32.
 #include "li_device.hpp"
 #include "li_internal.hpp"
+#include "li_probe.hpp"
 #include "li_timing.hpp"
 
 #include <algorithm>
 
 namespace li {
+
+#ifdef LI_PHASE_PROBE
+__device__ uint64_t g_phase_fp8[kProbeWaves * kProbeWords]; // phase records (instrumented build only)
+#endif
 namespace {
 
 constexpr int kSeg = 128;               // elements per quantization segment
@@ -437,6 +442,8 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    LI_PHASE_DECL;
+    LI_PHASE_START;
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     const int64_t first = row0 + (int64_t)wv * kTile;
     auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
@@ -626,6 +633,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
             issue(i + NB - 1, NX);
         }
         wait_after<NIT, NB - 1>(min(NB - 1, nt - 1 - i));
+        LI_PHASE_FIRST_IF(i == 0);
         const lds_u8 *slot = ring + SL * SLOT;
         int sb[NSEG];
 #pragma unroll
@@ -668,7 +676,9 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         outw[(nt - 1) * 4 * kTile + (lane & 31)] = p;
     }
     wait_vmcnt<0>(); // tiles issued ahead of the row count and never used
+    LI_PHASE_LOOP;
     __syncthreads(); // every wave's scores are in LDS (and the histogram is cleared)
+    LI_PHASE_SYNC;
     // The scores leave in one coalesced pass over the workgroup's rows (score
     // stores among the stream's loads interleave DRAM writes with the read
     // stream), which also counts their first radix digit.
@@ -686,6 +696,7 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         for (int j = threadIdx.x; j < rows; j += 256)
             out[row0 + j] = ((const __attribute__((address_space(3))) float *)s_out)[j];
     }
+    LI_PHASE_STORE(g_phase_fp8, wv, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1022,6 +1033,16 @@ hipError_t launch_absorb_fp8_r(const u16 *q, const u16 *W, uint8_t *codes, float
 }
 
 } // namespace
+
+#ifdef LI_PHASE_PROBE
+hipError_t phase_records_fp8(void **dev) { return hipGetSymbolAddress(dev, HIP_SYMBOL(g_phase_fp8)); }
+#else
+hipError_t phase_records_fp8(void **dev)
+{
+    *dev = nullptr;
+    return hipErrorNotSupported;
+}
+#endif
 
 int64_t fp8_query_scale_offset(int64_t Q, int64_t H, int64_t r) { return (Q * H * r + 255) / 256 * 256; }
 

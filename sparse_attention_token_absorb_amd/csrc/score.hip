@@ -20,6 +20,7 @@
 // follows starts from a known threshold bin.
 #include "li_device.hpp"
 #include "li_internal.hpp"
+#include "li_probe.hpp"
 #include "li_timing.hpp"
 
 #include <stdlib.h>
@@ -28,6 +29,10 @@
 #include <algorithm>
 
 namespace li {
+
+#ifdef LI_PHASE_PROBE
+__device__ uint64_t g_phase_bf16[kProbeWaves * kProbeWords]; // phase records (instrumented build only)
+#endif
 namespace {
 
 constexpr int kGatherTiles = 16; // max tiles per wave in gather mode (row offsets kept in LDS)
@@ -238,6 +243,8 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    LI_PHASE_DECL;
+    LI_PHASE_START;
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     const int64_t first = row0 + (int64_t)wv * kTile;
     auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
@@ -399,6 +406,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
             issue(c + NB - 1);
         }
         wait_after<NIC, NB - 1>(min(NB - 1, nchunks - 1 - c));
+        LI_PHASE_FIRST_IF(c == 0);
         const lds_u8 *buf = ring + SL * CHUNK;
         // a tile's accumulators start from the heads' biases, or (no bias)
         // its first step adds to a constant zero
@@ -431,7 +439,9 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
             if (c < nchunks) chunk(Uc, c);
         });
     wait_vmcnt<0>(); // chunks issued ahead of the row count and never used
+    LI_PHASE_LOOP;
     __syncthreads(); // every wave's scores are in LDS
+    LI_PHASE_SYNC;
     // The scores leave in one pass over the workgroup's rows, which also
     // counts their first radix digit (kept out of the stream above).
     float *out = a.out + (int64_t)q * a.out_ld;
@@ -447,6 +457,7 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     } else {
         for (int j = threadIdx.x; j < rows; j += 256) out[row0 + j] = ((const lds_f32 *)s_out)[j];
     }
+    LI_PHASE_STORE(g_phase_bf16, wv, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -915,6 +926,16 @@ __global__ __launch_bounds__(256) void k_gather_scores(const float *S, int64_t l
 }
 
 } // namespace
+
+#ifdef LI_PHASE_PROBE
+hipError_t phase_records_bf16(void **dev) { return hipGetSymbolAddress(dev, HIP_SYMBOL(g_phase_bf16)); }
+#else
+hipError_t phase_records_bf16(void **dev)
+{
+    *dev = nullptr;
+    return hipErrorNotSupported;
+}
+#endif
 
 hipError_t launch_gather_scores(const float *S, int64_t ld, const int32_t *cand, const int32_t *cand_count, int64_t M,
                                 float *out, int32_t Q, hipStream_t s)

@@ -51,6 +51,16 @@ def test_version_and_status_strings(L):
     assert L.li_status_str(99) == b"LI_ERR_UNKNOWN"
 
 
+def test_phase_records_only_in_the_instrumented_build(L):
+    """The product library records no phases: li_phase_records answers
+    LI_ERR_UNSUPPORTED for both decode kernels (without touching the GPU) and
+    rejects an unknown kernel id."""
+    buf = (ctypes.c_uint64 * 8)()
+    assert L.li_phase_records(B.LI_PHASE_SCORE_DECODE_BF16, buf, ctypes.sizeof(buf)) == B.LI_ERR_UNSUPPORTED
+    assert L.li_phase_records(B.LI_PHASE_SCORE_DECODE_FP8, None, 0) == B.LI_ERR_UNSUPPORTED
+    assert L.li_phase_records(7, buf, ctypes.sizeof(buf)) == B.LI_ERR_SHAPE
+
+
 def cache(**kw):
     d = dict(pool=FAKE.value, block_table=FAKE.value, seq_lens=FAKE.value, batch=1, max_pages=4, page_size=64,
              num_pages=4, r=256, dtype=B.LI_BF16, scales=None)
