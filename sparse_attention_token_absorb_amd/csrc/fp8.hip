@@ -444,6 +444,54 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     LI_PHASE_DECL;
     LI_PHASE_START;
+    // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
+    // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
+    // Requested first, beside the block-table row and the sequence id, and
+    // waited for with them before any tile is issued: one round trip for all
+    // of the start-up loads, and no wait for the query later in the stream
+    // (waiting for these loads once tiles are in flight would also wait for
+    // every tile issued before the wait).
+    i32x8 qa[HB][KS];
+    int sa[HB][NSEG];
+    float wr[HB][16];
+    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
+    {
+        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
+        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const int h = hb * 32 + (lane & 31);
+            const int hc = h < a.H ? h : a.H - 1;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
+                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
+                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (h >= a.H) {
+                    i32x8 z = {};
+                    v = z;
+                }
+                qa[hb][s] = v;
+            }
+            // every load is unconditional (indices clamped into the query),
+            // so they are all in flight together; heads past H are zeroed after
+#pragma unroll
+            for (int g = 0; g < NSEG; ++g) {
+                const uint32_t e = (__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu;
+                sa[hb][g] = h < a.H ? (int)e : 127;
+            }
+            const float *wq = a.w + (int64_t)q * a.H;
+            const float *bq = a.bias ? a.bias + (int64_t)q * a.H : a.w + (int64_t)q * a.H;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int hcl = hh < a.H ? hh : a.H - 1;
+                const float wv_ = wq[hcl], bv_ = bq[hcl];
+                wr[hb][r] = hh < a.H ? wv_ : 0.0f;
+                br[hb][r] = a.bias && hh < a.H ? bv_ : 0.0f;
+            }
+        }
+    }
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     const int64_t first = row0 + (int64_t)wv * kTile;
     auto tile_row0 = [&](int i) -> int64_t { return first + (int64_t)i * 4 * kTile; };
@@ -546,53 +594,12 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         }
     };
     const int npro = min(NB - 1, nt_max);
+    // every start-up load (query, weights, page ids, gathered rows) has
+    // landed: s_waitcnt vmcnt(0), issued as the builtin so that the compiler
+    // counts it and adds no wait of its own for these loads later
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int i = 0; i < npro; ++i) issue(i, i);
 
-    // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
-    // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
-    // Loaded after the first tiles are in flight: its loads then overlap
-    // theirs instead of delaying their issue.
-    i32x8 qa[HB][KS];
-    int sa[HB][NSEG];
-    float wr[HB][16];
-    f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
-    {
-        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
-        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            const int h = hb * 32 + (lane & 31);
-            const int hc = h < a.H ? h : a.H - 1;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint8_t *p = qc + (int64_t)hc * R + s * 64 + (lane >> 5) * 32;
-                const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
-                i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                if (h >= a.H) {
-                    i32x8 z = {};
-                    v = z;
-                }
-                qa[hb][s] = v;
-            }
-            // every load is unconditional (indices clamped into the query),
-            // so they are all in flight together; heads past H are zeroed after
-#pragma unroll
-            for (int g = 0; g < NSEG; ++g) {
-                const uint32_t e = (__float_as_uint(qs[(int64_t)hc * NSEG + g]) >> 23) & 0xFFu;
-                sa[hb][g] = h < a.H ? (int)e : 127;
-            }
-            const float *wq = a.w + (int64_t)q * a.H;
-            const float *bq = a.bias ? a.bias + (int64_t)q * a.H : a.w + (int64_t)q * a.H;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int hcl = hh < a.H ? hh : a.H - 1;
-                const float wv_ = wq[hcl], bv_ = bq[hcl];
-                wr[hb][r] = hh < a.H ? wv_ : 0.0f;
-                br[hb][r] = a.bias && hh < a.H ? bv_ : 0.0f;
-            }
-        }
-    }
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
     if (row0 >= n) {
         wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
