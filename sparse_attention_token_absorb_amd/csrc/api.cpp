@@ -356,7 +356,7 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
     // leaves the count to the selection pass.
     const bool fp8 = cache->dtype == LI_FP8;
     const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8)) &&
-                            li::selection_wants_counts(queries->max_valid);
+                            li::selection_wants_counts(Q, queries->max_valid);
     hipError_t e = hipSuccess;
     if (scored) {
         if (fused_hist) {
@@ -539,7 +539,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     sc.count = count;
 
     hipError_t e = hipSuccess;
-    const bool fused_hist = li::selection_wants_counts(M);
+    const bool fused_hist = li::selection_wants_counts(Q, M);
     if (fused_hist) {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
         e = li::launch_hist_clear(sw, Q, stream);

@@ -423,10 +423,18 @@ __device__ __forceinline__ void finish_levels(const Src &src, int m, uint32_t pr
 //   kCached (no histogram, max_n <= kKeyCache): the counting pass keeps the
 //           keys in LDS for the emission pass;
 //   kStream (longer rows): two passes over the row (one with a histogram),
-//           a smaller LDS footprint so that two workgroups share a CU.
+//           a smaller LDS footprint so that two workgroups share a CU;
+//   kSmall2 (no histogram, max_n <= 2 * kCandCap): kSmall with twice the
+//           keys per thread and a tie list as long as the row, for a few
+//           queries of up to 16384 rows (about 150 KiB of LDS: one
+//           workgroup per CU, which a few queries leave idle anyway).
 // ---------------------------------------------------------------------------
-enum { kSmall = 0, kCached = 1, kStream = 2 };
+enum { kSmall = 0, kCached = 1, kStream = 2, kSmall2 = 3 };
 constexpr int kStreamCap = 4096; // tied rows kept in LDS by the streaming mode
+
+// A few queries of 8193..16384 rows are selected by kSmall2, from keys the
+// selection counts itself (the scoring kernel then counts nothing).
+constexpr bool use_small2(int64_t Q, int64_t max_n) { return max_n > kCandCap && max_n <= 2 * kCandCap && Q <= 64; }
 
 // Keys and output ids of elements e * T + tid (e < E) of a row of at most mx
 // elements (zero past mx).  The map and the row are branched on once, not
@@ -478,7 +486,7 @@ __device__ __forceinline__ void load_small(const SelRow &r, int q, int mx, uint3
 template <bool HIST, int MODE>
 __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspace &ws)
 {
-    constexpr int CAP = MODE == kStream ? kStreamCap : kCandCap;
+    constexpr int CAP = MODE == kStream ? kStreamCap : (MODE == kSmall2 ? 2 * kCandCap : kCandCap);
     constexpr int KB = kB;
     __shared__ Scratch<NT> sh;
     __shared__ uint32_t h0[kHistBins];
@@ -495,8 +503,8 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
     }
     sh.clear_levels();
     int K = 0;
-    if constexpr (MODE == kSmall) {
-        constexpr int E = kCandCap / NT;
+    if constexpr (MODE == kSmall || MODE == kSmall2) {
+        constexpr int E = CAP / NT;
         const int mx = (int)c.max_n;
         uint32_t kk[E];
         int32_t id[E];
@@ -701,6 +709,10 @@ hipError_t launch_k_select(const SelCall &c, const SelWorkspace &ws, hipStream_t
         return hipGetLastError();
     }
     if constexpr (!HIST) {
+        if (use_small2(c.Q, c.max_n)) {
+            hipLaunchKernelGGL((k_select<HIST, kSmall2>), dim3(c.Q), dim3(NT), 0, s, c, ws);
+            return hipGetLastError();
+        }
         if (c.max_n <= kKeyCache) {
             hipLaunchKernelGGL((k_select<HIST, kCached>), dim3(c.Q), dim3(NT), 0, s, c, ws);
             return hipGetLastError();
@@ -915,7 +927,7 @@ int64_t cand_cap(int64_t Q, int64_t max_n) { return use_filter(Q, max_n) ? std::
 
 } // namespace
 
-bool selection_wants_counts(int64_t max_n) { return max_n > kCandCap; }
+bool selection_wants_counts(int64_t Q, int64_t max_n) { return max_n > kCandCap && !use_small2(Q, max_n); }
 
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n)
 {

@@ -281,6 +281,25 @@ def test_long_context_b4_n131072_other_requests(seed):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("N", [12288, 16384])
+def test_decode_b4_sweep_contexts_up_to_16384(N):
+    """The benchmark's context sweep (8K-128K) at the lengths where a few
+    queries' rows of 8193..16384 scores are selected by one workgroup per
+    query that counts the keys itself: every layer of the group full (every
+    score), then the HS group (anchor top-8192 with its nested top-2048)."""
+    h = H()
+    g = synth.long_context_b4(seed=16, N=N, keys_a=False)
+    say(f"sweep context N={N}: cache")
+    cache = h.build_cache(g)
+    qs = h.Queries(g)
+    for l in range(g.G):
+        verify_full(g, l, h.full_layer(g, cache, qs, l), tag=f"sweep N={N} layer {l}")
+    anchor, followers = h.hs_group(g, cache, qs)
+    verify_hs(g, anchor, followers, tag=f"sweep N={N} HS")
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_chunked_prefill_q4096_sampled_rows():
     h = H()
     g = synth.chunked_prefill_q4096()

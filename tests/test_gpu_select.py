@@ -111,6 +111,21 @@ def test_short_rows_exact(lens, distinct, k):
     _check_full(out, n_q, k, f"lens={lens} distinct={distinct}")
 
 
+@pytest.mark.parametrize("lens,distinct,k", [
+    ([16384, 12000, 8193], 1, 2048),     # every score equal: a tie list as long as the longest row
+    ([16384, 9000], 30, 2048),           # long equal runs
+    ([16384, 16000, 10000], 16384, 2048),  # mostly distinct
+    ([16384, 12000], 40, 16384),         # the budget covers every row
+])
+def test_rows_up_to_16384_exact(lens, distinct, k):
+    # a few queries over rows of 8193..16384 scores: one workgroup per query
+    # holds all of a row's keys and counts them itself (no histogram from the
+    # scoring kernel)
+    cache, seq, pos, mv, qt, w, n_q = _setup(61 + distinct, lens, distinct)
+    out = B.score_topk(cache, seq, pos, mv, qt, w, k, keep_scores=True)
+    _check_full(out, n_q, k, f"lens={lens} distinct={distinct}")
+
+
 def test_sign_spanning_scores_exact():
     cache, seq, pos, mv, qt, w, n_q = _setup(5, [3000, 2500], 500, w_sign=True)
     out = B.score_topk(cache, seq, pos, mv, qt, w, 700, keep_scores=True)
@@ -140,6 +155,7 @@ def test_many_queries_stream_exact():
     ([20000, 30000], 100, 8192, 2048),  # long anchor rows: nested selection in the filter
     ([20000, 900], 9, 8192, 2048),     # a sequence shorter than M, massive ties
     ([5000, 3000, 8192], 40, 8192, 2048),  # M covers every row: the anchor keeps all, its top-k nested
+    ([16384, 12000], 60, 8192, 2048),  # anchor rows of up to 16384: the one-workgroup selection counts them
 ])
 def test_hs_exact(lens, distinct, M, k):
     cache, seq, pos, mv, qt, w, n_q = _setup(41 + M, lens, distinct)
