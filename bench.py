@@ -204,6 +204,7 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
 
     if args.counters == "decode":
+        B.fused_filter(B.FUSED_FILTER_OFF)  # the scoring stream alone, as the roofline times it
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -216,6 +217,7 @@ def main() -> int:
         return 0
 
     if args.roofline_only:
+        B.fused_filter(B.FUSED_FILTER_OFF)  # the scoring stream alone (the filter pass in its own kernel)
         scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         sink = torch.empty(1, dtype=torch.float32, device=dev)
         bytes_launch = Bn * N * 2 * r + Bn * (H * r * 2 + H * 4)
@@ -351,9 +353,14 @@ def main() -> int:
     # Roofline of the decode scoring kernel (HIP events bound to each launch's
     # kernel start and end on its launch stream)
     # ------------------------------------------------------------------
-    def kernel_time(fn, cls, reps_):
+    def kernel_time(fn, cls, reps_, fused=False):
+        # Kernel-level timing.  By default the long-row selection's filter
+        # pass runs in a kernel of its own here, so a scoring launch is the
+        # latent stream alone (its roofline); fused=True times the launch as
+        # the decode step runs it, with the filter pass inside.
         B.timing_read(cls)
         B.timing_enable(True)
+        B.fused_filter(B.FUSED_FILTER_ON if fused else B.FUSED_FILTER_OFF)
         try:
             with torch.cuda.stream(stream):
                 for _ in range(reps_):
@@ -361,6 +368,7 @@ def main() -> int:
             torch.cuda.synchronize()
         finally:
             B.timing_enable(False)
+            B.fused_filter(B.FUSED_FILTER_ON)
         tot, n = B.timing_read(cls)
         for other in range(6):  # recycle the events of the other classes
             if other != cls:
@@ -372,6 +380,8 @@ def main() -> int:
     bytes_launch = Bn * N * bytes_row + Bn * bytes_query
     score_ms, n_launch = kernel_time(mode_b, B.LI_KERNEL_SCORE_DECODE, reps)
     sel_ms, _ = kernel_time(mode_b, B.LI_KERNEL_SELECT, reps)
+    fused_ms, _ = kernel_time(mode_b, B.LI_KERNEL_SCORE_DECODE, reps, fused=True)
+    fused_sel_ms, _ = kernel_time(mode_b, B.LI_KERNEL_SELECT, reps, fused=True)
     achieved = bytes_launch / (score_ms * 1e-3) / 1e9
     # cold (the roofline figure): reading 1 GiB of other data between
     # launches evicts the 256 MB Infinity Cache (a read-only scrub leaves no
@@ -404,8 +414,9 @@ def main() -> int:
         ws_l = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, nb, N, H, r, k, 0), dtype=torch.uint8, device=dev)
         out_l = B.TopK(torch.empty((nb, k), dtype=torch.int32, device=dev), torch.empty(nb, dtype=torch.int32, device=dev))
         run_l = lambda: B.score_topk(cache_l, seq_l, pos_l, N, qt_l, w_l, k, ws=ws_l, out=out_l)
-        for _ in range(2):
-            run_l()
+        with torch.cuda.stream(stream):  # the timed launches' stream: warm-ups must not overlap them
+            for _ in range(2):
+                run_l()
         l_ms, _ = kernel_time(run_l, B.LI_KERNEL_SCORE_DECODE, max(reps // 2, 4))
         l_bytes = nb * N * bytes_row + nb * bytes_query
         large[f"B{nb}"] = {"bytes_per_launch": l_bytes, "avg_launch_us": round(l_ms * 1e3, 2),
@@ -430,6 +441,10 @@ def main() -> int:
         "warm_achieved_GBs": round(achieved, 1), "warm_frac": round(achieved / HBM_PEAK_GBS, 4),
         "beyond_llc": large,
         "select_us_per_layer": round(sel_ms * 1e3, 2),
+        "with_fused_filter": {"score_plus_filter_us": round(fused_ms * 1e3, 2),
+                              "select_after_us": round(fused_sel_ms * 1e3, 2),
+                              "note": "the decode step's form: the selection's filter pass runs in the scoring "
+                                      "launch; the figures above time the scoring stream alone"},
         "baseline_r128_score_us": round(a_score_ms * 1e3, 2),
         "baseline_r128_GBs": round(a_bytes / (a_score_ms * 1e-3) / 1e9, 1),
         "hs_follower_gather_score_us": round(f_ms * 1e3, 2),

@@ -40,12 +40,15 @@
  *   - LI_ERR_HIP reports a failed launch (detail in li_last_error()).
  *   - Calls on different streams are independent; calls that share output
  *     or workspace buffers must be ordered by the caller.
- *   - Two environment variables, read once per process, choose between
- *     equivalent kernels (results are the same within rounding):
+ *   - Three environment variables, read once per process, choose between
+ *     equivalent kernels (results are the same within rounding, and up to
+ *     the order among equal scores):
  *     LI_DECODE_PATH=lds|vgpr forces the LDS-ring or the register-staged
  *     decode scoring kernel; LI_STREAM_NT=0|1 forces the non-temporal read
  *     policy of the decode latent stream off or on (default: on for
- *     launches that read 128 MiB or more).
+ *     launches that read 128 MiB or more); LI_FUSED_FILTER=0 starts with
+ *     the long-row selection's filter pass in a kernel of its own (see
+ *     li_fused_filter).
  */
 #ifndef LATENTINDEX_H
 #define LATENTINDEX_H
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LI_ABI_VERSION 3
+#define LI_ABI_VERSION 4
 #define LI_API __attribute__((visibility("default")))
 #define LI_PAGE_SIZE 64      /* rows per cache page                        */
 #define LI_MAX_HEADS 64      /* indexer heads per query                    */
@@ -329,6 +332,30 @@ typedef enum {
 } li_kernel_class;
 LI_API li_status li_timing_enable(int on);
 LI_API li_status li_timing_read(int kernel_class, double *total_ms, int64_t *launches);
+
+/*
+ * Where the filter pass of a long-row decode selection runs (li_score_topk
+ * with at most 64 queries over rows longer than 16384, its first radix
+ * digit counted by the scoring kernel).  The pass finds the digit on which
+ * the k-th largest score lies and sorts each row into "above" (selected)
+ * and "on" (tied, resolved by the final kernel); LatentIndex (paperlayer.ai
+ * summary of arXiv:2610.04635), §3.1/§4.1 (per-layer top-k), §3.2 (the HS
+ * anchor's nested top-k).
+ *   mode 1 (default): inside the decode scoring kernel, when its grid fits
+ *          the GPU at once: each workgroup waits (a bounded wait, 1 ms) for
+ *          the query's histogram to be complete, then sorts the rows it
+ *          holds in LDS.  If the wait runs out (other work held CUs
+ *          meanwhile, e.g. another stream's kernels), the final kernel
+ *          selects that query again from its scores alone.
+ *   mode 0: a kernel of its own after scoring.
+ *   mode 2: as 1 with a wait that always runs out at once, so every query
+ *          takes the final kernel's fallback (for testing that path).
+ * Results are the same in every mode up to the order among equal scores.
+ * Process-wide, applies to calls made after it; the initial mode is 1, or
+ * 0 when the environment variable LI_FUSED_FILTER=0 is set.  Returns
+ * LI_ERR_SHAPE for a mode outside 0..2.
+ */
+LI_API li_status li_fused_filter(int mode);
 
 /*
  * Phase records of the decode scoring kernels (instrumentation; only the

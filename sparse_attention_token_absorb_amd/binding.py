@@ -24,7 +24,8 @@ LI_OP_SCORE_TOPK, LI_OP_HS_SELECT, LI_OP_SCORE_TOPK_EXT_SCORES = 0, 1, 2
 PAGE_SIZE = 64
 EXPORTED = ["li_append_latent", "li_append_latent_rope", "li_rope_decoder", "li_query_bias", "li_absorb_query",
             "li_score_topk", "li_score_topk_noalloc", "li_hs_select", "li_workspace_bytes", "li_fp8_query_bytes", "li_fp8_query_scale_offset",
-            "li_timing_enable", "li_timing_read", "li_phase_records", "li_status_str", "li_last_error", "li_abi_version"]
+            "li_timing_enable", "li_timing_read", "li_fused_filter", "li_phase_records", "li_status_str", "li_last_error",
+            "li_abi_version"]
 (LI_KERNEL_SCORE_DECODE, LI_KERNEL_SCORE_PREFILL, LI_KERNEL_SCORE_GATHER, LI_KERNEL_SELECT, LI_KERNEL_ABSORB,
  LI_KERNEL_APPEND) = range(6)
 
@@ -86,6 +87,8 @@ def lib():
         L.li_timing_enable.restype = ctypes.c_int
         L.li_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.li_timing_read.restype = ctypes.c_int
+        L.li_fused_filter.argtypes = [ctypes.c_int]
+        L.li_fused_filter.restype = ctypes.c_int
         L.li_phase_records.argtypes = [ctypes.c_int, vp, sz]
         L.li_phase_records.restype = ctypes.c_int
         for f in ("li_append_latent", "li_absorb_query", "li_score_topk", "li_hs_select"):
@@ -225,6 +228,16 @@ def _queries(cache: LatentCache, seq: torch.Tensor, pos: torch.Tensor, max_valid
 def timing_enable(on: bool) -> None:
     """li_timing_enable: bracket every kernel-class launch with HIP events."""
     _check(lib().li_timing_enable(1 if on else 0), "li_timing_enable")
+
+
+FUSED_FILTER_OFF, FUSED_FILTER_ON, FUSED_FILTER_FALLBACK = 0, 1, 2
+
+
+def fused_filter(mode: int) -> None:
+    """li_fused_filter: where the long-row selection's filter pass runs
+    (0: its own kernel, 1: inside the decode scoring kernel, 2: as 1 with a
+    wait that always runs out, so the final kernel's fallback runs)."""
+    _check(lib().li_fused_filter(int(mode)), "li_fused_filter")
 
 
 def timing_read(kernel_class: int) -> Tuple[float, int]:

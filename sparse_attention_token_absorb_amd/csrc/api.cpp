@@ -10,6 +10,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -133,6 +134,26 @@ bool stream_nt(int64_t bytes)
     if (over >= 0) return over == 1;
     return bytes >= kStreamNtBytes;
 }
+
+// Where the filter pass of long-row decode selection runs (li_fused_filter):
+// 0 its own kernel, 1 inside the scoring kernel when its grid is resident at
+// once (see li::FilterArgs), 2 as 1 with a wait that always runs out.
+std::atomic<int> g_fused_filter{-1};
+
+int fused_filter_mode()
+{
+    int m = g_fused_filter.load(std::memory_order_relaxed);
+    if (m < 0) {
+        const char *e = getenv("LI_FUSED_FILTER");
+        int init = e && strcmp(e, "0") == 0 ? 0 : 1;
+        g_fused_filter.compare_exchange_strong(m, init);
+        m = g_fused_filter.load(std::memory_order_relaxed);
+    }
+    return m;
+}
+
+// The fused pass's bound on its wait: 1 ms of the 100 MHz constant clock.
+constexpr uint32_t kFilterWaitTicks = 100000;
 
 li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt, const float *w, int32_t H)
 {
@@ -358,6 +379,7 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
     const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8)) &&
                             li::selection_wants_counts(Q, queries->max_valid);
     hipError_t e = hipSuccess;
+    bool filtered = false;
     if (scored) {
         if (fused_hist) {
             li::TimedScope ts(LI_KERNEL_SELECT, stream);
@@ -372,17 +394,22 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
         a.hist = fused_hist ? sw.hist : nullptr;
         const int64_t row_bytes = fp8 ? cache->r + cache->r / 128 * 4 : (int64_t)cache->r * (cache->dtype == LI_BF16 ? 2 : 4);
         a.stream_nt = !many && stream_nt((int64_t)Q * queries->max_valid * row_bytes);
+        // the selection's filter pass, offered to the scoring kernel
+        const int fmode = fused_filter_mode();
+        a.flt = li::FilterArgs{fused_hist && fmode > 0 && li::selection_filters(Q, queries->max_valid),
+                               k, k_inner, idx, idx_inner, sw.cand, sw.cand2, sw.cap,
+                               fmode == 2 ? 0u : kFilterWaitTicks};
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream, true);
         if (fp8)
             e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, many,
-                                     queries->max_valid, stream);
+                                     queries->max_valid, stream, &filtered);
         else
-            e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream);
+            e = li::launch_score(a, cache->r, cache->dtype == LI_BF16, many, queries->max_valid, stream, &filtered);
         if (e != hipSuccess) return hip_fail(e, "score launch");
     }
     {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
-        e = li::launch_select(sc, sw, fused_hist, stream);
+        e = li::launch_select(sc, sw, fused_hist, stream, filtered);
     }
     if (e != hipSuccess) return hip_fail(e, "select launch");
 
@@ -581,6 +608,13 @@ size_t li_fp8_query_bytes(int32_t Q, int32_t H, int32_t r)
 {
     if (Q < 0 || H <= 0 || H > LI_MAX_HEADS || !r_supported(r, LI_FP8)) return 0;
     return (size_t)li::fp8_query_scale_offset(Q, H, r) + (size_t)Q * H * (r / 128) * 4;
+}
+
+li_status li_fused_filter(int mode)
+{
+    if (mode < 0 || mode > 2) return fail(LI_ERR_SHAPE, "fused filter mode %d outside [0, 2]", mode);
+    g_fused_filter.store(mode, std::memory_order_relaxed);
+    return ok();
 }
 
 li_status li_timing_enable(int on)

@@ -25,6 +25,7 @@
 #include "li_device.hpp"
 #include "li_internal.hpp"
 #include "li_probe.hpp"
+#include "li_tail.hpp"
 #include "li_timing.hpp"
 
 #include <algorithm>
@@ -688,21 +689,10 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     LI_PHASE_SYNC;
     // The scores leave in one coalesced pass over the workgroup's rows (score
     // stores among the stream's loads interleave DRAM writes with the read
-    // stream), which also counts their first radix digit.
-    float *out = a.out + (int64_t)q * a.out_ld;
+    // stream), which also counts their first radix digit; the fused filter
+    // pass follows when asked for.
     const int rows = (int)min64(4 * (int64_t)tiles_per_wave * kTile, n - row0);
-    if (a.hist) {
-        for (int j = threadIdx.x; j < rows; j += 256) {
-            const float p = ((const __attribute__((address_space(3))) float *)s_out)[j];
-            out[row0 + j] = p;
-            atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
-        }
-        __syncthreads();
-        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
-    } else {
-        for (int j = threadIdx.x; j < rows; j += 256)
-            out[row0 + j] = ((const __attribute__((address_space(3))) float *)s_out)[j];
-    }
+    score_tail(a, q, row0, rows, n, (const lds_f32 *)s_out, s_hist, (FilterLds *)ring_raw);
     LI_PHASE_STORE(g_phase_fp8, wv, lane);
 }
 
@@ -965,7 +955,7 @@ hipError_t launch_prefill_fp8_rh(const ScoreArgs &a, const float *pool_scales, i
 
 template <int R, int HB>
 hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int64_t max_rows,
-                               hipStream_t s)
+                               hipStream_t s, bool *filtered)
 {
     // ring next to the histogram, the staged scores (64 tiles per wave, 16 in
     // gather mode) and, in gather mode, the row table: 3 slots at r = 256,
@@ -982,26 +972,30 @@ hipError_t launch_score_fp8_rh(const ScoreArgs &a, const float *pool_scales, int
     if (!a.cand && tpw > kMaxTilesPerWaveF8) tpw = kMaxTilesPerWaveF8;
     const int64_t wgs = (tiles + 4 * tpw - 1) / (4 * tpw);
     const dim3 grid((unsigned)wgs, a.Q);
-    if (a.cand)
-        return launch_kernel(k_score_fp8<R, HB, true, NBG, false>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+    // the filter pass rides along when every workgroup of the grid is resident
+    ScoreArgs b = a;
+    b.flt.on = a.flt.on && !a.cand && a.hist && fused_filter_fits(wgs, a.Q);
+    if (filtered) *filtered = b.flt.on;
+    if (b.cand)
+        return launch_kernel(k_score_fp8<R, HB, true, NBG, false>, grid, dim3(256), 0, s, b, pool_scales, qscale_off,
                              (int)tpw);
-    if (a.stream_nt)
-        return launch_kernel(k_score_fp8<R, HB, false, NB, true>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+    if (b.stream_nt)
+        return launch_kernel(k_score_fp8<R, HB, false, NB, true>, grid, dim3(256), 0, s, b, pool_scales, qscale_off,
                              (int)tpw);
-    return launch_kernel(k_score_fp8<R, HB, false, NB, false>, grid, dim3(256), 0, s, a, pool_scales, qscale_off,
+    return launch_kernel(k_score_fp8<R, HB, false, NB, false>, grid, dim3(256), 0, s, b, pool_scales, qscale_off,
                          (int)tpw);
 }
 
 template <int R>
 hipError_t launch_score_fp8_r(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, bool prefill,
-                              int64_t max_rows, hipStream_t s)
+                              int64_t max_rows, hipStream_t s, bool *filtered)
 {
     if (prefill) {
         if (a.H <= 32) return launch_prefill_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s);
         return launch_prefill_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
     }
-    if (a.H <= 32) return launch_score_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s);
-    return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s);
+    if (a.H <= 32) return launch_score_fp8_rh<R, 1>(a, pool_scales, qscale_off, max_rows, s, filtered);
+    return launch_score_fp8_rh<R, 2>(a, pool_scales, qscale_off, max_rows, s, filtered);
 }
 
 template <int R, int D, bool IDENT = false>
@@ -1089,12 +1083,13 @@ hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH,
 }
 
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
-                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s)
+                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s, bool *filtered)
 {
+    if (filtered) *filtered = false;
     if (a.Q <= 0 || max_rows <= 0) return hipSuccess;
     const bool prefill = many_queries_per_seq && a.cand == nullptr && a.hist == nullptr;
-    if (r == 256) return launch_score_fp8_r<256>(a, pool_scales, qscale_off, prefill, max_rows, s);
-    if (r == 128) return launch_score_fp8_r<128>(a, pool_scales, qscale_off, prefill, max_rows, s);
+    if (r == 256) return launch_score_fp8_r<256>(a, pool_scales, qscale_off, prefill, max_rows, s, filtered);
+    if (r == 128) return launch_score_fp8_r<128>(a, pool_scales, qscale_off, prefill, max_rows, s, filtered);
     return hipErrorInvalidValue;
 }
 

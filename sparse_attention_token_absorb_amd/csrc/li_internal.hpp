@@ -10,7 +10,7 @@
 namespace li {
 
 constexpr int kHistBins = 4096;   // first radix digit: key bits [31:20]
-constexpr int kHistStride = kHistBins + 8; // per query: histogram, then the slots below
+constexpr int kHistStride = kHistBins + 16; // per query: histogram, then the slots below
 constexpr int kSelThreads = 1024; // threads of the per-query selection workgroup
 
 // Per-query slots after the histogram.
@@ -23,6 +23,27 @@ enum {
     kSlotBins = kHistBins + 5,   // threshold digits found by the filter: outer | inner << 16 (-1: none)
     kSlotAboveO = kHistBins + 6, // rows in digits above the outer threshold digit
     kSlotAboveI = kHistBins + 7, // the same for the inner one
+    kSlotTotal = kHistBins + 8,  // rows counted into the histogram so far (fused filter pass)
+    kSlotErr = kHistBins + 9,    // nonzero: a fused filter pass gave up waiting (the final kernel redoes the query)
+};
+
+// The filter pass of a long-row selection, run inside the decode scoring
+// kernel (on: the launcher guarantees that every workgroup of the grid is
+// resident at once).  Once every workgroup of a query has added its scores'
+// first digits to the histogram, each one finds the threshold digits from it
+// and emits, from the scores it holds in LDS, its rows above them to idx /
+// idx_inner and its rows on them to the tie lists cand / cand2 (the
+// selection's workspace), as the separate filter kernel would.
+struct FilterArgs {
+    bool on;
+    int32_t k;
+    int32_t k_inner; // 0: no nested selection
+    int32_t *idx;    // [Q][k]
+    int32_t *idx_inner;
+    uint2 *cand; // [Q][cap]
+    uint2 *cand2;
+    int64_t cap;
+    uint32_t wait_ticks; // bound on the wait for the query's histogram (100 MHz clock ticks)
 };
 
 // Geometry of a paged pool, for bounding device-resident indices.
@@ -69,11 +90,19 @@ struct ScoreArgs {
     int32_t *hist;    // optional [Q][kHistStride]: first-digit counts of the keys written
                       // (accumulated) and the query's row count in slot kSlotN
     bool stream_nt;   // latent rows are read with the non-temporal policy (not kept in the caches)
+    FilterArgs flt;   // optional fused filter pass (contiguous decode with a histogram only)
 };
 
 // Scoring.  `max_rows` bounds every query's row count (grid sizing).
+// filtered (optional): set to whether the launch ran the fused filter pass
+// that a.flt asked for (the selection then skips its own filter kernel).
 hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq,
-                        int64_t max_rows, hipStream_t s);
+                        int64_t max_rows, hipStream_t s, bool *filtered = nullptr);
+
+// Compute units of the current device (0 if unknown), and whether a decode
+// scoring grid of wgs_per_query x Q workgroups is resident all at once.
+int device_cu_count();
+bool fused_filter_fits(int64_t wgs_per_query, int64_t Q);
 
 // out[q][j] = S[q][cand[q][j]] for j < min(cand_count[q], M) (candidates
 // clamped into [0, ld)); entries past the count are left untouched.
@@ -101,7 +130,7 @@ hipError_t launch_append_fp8(void *pool, float *scales, const int32_t *bt, const
                              const int32_t *seq, const int32_t *pos, int T, const RopeArgs &rope, hipStream_t s);
 hipError_t launch_absorb_fp8(const void *q, const void *W, void *qt, int64_t QH, int d, int r, hipStream_t s);
 hipError_t launch_score_fp8(const ScoreArgs &a, const float *pool_scales, int64_t qscale_off, int r,
-                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s);
+                            bool many_queries_per_seq, int64_t max_rows, hipStream_t s, bool *filtered = nullptr);
 
 // Append rows into the paged pool.
 hipError_t launch_append(void *pool, const int32_t *bt, const PoolGeom &geo, int r, int esize, const void *rows,
@@ -156,8 +185,16 @@ SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n);
 // Zero the histograms (before a scoring kernel accumulates into them).
 hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s);
 // The selection proper (after scores exist).  have_hist: a scoring kernel
-// filled ws.hist (histogram and row counts) for these very scores.
-hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s);
+// filled ws.hist (histogram and row counts) for these very scores; filtered:
+// it also ran the filter pass (ScoreArgs::flt), so only the tie resolution
+// is left.
+hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s,
+                         bool filtered = false);
+
+// Whether the selection of Q queries over rows of up to max_n scores takes
+// the filter path (many workgroups per query, then the tie resolution),
+// whose filter pass a decode scoring kernel can run (ScoreArgs::flt).
+bool selection_filters(int64_t Q, int64_t max_n);
 
 // Whether a selection of Q queries over rows of up to max_n scores wants the
 // scoring kernel to count the first radix digit: rows of up to 8192 scores,

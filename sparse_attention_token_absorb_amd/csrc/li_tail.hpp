@@ -1,0 +1,197 @@
+// The tail of the decode scoring kernels (gfx950): the staged scores leave
+// in one pass per workgroup, which also counts their first radix digit, and
+// optionally the filter pass of the top-k selection runs right there, on
+// the scores the workgroup still holds in LDS.
+//
+// LatentIndex (paperlayer.ai summary of arXiv:2610.04635), §3.1/§4.1 and
+// §C.4: each layer keeps its own top-k rows of the valid prefix (the HS
+// anchor its top-M and, nested in them, its top-k).  The selection is a
+// radix select on order-preserving keys; its first pass finds the digit on
+// which the k-th largest key lies (from the query's first-digit histogram)
+// and splits the rows into those above it (selected) and those on it (tied,
+// resolved later by the remaining digits).
+#pragma once
+
+#include "li_device.hpp"
+#include "li_internal.hpp"
+#include "li_radix.hpp"
+
+namespace li {
+namespace {
+
+// LDS scratch of the fused filter pass, carved from the chunk ring (which
+// the stream no longer uses by then).
+struct FilterLds {
+    uint32_t wtot[4];
+    int res[4];
+    int cnt[4];
+    int base[4];
+    int err;
+};
+
+
+
+// Loads and adds at agent scope: performed where every XCD sees them (not in
+// this XCD's L2), so workgroups on different XCDs exchange counts without a
+// cache writeback or invalidate.
+__device__ __forceinline__ int load_agent(int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int add_agent(int32_t *p, int v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The filter pass over this workgroup's rows row0 .. row0 + rows - 1 of
+// query q (n rows in all), their scores in s_out; the workgroup's digit
+// counts and its row count are already being added into the query's
+// histogram hq and its row total (all 256 threads).
+__device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t row0, int rows, int n,
+                                            const lds_f32 *s_out, uint32_t *s_hist, int32_t *hq, FilterLds *fl)
+{
+    const int tid = threadIdx.x;
+    const FilterArgs &f = a.flt;
+    const int K = min(n, f.k);
+    const int Ki = f.k_inner > 0 ? min(n, f.k_inner) : 0;
+    const uint32_t rem[2] = {(uint32_t)K, (uint32_t)(Ki > 0 ? Ki : K)};
+    if (tid < 4) fl->cnt[tid] = 0;
+    // Wait for the whole histogram: once the row total reaches n every
+    // workgroup has issued its adds, and a histogram whose bins sum to n holds
+    // every add (no bin reads more than its final count), so a sum short of n
+    // is read again.  No cache writeback or invalidate is involved.  The
+    // launcher fuses the pass only when the whole grid fits the GPU at once,
+    // so the wait normally ends within microseconds; it is bounded
+    // (f.wait_ticks of the 100 MHz constant clock) because other work can
+    // hold CUs meanwhile (another stream's kernels, another fused launch
+    // waiting the same way).  A workgroup whose wait runs out records it in
+    // the query's error slot and leaves; the final kernel then selects that
+    // query again from its scores alone.
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        if (tid == 0) {
+            int err = __builtin_amdgcn_s_memrealtime() - t0 >= f.wait_ticks;
+            while (!err && load_agent(hq + kSlotTotal) < n) {
+                __builtin_amdgcn_s_sleep(2);
+                err = __builtin_amdgcn_s_memrealtime() - t0 >= f.wait_ticks;
+            }
+            if (err) add_agent(hq + kSlotErr, 1);
+            fl->err = err;
+        }
+        __syncthreads();
+        if (fl->err) return;
+        constexpr int PB = kHistBins / 256;
+        uint32_t hv[PB];
+#pragma unroll
+        for (int e = 0; e < PB; ++e) hv[e] = (uint32_t)load_agent(hq + e * 256 + tid);
+#pragma unroll
+        for (int e = 0; e < PB; ++e) s_hist[e * 256 + tid] = hv[e];
+        __syncthreads();
+        find_bins<256, kHistBins, 2>(s_hist, rem, *fl);
+        const uint32_t total = fl->wtot[0] + fl->wtot[1] + fl->wtot[2] + fl->wtot[3];
+        if (total == (uint32_t)n) break;
+        __syncthreads(); // every thread has read this round's results
+        __builtin_amdgcn_s_sleep(2);
+    }
+    const int bin = fl->res[0];
+    const int bin_i = Ki > 0 ? fl->res[2] : -1;
+    if (blockIdx.x == 0 && tid == 0) { // every workgroup finds the same digits; the final kernel reads them here
+        hq[kSlotBins] = (int32_t)(((uint32_t)fl->res[0] & 0xFFFFu) | ((uint32_t)fl->res[2] << 16));
+        hq[kSlotAboveO] = fl->res[1];
+        hq[kSlotAboveI] = fl->res[3];
+    }
+    if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
+    const bool inner = Ki > 0;
+    const bool sep = inner && bin_i != bin; // inner ties need a list of their own
+    int nup = 0, ntie = 0, nupi = 0, ntiei = 0;
+    for (int j = tid; j < rows; j += 256) {
+        const int dg = (int)(score_key(s_out[j]) >> kDigit0Shift);
+        nup += dg > bin;
+        ntie += dg == bin;
+        if (inner) {
+            nupi += dg > bin_i;
+            ntiei += sep && dg == bin_i;
+        }
+    }
+    // this thread's offsets in the workgroup's four runs: an exclusive wave
+    // scan plus one LDS atomic per wave and run, then one global add per run
+    const int cnts[4] = {nup, ntie, nupi, ntiei};
+    int loc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t incl = wave_incl_scan((uint32_t)cnts[j]);
+        const int wt = __builtin_amdgcn_readlane((int)incl, 63);
+        int wb = 0;
+        if (wt && (tid & 63) == 0) wb = atomicAdd(&fl->cnt[j], wt);
+        wb = __builtin_amdgcn_readfirstlane(wb);
+        loc[j] = wb + (int)incl - cnts[j];
+    }
+    __syncthreads();
+    if (tid < 4) {
+        const int slot = tid == 0 ? kSlotUpO : tid == 1 ? kSlotTieO : tid == 2 ? kSlotUpI : kSlotTieI;
+        const int v = fl->cnt[tid];
+        fl->base[tid] = v ? add_agent(hq + slot, v) : 0;
+    }
+    __syncthreads();
+    int pu = fl->base[0] + loc[0], pt = fl->base[1] + loc[1], pui = fl->base[2] + loc[2], pti = fl->base[3] + loc[3];
+    int32_t *out = f.idx + (int64_t)q * f.k;
+    int32_t *outi = inner ? f.idx_inner + (int64_t)q * f.k_inner : nullptr;
+    uint2 *cand = f.cand + (int64_t)q * f.cap;
+    uint2 *cand2 = f.cand2 + (int64_t)q * f.cap;
+    for (int j = tid; j < rows; j += 256) {
+        const uint32_t key = score_key(s_out[j]);
+        const int dg = (int)(key >> kDigit0Shift);
+        const int32_t i = (int32_t)(row0 + j);
+        if (dg > bin) {
+            if (pu < f.k) out[pu] = i;
+            ++pu;
+        } else if (dg == bin) {
+            if (pt < f.cap) cand[pt] = make_uint2(key, (uint32_t)i);
+            ++pt;
+        }
+        if (inner) {
+            if (dg > bin_i) {
+                if (pui < f.k_inner) outi[pui] = i;
+                ++pui;
+            } else if (sep && dg == bin_i) {
+                if (pti < f.cap) cand2[pti] = make_uint2(key, (uint32_t)i);
+                ++pti;
+            }
+        }
+    }
+}
+
+// After the stream, with every row's score staged in s_out (workgroup-local
+// row j is row row0 + j of query q, j < rows): the scores leave in one
+// coalesced pass; with a histogram, their first radix digits are counted in
+// LDS and merged into the query's histogram (non-empty bins only), and with
+// the fused filter pass the scores leave after it (nothing in this launch
+// reads them).  All 256 threads.
+__device__ __forceinline__ void score_tail(const ScoreArgs &a, int q, int64_t row0, int rows, int n,
+                                           const lds_f32 *s_out, uint32_t *s_hist, FilterLds *fl)
+{
+    const int tid = threadIdx.x;
+    float *out = a.out + (int64_t)q * a.out_ld;
+    if (!a.hist) {
+        for (int j = tid; j < rows; j += 256) out[row0 + j] = s_out[j];
+        return;
+    }
+    int32_t *hq = a.hist + (int64_t)q * kHistStride;
+    const bool fused = a.flt.on;
+    for (int j = tid; j < rows; j += 256) {
+        const float p = s_out[j];
+        if (!fused) out[row0 + j] = p;
+        atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+    }
+    __syncthreads();
+    hist_flush(s_hist, hq, 256, tid);
+    if (!fused) return;
+    __syncthreads(); // every thread has issued its adds (and read s_hist, which the filter pass reuses)
+    if (tid == 0) add_agent(hq + kSlotTotal, rows);
+    filter_pass(a, q, row0, rows, n, s_out, s_hist, hq, fl);
+    for (int j = tid; j < rows; j += 256) out[row0 + j] = s_out[j];
+}
+
+} // namespace
+} // namespace li

@@ -21,6 +21,7 @@
 #include "li_device.hpp"
 #include "li_internal.hpp"
 #include "li_probe.hpp"
+#include "li_tail.hpp"
 #include "li_timing.hpp"
 
 #include <stdlib.h>
@@ -443,20 +444,10 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     __syncthreads(); // every wave's scores are in LDS
     LI_PHASE_SYNC;
     // The scores leave in one pass over the workgroup's rows, which also
-    // counts their first radix digit (kept out of the stream above).
-    float *out = a.out + (int64_t)q * a.out_ld;
+    // counts their first radix digit (kept out of the stream above), and
+    // the fused filter pass follows when asked for.
     const int rows = (int)min64(4 * (int64_t)tiles_per_wave * kTile, n - row0);
-    if (a.hist) {
-        for (int j = threadIdx.x; j < rows; j += 256) {
-            const float p = ((const lds_f32 *)s_out)[j];
-            out[row0 + j] = p;
-            atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
-        }
-        __syncthreads();
-        hist_flush(s_hist, a.hist + (int64_t)q * kHistStride, 256, threadIdx.x);
-    } else {
-        for (int j = threadIdx.x; j < rows; j += 256) out[row0 + j] = ((const lds_f32 *)s_out)[j];
-    }
+    score_tail(a, q, row0, rows, n, (const lds_f32 *)s_out, s_hist, (FilterLds *)ring_raw);
     LI_PHASE_STORE(g_phase_bf16, wv, lane);
 }
 
@@ -848,7 +839,7 @@ bool use_vgpr_decode(int r, bool gather)
 }
 
 template <int R, int HB>
-hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStream_t s)
+hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStream_t s, bool *filtered)
 {
     const int64_t tiles = (max_rows + kTile - 1) / kTile;
     if (prefill) {
@@ -894,22 +885,26 @@ hipError_t launch_bf16(const ScoreArgs &a, bool prefill, int64_t max_rows, hipSt
     // chunk ring: 96 KiB next to the histogram and the staged scores
     constexpr int CPT = R == 256 ? 2 : 1;
     constexpr int NB = R == 64 ? 6 : 3;
+    // the filter pass rides along when every workgroup of the grid is resident
+    ScoreArgs b = a;
+    b.flt.on = a.flt.on && !a.cand && a.hist && fused_filter_fits(wgs, a.Q);
+    if (filtered) *filtered = b.flt.on;
     auto go = [&](auto BIASc) {
         constexpr bool BI = decltype(BIASc)::value;
-        const dim3 grid((unsigned)wgs, a.Q);
-        if (a.cand) return launch_kernel(k_score_decode<R, HB, true, NB, CPT, false, BI>, grid, dim3(256), 0, s, a, (int)tpw);
-        if (a.stream_nt)
-            return launch_kernel(k_score_decode<R, HB, false, NB, CPT, true, BI>, grid, dim3(256), 0, s, a, (int)tpw);
-        return launch_kernel(k_score_decode<R, HB, false, NB, CPT, false, BI>, grid, dim3(256), 0, s, a, (int)tpw);
+        const dim3 grid((unsigned)wgs, b.Q);
+        if (b.cand) return launch_kernel(k_score_decode<R, HB, true, NB, CPT, false, BI>, grid, dim3(256), 0, s, b, (int)tpw);
+        if (b.stream_nt)
+            return launch_kernel(k_score_decode<R, HB, false, NB, CPT, true, BI>, grid, dim3(256), 0, s, b, (int)tpw);
+        return launch_kernel(k_score_decode<R, HB, false, NB, CPT, false, BI>, grid, dim3(256), 0, s, b, (int)tpw);
     };
-    return a.bias ? go(std::true_type{}) : go(std::false_type{});
+    return b.bias ? go(std::true_type{}) : go(std::false_type{});
 }
 
 template <int R>
-hipError_t launch_r(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStream_t s)
+hipError_t launch_r(const ScoreArgs &a, bool prefill, int64_t max_rows, hipStream_t s, bool *filtered)
 {
-    if (a.H <= 32) return launch_bf16<R, 1>(a, prefill, max_rows, s);
-    return launch_bf16<R, 2>(a, prefill, max_rows, s);
+    if (a.H <= 32) return launch_bf16<R, 1>(a, prefill, max_rows, s, filtered);
+    return launch_bf16<R, 2>(a, prefill, max_rows, s, filtered);
 }
 
 // Candidate scores from scores kept by position.
@@ -946,9 +941,30 @@ hipError_t launch_gather_scores(const float *S, int64_t ld, const int32_t *cand,
     return hipGetLastError();
 }
 
-hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq, int64_t max_rows,
-                        hipStream_t s)
+int device_cu_count()
 {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+bool fused_filter_fits(int64_t wgs_per_query, int64_t Q)
+{
+    // one decode scoring workgroup per CU fits (its LDS allows no more), so
+    // a grid of at most one workgroup per CU is resident at once
+    return wgs_per_query * Q <= device_cu_count();
+}
+
+hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_per_seq, int64_t max_rows,
+                        hipStream_t s, bool *filtered)
+{
+    if (filtered) *filtered = false;
     if (a.Q <= 0 || max_rows <= 0) return hipSuccess;
     const bool prefill = many_queries_per_seq && a.cand == nullptr;
     if (!bf16) {
@@ -958,9 +974,9 @@ hipError_t launch_score(const ScoreArgs &a, int r, bool bf16, bool many_queries_
                              (int)per);
     }
     switch (r) {
-    case 64: return launch_r<64>(a, prefill, max_rows, s);
-    case 128: return launch_r<128>(a, prefill, max_rows, s);
-    case 256: return launch_r<256>(a, prefill, max_rows, s);
+    case 64: return launch_r<64>(a, prefill, max_rows, s, filtered);
+    case 128: return launch_r<128>(a, prefill, max_rows, s, filtered);
+    case 256: return launch_r<256>(a, prefill, max_rows, s, filtered);
     default: return hipErrorInvalidValue;
     }
 }

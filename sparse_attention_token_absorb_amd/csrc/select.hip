@@ -30,6 +30,7 @@
 // the budget needs: equal scores are interchangeable, and the fixed order
 // keeps nested selections nested.
 #include "li_internal.hpp"
+#include "li_radix.hpp"
 
 #include <algorithm>
 
@@ -92,24 +93,6 @@ __device__ __forceinline__ int query_n(const SelCall &c, int q)
     return clamp_n(n, c.max_n);
 }
 
-__device__ __forceinline__ uint64_t lanes_below() { return (1ull << (threadIdx.x & 63)) - 1ull; }
-
-// Inclusive prefix sum over the lanes of a wave (lane 0 first), on DPP: row
-// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the last lane of
-// row 0 (and of row 2) is added to row 1 (row 3), and that of row 1 to rows
-// 2 and 3.  Lanes without a source read 0.  Whole waves must reach it.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
-{
-    int v = (int)x;
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
-    return (uint32_t)v;
-}
-
 // Smallest and largest of x over the wave (unsigned), in every lane: DPP
 // row shifts leave each row's extreme in its last lane (a lane without a
 // source keeps its own value), and the four rows are combined by readlane.
@@ -167,58 +150,6 @@ struct HistRegs {
         for (int e = 0; e < kHistBins / T; ++e) h[e * T + threadIdx.x] = v[e];
     }
 };
-
-// Block-wide search on an LDS histogram of NB bins (bin order = key order)
-// for NR budgets at once: for budget j, sh.res[2j] = the bin b holding the
-// rem[j]-th largest element (-1 if rem[j] exceeds the total) and
-// sh.res[2j+1] = elements in bins > b.  Each thread sums a run of adjacent
-// bins, a DPP scan and the wave totals give every thread the count above its
-// run, and the thread whose run crosses a budget searches it.  Two barriers;
-// the caller puts a barrier between its reads of an earlier result and the
-// next call.
-template <int T, int NB, int NR>
-__device__ void find_bins(const uint32_t *h, const uint32_t (&rem)[NR], Scratch<T> &sh)
-{
-    constexpr int NW = T / 64;
-    constexpr int PER = NB >= T ? NB / T : 1; // bins per thread
-    constexpr int ACT = NB / PER;             // threads holding bins
-    static_assert(PER * ACT == NB && NR <= 2, "bins per thread");
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t v[PER];
-    uint32_t s = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        v[j] = tid < ACT ? h[tid * PER + j] : 0u;
-        s += v[j];
-    }
-    // run of this thread and all later ones: the wave's suffix plus later waves
-    const uint32_t p = wave_incl_scan(s);
-    const uint32_t wtotal = (uint32_t)__builtin_amdgcn_readlane((int)p, 63);
-    if (lane == 0) sh.wtot[wv] = wtotal;
-    if (tid < NR) sh.res[2 * tid] = -1;
-    __syncthreads();
-    uint32_t later = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) later += w2 > wv ? sh.wtot[w2] : 0u;
-    const uint32_t incl = wtotal - p + s + later; // elements in this run and above it
-    const uint32_t excl = incl - s;               // elements above this run
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        if (excl < rem[j] && incl >= rem[j]) {
-            uint32_t acc = excl;
-#pragma unroll
-            for (int jj = PER - 1; jj >= 0; --jj) {
-                if (acc + v[jj] >= rem[j]) {
-                    sh.res[2 * j] = tid * PER + jj;
-                    sh.res[2 * j + 1] = (int)acc;
-                    break;
-                }
-                acc += v[jj];
-            }
-        }
-    }
-    __syncthreads();
-}
 
 // Compacting append for U rounds at once: lanes with e[u] set get slots
 // base + (rank in round order, then lane order) from one LDS atomic per
@@ -483,16 +414,21 @@ __device__ __forceinline__ void load_small(const SelRow &r, int q, int mx, uint3
     }
 }
 
-template <bool HIST, int MODE>
-__device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspace &ws)
+template <int MODE>
+constexpr int select_cap()
 {
-    constexpr int CAP = MODE == kStream ? kStreamCap : (MODE == kSmall2 ? 2 * kCandCap : kCandCap);
+    return MODE == kStream ? kStreamCap : (MODE == kSmall2 ? 2 * kCandCap : kCandCap);
+}
+
+// select_query on LDS the caller provides: the digit histogram h0
+// [kHistBins], the tie list ck / ci [select_cap<MODE>()] and, in the cached
+// mode, the key cache [kKeyCache].
+template <bool HIST, int MODE>
+__device__ __forceinline__ void select_query_in(const SelCall &c, const SelWorkspace &ws, Scratch<NT> &sh,
+                                                uint32_t *h0, uint32_t *ck, int32_t *ci, uint32_t *cache)
+{
+    constexpr int CAP = select_cap<MODE>();
     constexpr int KB = kB;
-    __shared__ Scratch<NT> sh;
-    __shared__ uint32_t h0[kHistBins];
-    __shared__ uint32_t ck[CAP];
-    __shared__ int32_t ci[CAP];
-    __shared__ uint32_t cache[MODE == kCached ? kKeyCache : 1];
     const int tid = threadIdx.x;
     const int q = blockIdx.x;
     const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
@@ -687,6 +623,17 @@ __device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspac
 }
 
 template <bool HIST, int MODE>
+__device__ __forceinline__ void select_query(const SelCall &c, const SelWorkspace &ws)
+{
+    __shared__ Scratch<NT> sh;
+    __shared__ uint32_t h0[kHistBins];
+    __shared__ uint32_t ck[select_cap<MODE>()];
+    __shared__ int32_t ci[select_cap<MODE>()];
+    __shared__ uint32_t cache[MODE == kCached ? kKeyCache : 1];
+    select_query_in<HIST, MODE>(c, ws, sh, h0, ck, ci, cache);
+}
+
+template <bool HIST, int MODE>
 __global__ __launch_bounds__(NT) void k_select(SelCall c, SelWorkspace ws)
 {
     select_query<HIST, MODE>(c, ws);
@@ -834,6 +781,31 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
         }
 }
 
+// The whole selection of query blockIdx.x from its scores (the streaming
+// one-workgroup mode), then the nested one over the outer winners: the
+// final kernel's fallback when the fused filter pass did not complete.
+__device__ __forceinline__ void final_from_scores(const SelCall &c, const SelWorkspace &ws, Scratch<NT> &sh,
+                                                  uint32_t *h0, uint32_t *ck, int32_t *ci)
+{
+    SelCall oc = c;
+    oc.k_inner = 0;
+    oc.idx_inner = nullptr;
+    oc.count_inner = nullptr;
+    select_query_in<false, kStream>(oc, ws, sh, h0, ck, ci, nullptr);
+    if (c.k_inner <= 0) return;
+    __syncthreads(); // the outer winners and their count are visible to the whole workgroup
+    SelCall ic = oc;
+    ic.row = SelRow{c.row.S, c.row.ld, c.idx, c.k, c.idx, c.k};
+    ic.src_mode = kSrcCount;
+    ic.cnt = c.count;
+    ic.cnt_cap = c.k;
+    ic.k = c.k_inner;
+    ic.max_n = std::min<int64_t>(c.k, c.max_n);
+    ic.idx = c.idx_inner;
+    ic.count = c.count_inner;
+    select_query_in<false, kStream>(ic, ws, sh, h0, ck, ci, nullptr);
+}
+
 // The remaining digits among the tied rows: blockIdx.y = 0 for the outer
 // selection, 1 for the nested one, one workgroup per query each.
 __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
@@ -867,6 +839,15 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     const int bins = hq[kSlotBins];
     const int above_o = hq[kSlotAboveO];
     const int above_i = hq[kSlotAboveI];
+    if (hq[kSlotErr]) {
+        // Some workgroup of the scoring launch gave up waiting for the others
+        // (the fused filter pass found the grid not all resident at once):
+        // this query's filter results are incomplete, so the selection runs
+        // again from the scores alone, the nested one over the outer winners.
+        static_assert(kHistBins + kStreamCap <= kCandCap && kStreamCap <= kCandCap, "fallback LDS");
+        if (!inner) final_from_scores(c, ws, sh, ck, ck + kHistBins, ci);
+        return;
+    }
     const int K = min(n, c.k);
     const int Kp = inner ? min(n, c.k_inner) : K;
     if (Kp > 0) {
@@ -955,14 +936,18 @@ hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s)
+bool selection_filters(int64_t Q, int64_t max_n) { return use_filter(Q, max_n); }
+
+hipError_t launch_select(const SelCall &c, const SelWorkspace &ws, bool have_hist, hipStream_t s, bool filtered)
 {
     if (c.Q <= 0) return hipSuccess;
     if (have_hist && use_filter(c.Q, c.max_n)) {
-        const int64_t chunks = (c.max_n + kFilterChunk - 1) / kFilterChunk;
-        hipLaunchKernelGGL(k_filter, dim3((unsigned)chunks, c.Q), dim3(kFilterThreads), 0, s, c, ws);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (!filtered) { // else the scoring kernel ran the filter pass
+            const int64_t chunks = (c.max_n + kFilterChunk - 1) / kFilterChunk;
+            hipLaunchKernelGGL(k_filter, dim3((unsigned)chunks, c.Q), dim3(kFilterThreads), 0, s, c, ws);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(k_final, dim3(c.Q, c.k_inner > 0 ? 2 : 1), dim3(NT), 0, s, c, ws);
         return hipGetLastError();
     }

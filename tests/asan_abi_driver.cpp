@@ -140,6 +140,8 @@ int main()
     int64_t n = 0;
     expect(li_timing_read(99, &ms, &n), LI_ERR_SHAPE, "timing class");
     expect(li_timing_read(0, nullptr, &n), LI_ERR_NULL, "timing NULL");
+    expect(li_fused_filter(3), LI_ERR_SHAPE, "fused filter mode");
+    expect(li_fused_filter(1), LI_OK, "fused filter mode 1");
     printf("%s: %d failures\n", failures ? "FAIL" : "ok", failures);
     return failures ? 1 : 0;
 }

@@ -45,7 +45,7 @@ def test_only_the_abi_is_exported():
 
 
 def test_version_and_status_strings(L):
-    assert L.li_abi_version() == 3
+    assert L.li_abi_version() == 4
     assert L.li_status_str(0) == b"LI_OK"
     assert L.li_status_str(4) == b"LI_ERR_WORKSPACE"
     assert L.li_status_str(99) == b"LI_ERR_UNKNOWN"
@@ -59,6 +59,15 @@ def test_phase_records_only_in_the_instrumented_build(L):
     assert L.li_phase_records(B.LI_PHASE_SCORE_DECODE_BF16, buf, ctypes.sizeof(buf)) == B.LI_ERR_UNSUPPORTED
     assert L.li_phase_records(B.LI_PHASE_SCORE_DECODE_FP8, None, 0) == B.LI_ERR_UNSUPPORTED
     assert L.li_phase_records(7, buf, ctypes.sizeof(buf)) == B.LI_ERR_SHAPE
+
+
+def test_fused_filter_mode_knob(L):
+    """li_fused_filter takes modes 0..2 (host state only, no GPU work) and
+    rejects others; the default mode is restored afterwards."""
+    for m in (0, 2, 1):
+        assert L.li_fused_filter(m) == B.LI_OK
+    assert L.li_fused_filter(3) == B.LI_ERR_SHAPE
+    assert L.li_fused_filter(-1) == B.LI_ERR_SHAPE
 
 
 def cache(**kw):

@@ -143,6 +143,23 @@ def test_long_rows_exact(distinct):
     _check_full(out, n_q, 2048, f"long distinct={distinct}", k_inner=512)
 
 
+@pytest.mark.parametrize("mode", [B.FUSED_FILTER_OFF, B.FUSED_FILTER_FALLBACK])
+@pytest.mark.parametrize("distinct", [3, 40000])
+def test_long_rows_exact_in_every_filter_mode(mode, distinct):
+    # the filter pass in a kernel of its own, and the fused pass whose wait
+    # runs out at once (every query then selected again by the final kernel
+    # from its scores alone, the nested selection over the outer winners)
+    B.fused_filter(mode)
+    try:
+        cache, seq, pos, mv, qt, w, n_q = _setup(21, [40000, 23000], distinct)
+        out = B.score_topk(cache, seq, pos, mv, qt, w, 2048, k_inner=512, keep_scores=True)
+        _check_full(out, n_q, 2048, f"long distinct={distinct} mode={mode}", k_inner=512)
+        out = B.score_topk(cache, seq, pos, mv, qt, w, 5000, keep_scores=True)
+        _check_full(out, n_q, 5000, f"long k=5000 distinct={distinct} mode={mode}")
+    finally:
+        B.fused_filter(B.FUSED_FILTER_ON)
+
+
 def test_many_queries_stream_exact():
     # more than 64 queries over rows beyond 8192: the streaming selection
     cache, seq, pos, mv, qt, w, n_q = _setup(31, [12000, 9000, 20000], 60, Q_per_seq=24)
