@@ -296,7 +296,19 @@ LI_API li_status li_hs_select(const li_cache *cache, const li_queries *queries, 
 enum { LI_OP_SCORE_TOPK = 0, LI_OP_HS_SELECT = 1, LI_OP_SCORE_TOPK_EXT_SCORES = 2 };
 
 /* Workspace bytes for `op` at these sizes (M ignored for the score_topk ops,
- * max_valid ignored for LI_OP_HS_SELECT).  0 means invalid sizes. */
+ * max_valid ignored for LI_OP_HS_SELECT).  0 means invalid sizes.
+ * Every workspace starts with a region of LI_WORKSPACE_ZEROED_BYTES that
+ * should be zero before the workspace's first use (e.g. hipMemset once after
+ * allocating it): the long-row selection (at most 64 queries over rows
+ * longer than 16384) keeps each query's first-digit histogram and counters
+ * there instead of clearing them with a kernel of its own, and every call
+ * leaves the region zero again.  A region that is not zero costs time, not
+ * correctness: the selection finds the histogram inconsistent (its bins do
+ * not add up to the row count), selects those queries again from their
+ * scores alone (after a wait of up to 1 ms in li_fused_filter mode 1), and
+ * leaves the region zero.  The workspaces of li_score_topk and li_hs_select
+ * share this layout, so one buffer may serve both (calls in stream order). */
+#define LI_WORKSPACE_ZEROED_BYTES (64 * 4112 * 4)
 LI_API size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32_t r, int32_t k,
                           int32_t M);
 

@@ -270,9 +270,15 @@ def workspace_bytes(op: int, Q: int, max_valid: int, H: int, r: int, k: int, M: 
     return int(lib().li_workspace_bytes(op, Q, max_valid, H, r, k, M))
 
 
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of nbytes, zero-filled: its leading region must be zero
+    before its first use (li_workspace_bytes), and every call leaves it so."""
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
 def _workspace(device, nbytes: int, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is None:
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        return workspace(nbytes, device)
     _need(ws, "ws", torch.uint8, device)
     return ws
 

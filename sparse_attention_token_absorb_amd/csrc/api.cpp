@@ -177,6 +177,8 @@ li::ScoreArgs score_args(const li_cache *c, const li_queries *qs, const void *qt
 
 extern "C" {
 
+static_assert(li::kSyncBytes == ((size_t)LI_WORKSPACE_ZEROED_BYTES + 255) / 256 * 256, "zeroed region size");
+
 int32_t li_abi_version(void) { return LI_ABI_VERSION; }
 
 const char *li_last_error(void) { return g_last_error.c_str(); }
@@ -204,11 +206,11 @@ size_t li_workspace_bytes(int op, int32_t Q, int32_t max_valid, int32_t H, int32
     case LI_OP_SCORE_TOPK_EXT_SCORES: {
         if (max_valid < 0) return 0;
         size_t b = op == LI_OP_SCORE_TOPK ? align256((size_t)Q * score_ld(max_valid) * 4) : 0;
-        return b + align256(li::sel_workspace_bytes(Q, std::max(max_valid, 1)));
+        return li::kSyncBytes + b + align256(li::sel_workspace_bytes(Q, std::max(max_valid, 1)));
     }
     case LI_OP_HS_SELECT:
         if (M <= 0 || M > LI_MAX_TOPK) return 0;
-        return align256((size_t)Q * M * 4) + align256(li::sel_workspace_bytes(Q, M));
+        return li::kSyncBytes + align256((size_t)Q * M * 4) + align256(li::sel_workspace_bytes(Q, M));
     default: return 0;
     }
 }
@@ -340,7 +342,8 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
     if (!ws || ws_bytes < need)
         return fail(LI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
 
-    uint8_t *p = (uint8_t *)ws;
+    int32_t *sync = (int32_t *)ws; // the zeroed region (see li_workspace_bytes)
+    uint8_t *p = (uint8_t *)ws + li::kSyncBytes;
     float *S = scores;
     int64_t sld = ld;
     if (!S) {
@@ -349,7 +352,7 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
         p += align256((size_t)Q * sld * 4);
     }
     const int64_t max_n = std::max(queries->max_valid, 1);
-    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, max_n);
+    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, max_n, sync);
 
     li::SelCall sc{};
     sc.row = li::SelRow{S, sld, nullptr, 0, nullptr, 0};
@@ -378,10 +381,13 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
     const bool fp8 = cache->dtype == LI_FP8;
     const bool fused_hist = scored && !(many && (cache->dtype == LI_BF16 || fp8)) &&
                             li::selection_wants_counts(Q, queries->max_valid);
+    // On the filter path the histogram lives in the workspace's zeroed region
+    // (no clearing kernel); the other counting paths clear theirs first.
+    const bool filter_path = fused_hist && li::selection_filters(Q, queries->max_valid);
     hipError_t e = hipSuccess;
     bool filtered = false;
     if (scored) {
-        if (fused_hist) {
+        if (fused_hist && !filter_path) {
             li::TimedScope ts(LI_KERNEL_SELECT, stream);
             e = li::launch_hist_clear(sw, Q, stream);
         }
@@ -396,9 +402,8 @@ li_status score_topk_impl(const li_cache *cache, const li_queries *queries, cons
         a.stream_nt = !many && stream_nt((int64_t)Q * queries->max_valid * row_bytes);
         // the selection's filter pass, offered to the scoring kernel
         const int fmode = fused_filter_mode();
-        a.flt = li::FilterArgs{fused_hist && fmode > 0 && li::selection_filters(Q, queries->max_valid),
-                               k, k_inner, idx, idx_inner, sw.cand, sw.cand2, sw.cap,
-                               fmode == 2 ? 0u : kFilterWaitTicks};
+        a.flt = li::FilterArgs{filter_path && fmode > 0, filter_path, k, k_inner, idx, idx_inner, sw.cand, sw.cand2,
+                               sw.cap, fmode == 2 ? 0u : kFilterWaitTicks};
         li::TimedScope ts(many ? LI_KERNEL_SCORE_PREFILL : LI_KERNEL_SCORE_DECODE, stream, true);
         if (fp8)
             e = li::launch_score_fp8(a, cache->scales, li::fp8_query_scale_offset(Q, H, cache->r), cache->r, many,
@@ -496,11 +501,12 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     if (!ws || ws_bytes < need)
         return fail(LI_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
 
-    uint8_t *p = (uint8_t *)ws;
+    int32_t *sync = (int32_t *)ws; // the zeroed region (see li_workspace_bytes)
+    uint8_t *p = (uint8_t *)ws + li::kSyncBytes;
     float *S = cand_scores ? cand_scores : (float *)p;
     float *S_pos = (float *)p; // by-position scores (see below)
     p += align256((size_t)Q * M * 4);
-    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, M);
+    li::SelWorkspace sw = li::sel_workspace_carve(p, Q, M, sync);
 
     // When M >= max_valid, no query has more valid rows than M, so scoring a
     // query's whole valid prefix reads no more rows than its candidates may
@@ -567,7 +573,8 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
 
     hipError_t e = hipSuccess;
     const bool fused_hist = li::selection_wants_counts(Q, M);
-    if (fused_hist) {
+    const bool filter_path = fused_hist && li::selection_filters(Q, M); // histogram in the zeroed region
+    if (fused_hist && !filter_path) {
         li::TimedScope ts(LI_KERNEL_SELECT, stream);
         e = li::launch_hist_clear(sw, Q, stream);
     }
@@ -581,6 +588,7 @@ li_status li_hs_select(const li_cache *cache, const li_queries *queries, const i
     a.out_ld = M;
     a.max_rows = M;
     a.hist = fused_hist ? sw.hist : nullptr;
+    a.flt.filter_path = filter_path;
     {
         li::TimedScope ts(LI_KERNEL_SCORE_GATHER, stream, true);
         if (cache->dtype == LI_FP8)

@@ -601,7 +601,10 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int i = 0; i < npro; ++i) issue(i, i);
 
-    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) {
+        a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+        if (a.flt.filter_path) zero_filter_counters(a.hist + (int64_t)q * kHistStride);
+    }
     if (row0 >= n) {
         wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
         return;

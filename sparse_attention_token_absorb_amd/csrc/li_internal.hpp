@@ -24,8 +24,19 @@ enum {
     kSlotAboveO = kHistBins + 6, // rows in digits above the outer threshold digit
     kSlotAboveI = kHistBins + 7, // the same for the inner one
     kSlotTotal = kHistBins + 8,  // rows counted into the histogram so far (fused filter pass)
-    kSlotErr = kHistBins + 9,    // nonzero: a fused filter pass gave up waiting (the final kernel redoes the query)
+    kSlotDone = kHistBins + 9,   // rows the filter pass has sorted (short of n: the final kernel redoes the query)
+    kSlotResult = kHistBins + 10, // 64-bit (slots 10, 11): threshold digits published by the fused filter pass
 };
+
+// The long-row selection's filter path (at most kSyncQueries queries) keeps
+// each query's histogram and counters in a region at the start of the
+// workspace, which is zero between calls: the final kernel clears what a
+// call added to it (the histogram, the row total, the published digits), and
+// the scoring kernel's first workgroup zeroes the per-call counters before
+// any workgroup can use them, so no kernel has to clear the histogram before
+// scoring.
+constexpr int kSyncQueries = 64;
+constexpr size_t kSyncBytes = ((size_t)kSyncQueries * kHistStride * 4 + 255) & ~(size_t)255;
 
 // The filter pass of a long-row selection, run inside the decode scoring
 // kernel (on: the launcher guarantees that every workgroup of the grid is
@@ -36,6 +47,9 @@ enum {
 // selection's workspace), as the separate filter kernel would.
 struct FilterArgs {
     bool on;
+    bool filter_path; // the selection takes the filter path: the histogram is the
+                      // query's entry in the workspace's zeroed region, and the
+                      // scoring kernel's first workgroup zeroes the per-call counters
     int32_t k;
     int32_t k_inner; // 0: no nested selection
     int32_t *idx;    // [Q][k]
@@ -180,7 +194,9 @@ struct SelCall {
 };
 
 size_t sel_workspace_bytes(int64_t Q, int64_t max_n);
-SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n);
+// base: the workspace past its zeroed region sync (the filter path's
+// histograms, when the selection takes that path).
+SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n, int32_t *sync);
 
 // Zero the histograms (before a scoring kernel accumulates into them).
 hipError_t launch_hist_clear(const SelWorkspace &ws, int64_t Q, hipStream_t s);

@@ -44,6 +44,18 @@ __device__ __forceinline__ int add_agent(int32_t *p, int v)
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The per-call counters of query q's entry in the workspace's zeroed region
+// (rows above and on the threshold digits, rows sorted), zeroed by the
+// scoring kernel's first workgroup before it counts its own rows: no
+// workgroup uses them before the query's histogram is complete, which needs
+// that workgroup's rows, so the zeroes land first.  Thread 0 of workgroup 0.
+__device__ __forceinline__ void zero_filter_counters(int32_t *hq)
+{
+    const int slots[5] = {kSlotUpO, kSlotTieO, kSlotUpI, kSlotTieI, kSlotDone};
+#pragma unroll
+    for (int i = 0; i < 5; ++i) __hip_atomic_store(hq + slots[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The filter pass over this workgroup's rows row0 .. row0 + rows - 1 of
 // query q (n rows in all), their scores in s_out; the workgroup's digit
 // counts and its row count are already being added into the query's
@@ -57,50 +69,73 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
     const int Ki = f.k_inner > 0 ? min(n, f.k_inner) : 0;
     const uint32_t rem[2] = {(uint32_t)K, (uint32_t)(Ki > 0 ? Ki : K)};
     if (tid < 4) fl->cnt[tid] = 0;
-    // Wait for the whole histogram: once the row total reaches n every
-    // workgroup has issued its adds, and a histogram whose bins sum to n holds
-    // every add (no bin reads more than its final count), so a sum short of n
-    // is read again.  No cache writeback or invalidate is involved.  The
-    // launcher fuses the pass only when the whole grid fits the GPU at once,
-    // so the wait normally ends within microseconds; it is bounded
-    // (f.wait_ticks of the 100 MHz constant clock) because other work can
-    // hold CUs meanwhile (another stream's kernels, another fused launch
-    // waiting the same way).  A workgroup whose wait runs out records it in
-    // the query's error slot and leaves; the final kernel then selects that
-    // query again from its scores alone.
+    // The workgroup whose row count completes the query's row total (its
+    // add returns n - rows) finds the threshold digits for all of them:
+    // every other workgroup has issued its histogram adds by then, and a
+    // histogram whose bins sum to n holds every add (no bin reads more than
+    // its final count), so a sum short of n is read again.  It publishes the
+    // digits and the counts above them in one 64-bit word, which the other
+    // workgroups poll.  Only agent-scope loads, adds and stores are used:
+    // no cache writeback or invalidate.  The launcher fuses the pass only
+    // when the whole grid fits the GPU at once, so the wait normally ends
+    // within microseconds; it is bounded (f.wait_ticks of the 100 MHz
+    // constant clock) because other work can hold CUs meanwhile (another
+    // stream's kernels, another fused launch waiting the same way).  A
+    // workgroup whose wait runs out leaves its rows unsorted (they are then
+    // missing from the query's count of sorted rows), and the final kernel
+    // selects that query again from its scores alone.
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-        if (tid == 0) {
-            int err = __builtin_amdgcn_s_memrealtime() - t0 >= f.wait_ticks;
-            while (!err && load_agent(hq + kSlotTotal) < n) {
-                __builtin_amdgcn_s_sleep(2);
-                err = __builtin_amdgcn_s_memrealtime() - t0 >= f.wait_ticks;
-            }
-            if (err) add_agent(hq + kSlotErr, 1);
-            fl->err = err;
+    auto expired = [&] { return __builtin_amdgcn_s_memrealtime() - t0 >= f.wait_ticks; };
+    uint64_t *res_word = (uint64_t *)(hq + kSlotResult);
+    if (tid == 0) fl->err = add_agent(hq + kSlotTotal, rows) + rows == n ? 2 : 0; // 2: this workgroup is last
+    __syncthreads();
+    if (fl->err == 2) {
+        for (;;) {
+            constexpr int PB = kHistBins / 256;
+            uint32_t hv[PB];
+#pragma unroll
+            for (int e = 0; e < PB; ++e) hv[e] = (uint32_t)load_agent(hq + e * 256 + tid);
+#pragma unroll
+            for (int e = 0; e < PB; ++e) s_hist[e * 256 + tid] = hv[e];
+            __syncthreads();
+            find_bins<256, kHistBins, 2>(s_hist, rem, *fl);
+            const uint32_t total = fl->wtot[0] + fl->wtot[1] + fl->wtot[2] + fl->wtot[3];
+            if (total == (uint32_t)n) break;
+            __syncthreads(); // every thread has read this round's results
+            if (tid == 0) fl->err = expired() ? 1 : 2;
+            __syncthreads();
+            if (fl->err == 1) break;
         }
-        __syncthreads();
-        if (fl->err) return;
-        constexpr int PB = kHistBins / 256;
-        uint32_t hv[PB];
-#pragma unroll
-        for (int e = 0; e < PB; ++e) hv[e] = (uint32_t)load_agent(hq + e * 256 + tid);
-#pragma unroll
-        for (int e = 0; e < PB; ++e) s_hist[e * 256 + tid] = hv[e];
-        __syncthreads();
-        find_bins<256, kHistBins, 2>(s_hist, rem, *fl);
-        const uint32_t total = fl->wtot[0] + fl->wtot[1] + fl->wtot[2] + fl->wtot[3];
-        if (total == (uint32_t)n) break;
-        __syncthreads(); // every thread has read this round's results
-        __builtin_amdgcn_s_sleep(2);
+        if (tid == 0) {
+            if (fl->err != 1) {
+                // for the final kernel, then for the other workgroups
+                hq[kSlotBins] = (int32_t)(((uint32_t)fl->res[0] & 0xFFFFu) | ((uint32_t)fl->res[2] << 16));
+                hq[kSlotAboveO] = fl->res[1];
+                hq[kSlotAboveI] = fl->res[3];
+                const uint64_t w = (1ull << 63) | (uint64_t)(uint32_t)(fl->res[0] + 1) |
+                                   ((uint64_t)(uint32_t)(fl->res[2] + 1) << 13);
+                __hip_atomic_store(res_word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                fl->err = 0;
+            }
+        }
+    } else if (tid == 0) {
+        uint64_t w = 0;
+        int err = 0;
+        while (!((w = __hip_atomic_load(res_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 63)) {
+            __builtin_amdgcn_s_sleep(2);
+            if (expired()) {
+                err = 1;
+                break;
+            }
+        }
+        fl->err = err;
+        fl->res[0] = (int)(w & 0x1FFFu) - 1;
+        fl->res[2] = (int)((w >> 13) & 0x1FFFu) - 1;
     }
+    __syncthreads();
+    if (fl->err) return;
     const int bin = fl->res[0];
     const int bin_i = Ki > 0 ? fl->res[2] : -1;
-    if (blockIdx.x == 0 && tid == 0) { // every workgroup finds the same digits; the final kernel reads them here
-        hq[kSlotBins] = (int32_t)(((uint32_t)fl->res[0] & 0xFFFFu) | ((uint32_t)fl->res[2] << 16));
-        hq[kSlotAboveO] = fl->res[1];
-        hq[kSlotAboveI] = fl->res[3];
-    }
     if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
     const bool inner = Ki > 0;
     const bool sep = inner && bin_i != bin; // inner ties need a list of their own
@@ -160,6 +195,7 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
             }
         }
     }
+    if (tid == 0) add_agent(hq + kSlotDone, rows); // this workgroup's rows are sorted
 }
 
 // After the stream, with every row's score staged in s_out (workgroup-local
@@ -188,7 +224,6 @@ __device__ __forceinline__ void score_tail(const ScoreArgs &a, int q, int64_t ro
     hist_flush(s_hist, hq, 256, tid);
     if (!fused) return;
     __syncthreads(); // every thread has issued its adds (and read s_hist, which the filter pass reuses)
-    if (tid == 0) add_agent(hq + kSlotTotal, rows);
     filter_pass(a, q, row0, rows, n, s_out, s_hist, hq, fl);
     for (int j = tid; j < rows; j += 256) out[row0 + j] = s_out[j];
 }

@@ -368,7 +368,10 @@ __global__ __launch_bounds__(256) void k_score_decode(ScoreArgs a, int tiles_per
     const int npro = min(NB - 1, CPT * nt_max);
     for (int c = 0; c < npro; ++c) issue(c);
 
-    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) {
+        a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+        if (a.flt.filter_path) zero_filter_counters(a.hist + (int64_t)q * kHistStride);
+    }
     if (row0 >= n) {
         wait_vmcnt<0>(); // no LDS write may land after the workgroup has left
         return;
@@ -476,7 +479,10 @@ __global__ __launch_bounds__(256) void k_score_decode_vr(ScoreArgs a, int tiles_
     const int b = clamp_index(a.qseq[q], a.batch);
     int n = GATHER ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
-    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) {
+        a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+        if (a.flt.filter_path) zero_filter_counters(a.hist + (int64_t)q * kHistStride);
+    }
     const int64_t row0 = (int64_t)blockIdx.x * 4 * tiles_per_wave * kTile;
     if (row0 >= n) return;
     if (a.hist) hist_zero(s_hist, 256, threadIdx.x);
@@ -784,7 +790,10 @@ __global__ __launch_bounds__(256) void k_score_f32(ScoreArgs a, int R, int rows_
     const int b = clamp_index(a.qseq[q], a.batch);
     int n = a.cand ? min(a.cand_count[q], (int)a.cand_ld) : valid_rows(a.qpos[q], a.seq_lens[b]);
     n = (int)min64(n, a.max_rows);
-    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+    if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) {
+        a.hist[(int64_t)q * kHistStride + kSlotN] = n;
+        if (a.flt.filter_path) zero_filter_counters(a.hist + (int64_t)q * kHistStride);
+    }
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
     if (row0 >= n) return;
     const int64_t row1 = min64(row0 + rows_per_wg, n);

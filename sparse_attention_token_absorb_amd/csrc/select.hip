@@ -710,7 +710,10 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
         hq[kSlotAboveO] = sh.res[1];
         hq[kSlotAboveI] = sh.res[3];
     }
-    if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
+    // a histogram that does not hold exactly n rows (inconsistent counts)
+    // leaves this workgroup's rows unsorted, and the final kernel redoes the query
+    if (sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3] != (uint32_t)n) return;
+    if (bin < 0 || (Ki > 0 && bin_i < 0)) return;
     const bool inner = Ki > 0;
     const bool sep = inner && bin_i != bin; // inner ties need a list of their own
     int nup = 0, ntie = 0, nupi = 0, ntiei = 0;
@@ -779,6 +782,23 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(SelCall c, SelWorkspa
                 }
             }
         }
+    if (tid == 0) // this workgroup's rows are sorted
+        atomicAdd(&hq[kSlotDone], (int)((int64_t)n - i0 < kFilterChunk ? (int64_t)n - i0 : kFilterChunk));
+}
+
+// What a call added to the query's entry of the workspace's zeroed region:
+// the histogram, the row total and the published digits (the scoring
+// kernel's first workgroup zeroes the other counters itself).  The final
+// kernel's outer workgroup, which no other reader of them outlives.
+__device__ __forceinline__ void clear_sync(int32_t *hq)
+{
+    const int tid = threadIdx.x;
+    for (int j = tid; j < kHistBins; j += NT) hq[j] = 0;
+    if (tid == 0) {
+        hq[kSlotTotal] = 0;
+        hq[kSlotResult] = 0;
+        hq[kSlotResult + 1] = 0;
+    }
 }
 
 // The whole selection of query blockIdx.x from its scores (the streaming
@@ -817,7 +837,7 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     const int tid = threadIdx.x;
     const int q = blockIdx.x;
     const bool inner = blockIdx.y == 1;
-    const int32_t *hq = ws.hist + (int64_t)q * kHistStride;
+    int32_t *hq = ws.hist + (int64_t)q * kHistStride;
     const int kout = inner ? c.k_inner : c.k;
     int32_t *out = (inner ? c.idx_inner : c.idx) + (int64_t)q * kout;
     sh.clear_levels();
@@ -839,13 +859,16 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     const int bins = hq[kSlotBins];
     const int above_o = hq[kSlotAboveO];
     const int above_i = hq[kSlotAboveI];
-    if (hq[kSlotErr]) {
-        // Some workgroup of the scoring launch gave up waiting for the others
-        // (the fused filter pass found the grid not all resident at once):
-        // this query's filter results are incomplete, so the selection runs
-        // again from the scores alone, the nested one over the outer winners.
+    if (hq[kSlotDone] != n) {
+        // The filter pass did not sort every row: a workgroup of a fused pass
+        // gave up waiting for the others (the grid was not all resident at
+        // once), or the histogram was inconsistent.  The selection runs again
+        // from the scores alone, the nested one over the outer winners.
         static_assert(kHistBins + kStreamCap <= kCandCap && kStreamCap <= kCandCap, "fallback LDS");
-        if (!inner) final_from_scores(c, ws, sh, ck, ck + kHistBins, ci);
+        if (!inner) {
+            final_from_scores(c, ws, sh, ck, ck + kHistBins, ci);
+            clear_sync(hq);
+        }
         return;
     }
     const int K = min(n, c.k);
@@ -893,6 +916,7 @@ __global__ __launch_bounds__(NT) void k_final(SelCall c, SelWorkspace ws)
     }
     for (int i = Kp + tid; i < kout; i += NT) out[i] = -1;
     if (tid == 0) (inner ? c.count_inner : c.count)[q] = Kp;
+    if (!inner) clear_sync(hq);
 }
 
 // Clears the per-query histograms and slots before a scoring kernel
@@ -902,7 +926,7 @@ __global__ __launch_bounds__(256) void k_hist_clear(int32_t *hist, int64_t words
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) hist[i] = 0;
 }
 
-bool use_filter(int64_t Q, int64_t max_n) { return max_n > kKeyCache && Q <= 64; }
+bool use_filter(int64_t Q, int64_t max_n) { return max_n > kKeyCache && Q <= kSyncQueries; }
 
 int64_t cand_cap(int64_t Q, int64_t max_n) { return use_filter(Q, max_n) ? std::min<int64_t>(max_n, 65536) : 0; }
 
@@ -917,10 +941,10 @@ size_t sel_workspace_bytes(int64_t Q, int64_t max_n)
     return b + 2 * (size_t)Q * cand_cap(Q, max_n) * 8;
 }
 
-SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n)
+SelWorkspace sel_workspace_carve(void *base, int64_t Q, int64_t max_n, int32_t *sync)
 {
     SelWorkspace w;
-    w.hist = (int32_t *)base;
+    w.hist = use_filter(Q, max_n) ? sync : (int32_t *)base;
     size_t off = ((size_t)Q * kHistStride * 4 + 255) & ~(size_t)255;
     w.cap = cand_cap(Q, max_n);
     w.cand = (uint2 *)((uint8_t *)base + off);

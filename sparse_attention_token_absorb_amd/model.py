@@ -99,11 +99,9 @@ class IndexerModel:
             self.q_lat = [torch.empty((Q, H, r), dtype=torch.bfloat16, device=dev) for _ in range(lmap.n_layers)]
             self.q_key = self.q  # a native bf16 indexer scores its keys with q as it is
         kmax = max(self.k, self.M)
-        self.ws = torch.empty(max(B.workspace_bytes(B.LI_OP_SCORE_TOPK, Q, nv, H, max(r, d), kmax, 0),
-                                  B.workspace_bytes(B.LI_OP_SCORE_TOPK_EXT_SCORES, Q, nv, H, max(r, d), kmax, 0)),
-                              dtype=torch.uint8, device=dev)
-        self.ws_hs = torch.empty(B.workspace_bytes(B.LI_OP_HS_SELECT, Q, 0, H, r, self.k, self.M), dtype=torch.uint8,
-                                 device=dev)
+        self.ws = B.workspace(max(B.workspace_bytes(B.LI_OP_SCORE_TOPK, Q, nv, H, max(r, d), kmax, 0),
+                                  B.workspace_bytes(B.LI_OP_SCORE_TOPK_EXT_SCORES, Q, nv, H, max(r, d), kmax, 0)), dev)
+        self.ws_hs = B.workspace(B.workspace_bytes(B.LI_OP_HS_SELECT, Q, 0, H, r, self.k, self.M), dev)
         self.out = [B.TopK(i32(Q, self.k), i32(Q), scores=f32(Q, nv) if keep_scores else None)
                     for _ in range(lmap.n_layers)]
         # HS anchors: top-M candidates with the anchor's own top-k nested

@@ -51,8 +51,8 @@ def test_graph_replays_match_eager():
         B.append_latent(f8, h.to_dev(g.latent[b][:n], torch.bfloat16), h.i32(np.full(n, b)), h.i32(np.arange(n)))
     f8q = B.absorb_query(h.to_dev(g.q[0], torch.bfloat16), h.to_dev(g.W[0], torch.bfloat16), fp8=True)
 
-    ws = torch.empty(B.workspace_bytes(B.LI_OP_SCORE_TOPK, Q, N, 64, 256, g.M, 0), dtype=torch.uint8, device=dev)
-    ws_hs = torch.empty(B.workspace_bytes(B.LI_OP_HS_SELECT, Q, 0, 64, 256, g.k, g.M), dtype=torch.uint8, device=dev)
+    ws = B.workspace(B.workspace_bytes(B.LI_OP_SCORE_TOPK, Q, N, 64, 256, g.M, 0), dev)
+    ws_hs = B.workspace(B.workspace_bytes(B.LI_OP_HS_SELECT, Q, 0, 64, 256, g.k, g.M), dev)
     i32 = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
     full = B.TopK(i32(Q, g.k), i32(Q), scores=torch.empty((Q, N), dtype=torch.float32, device=dev))
     anchor = B.TopK(i32(Q, g.M), i32(Q), i32(Q, g.k), i32(Q))

@@ -160,6 +160,24 @@ def test_long_rows_exact_in_every_filter_mode(mode, distinct):
         B.fused_filter(B.FUSED_FILTER_ON)
 
 
+@pytest.mark.parametrize("mode", [B.FUSED_FILTER_ON, B.FUSED_FILTER_OFF])
+def test_long_rows_with_a_dirty_workspace(mode):
+    # a workspace that was not zero-filled: the filter path cannot trust the
+    # histogram in its leading region (the bins do not sum to the row count),
+    # the final kernel selects again from the scores, and every call leaves
+    # the region zeroed, so the calls after it run the normal path
+    B.fused_filter(mode)
+    try:
+        cache, seq, pos, mv, qt, w, n_q = _setup(23, [40000, 23000], 500)
+        nb = B.workspace_bytes(B.LI_OP_SCORE_TOPK, len(n_q), mv, H, R, 2048, 0)
+        ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=_dev())
+        for rep in range(3):
+            out = B.score_topk(cache, seq, pos, mv, qt, w, 2048, k_inner=512, keep_scores=True, ws=ws)
+            _check_full(out, n_q, 2048, f"dirty workspace, call {rep}, mode {mode}", k_inner=512)
+    finally:
+        B.fused_filter(B.FUSED_FILTER_ON)
+
+
 def test_many_queries_stream_exact():
     # more than 64 queries over rows beyond 8192: the streaming selection
     cache, seq, pos, mv, qt, w, n_q = _setup(31, [12000, 9000, 20000], 60, Q_per_seq=24)
