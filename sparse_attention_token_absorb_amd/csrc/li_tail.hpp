@@ -74,8 +74,8 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
     // every other workgroup has issued its histogram adds by then, and a
     // histogram whose bins sum to n holds every add (no bin reads more than
     // its final count), so a sum short of n is read again.  It publishes the
-    // digits and the counts above them in one 64-bit word, which the other
-    // workgroups poll.  Only agent-scope loads, adds and stores are used:
+    // digits in one 64-bit word (with a flag and the row count n), which the
+    // other workgroups poll.  Only agent-scope loads, adds and stores are used:
     // no cache writeback or invalidate.  The launcher fuses the pass only
     // when the whole grid fits the GPU at once, so the wait normally ends
     // within microseconds; it is bounded (f.wait_ticks of the 100 MHz
@@ -112,8 +112,8 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
                 hq[kSlotBins] = (int32_t)(((uint32_t)fl->res[0] & 0xFFFFu) | ((uint32_t)fl->res[2] << 16));
                 hq[kSlotAboveO] = fl->res[1];
                 hq[kSlotAboveI] = fl->res[3];
-                const uint64_t w = (1ull << 63) | (uint64_t)(uint32_t)(fl->res[0] + 1) |
-                                   ((uint64_t)(uint32_t)(fl->res[2] + 1) << 13);
+                const uint64_t w = (1ull << 63) | ((uint64_t)(uint32_t)n << 26) |
+                                   (uint64_t)(uint32_t)(fl->res[0] + 1) | ((uint64_t)(uint32_t)(fl->res[2] + 1) << 13);
                 __hip_atomic_store(res_word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 fl->err = 0;
             }
@@ -121,7 +121,11 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
     } else if (tid == 0) {
         uint64_t w = 0;
         int err = 0;
-        while (!((w = __hip_atomic_load(res_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 63)) {
+        // the word is this call's once its flag is set and it names this
+        // query's row count (a workspace that was not zeroed may hold any bits)
+        const uint64_t want = (1ull << 63) | ((uint64_t)(uint32_t)n << 26);
+        while (((w = __hip_atomic_load(res_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & ~0x3FFFFFFull) !=
+               want) {
             __builtin_amdgcn_s_sleep(2);
             if (expired()) {
                 err = 1;

@@ -160,17 +160,23 @@ def test_long_rows_exact_in_every_filter_mode(mode, distinct):
         B.fused_filter(B.FUSED_FILTER_ON)
 
 
+@pytest.mark.parametrize("fill", ["random", "ones"])
 @pytest.mark.parametrize("mode", [B.FUSED_FILTER_ON, B.FUSED_FILTER_OFF])
-def test_long_rows_with_a_dirty_workspace(mode):
+def test_long_rows_with_a_dirty_workspace(mode, fill):
     # a workspace that was not zero-filled: the filter path cannot trust the
-    # histogram in its leading region (the bins do not sum to the row count),
-    # the final kernel selects again from the scores, and every call leaves
-    # the region zeroed, so the calls after it run the normal path
+    # histogram in its leading region (the bins do not sum to the row count)
+    # nor a published threshold word (all ones sets its flag but names no
+    # query's row count), the final kernel selects again from the scores, and
+    # every call leaves the region zeroed, so the calls after it run the
+    # normal path
     B.fused_filter(mode)
     try:
         cache, seq, pos, mv, qt, w, n_q = _setup(23, [40000, 23000], 500)
         nb = B.workspace_bytes(B.LI_OP_SCORE_TOPK, len(n_q), mv, H, R, 2048, 0)
-        ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=_dev())
+        if fill == "random":
+            ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=_dev())
+        else:
+            ws = torch.full((nb,), 255, dtype=torch.uint8, device=_dev())
         for rep in range(3):
             out = B.score_topk(cache, seq, pos, mv, qt, w, 2048, k_inner=512, keep_scores=True, ws=ws)
             _check_full(out, n_q, 2048, f"dirty workspace, call {rep}, mode {mode}", k_inner=512)
