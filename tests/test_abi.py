@@ -169,6 +169,21 @@ def test_workspace_sizes(L):
     assert big > small
 
 
+def test_every_workspace_starts_with_the_zeroed_region(L):
+    """Every op's workspace holds the region the long-row selection keeps
+    zeroed (64 queries x 4112 words, the header's LI_WORKSPACE_ZEROED_BYTES)
+    ahead of everything else: the smallest workspace of each op is larger
+    than it, and the binding's own workspaces come zero-filled."""
+    torch = pytest.importorskip("torch")
+    zeroed = 64 * 4112 * 4
+    hdr = open(os.path.join(ROOT, "include", "latentindex.h")).read()
+    assert "#define LI_WORKSPACE_ZEROED_BYTES (64 * 4112 * 4)" in hdr
+    for op, mv, M in ((B.LI_OP_SCORE_TOPK, 1, 0), (B.LI_OP_SCORE_TOPK_EXT_SCORES, 1, 0), (B.LI_OP_HS_SELECT, 0, 1)):
+        assert B.workspace_bytes(op, 1, mv, 64, 256, 1, M) > zeroed
+    w = B.workspace(1000, "cpu")
+    assert w.dtype == torch.uint8 and int(w.numel()) == 1000 and int(w.count_nonzero()) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
