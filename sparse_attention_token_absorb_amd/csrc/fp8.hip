@@ -420,6 +420,98 @@ __global__ __launch_bounds__(256) void k_absorb_fp8_row(const u16 *q, const u16 
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// The query of an FP8 decode launch into LDS, once per workgroup: wave w
+// moves the codes of heads 16w .. 16w+15 (rows past H repeat row H-1 and are
+// zeroed when read) into the last slot of its ring, which the stream does not
+// touch before its (NB-1)-th tile, the 16-byte pieces of head h's row
+// rotated by h so that the A-fragment reads (32 heads, the same piece) fall
+// in distinct banks; wave 0 also moves the segment scales, wave 1 the head
+// weights, wave 2 the heads' decoder biases (when there are any).  Returns
+// the number of loads this wave issued.
+template <int R, int HB, int NB, int SLOT>
+__device__ __forceinline__ int stage_query_fp8(const uint8_t *qc, const float *qs, const float *wq, const float *bq,
+                                               int H, lds_u8 *ring, lds_u8 *s_qs, lds_u8 *s_w, lds_u8 *s_b)
+{
+    constexpr int PR = R / 16;         // 16-byte pieces per row of codes
+    constexpr int NIC = 16 * R / 1024; // 16 rows, 1 KiB per instruction
+    constexpr int NSEG = R / kSeg;
+    static_assert(SLOT >= 16 * R, "a ring slot holds 16 rows of query codes");
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int issued = 0;
+    if (wv * 16 < HB * 32) {
+        lds_u8 *slot = ring + (wv * NB + NB - 1) * SLOT;
+#pragma unroll
+        for (int ii = 0; ii < NIC; ++ii) {
+            const int p = ii * 64 + lane;
+            const int h = wv * 16 + p / PR, cs = p % PR;
+            const int hs = h < H ? h : H - 1;
+            dma16(qc + (int64_t)hs * R + (cs ^ (h & (PR - 1))) * 16, slot + ii * 1024);
+        }
+        issued = NIC;
+    }
+    if (wv == 0) {
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g) {
+            const int e = g * 64 + lane;
+            dma4(qs + (e < H * NSEG ? e : H * NSEG - 1), s_qs + g * 256);
+        }
+        issued += NSEG;
+    }
+    if (wv == 1) {
+        dma4(wq + (lane < H ? lane : H - 1), s_w);
+        ++issued;
+    }
+    if (wv == 2 && bq) {
+        dma4(bq + (lane < H ? lane : H - 1), s_b);
+        ++issued;
+    }
+    return issued;
+}
+
+// The staged query into registers (after the workgroup barrier that follows
+// its staging): A fragments, segment scales as E8M0 exponents, weights and
+// biases, heads past H zero (their scales 2^0).
+template <int R, int HB, int NB, int SLOT>
+__device__ __forceinline__ void read_query_fp8(const lds_u8 *ring, const lds_f32 *s_qs, const lds_f32 *s_w,
+                                               const lds_f32 *s_b, bool has_bias, int H, i32x8 (&qa)[HB][R / 64],
+                                               int (&sa)[HB][R / kSeg], float (&wr)[HB][16], f32x16 (&br)[HB])
+{
+    constexpr int PR = R / 16;
+    constexpr int KS = R / 64;
+    constexpr int NSEG = R / kSeg;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 32 + (lane & 31);
+        const bool live = h < H;
+        const lds_u8 *row = ring + ((h >> 4) * NB + NB - 1) * SLOT + (h & 15) * R;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int p0 = 4 * s + 2 * (lane >> 5);
+            const u32x4 lo = *(const lds_u32x4 *)(row + (p0 ^ (h & (PR - 1))) * 16);
+            const u32x4 hi = *(const lds_u32x4 *)(row + ((p0 + 1) ^ (h & (PR - 1))) * 16);
+            i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if (!live) {
+                i32x8 z = {};
+                v = z;
+            }
+            qa[hb][s] = v;
+        }
+#pragma unroll
+        for (int g = 0; g < NSEG; ++g) {
+            const uint32_t e = (__float_as_uint(s_qs[(live ? h : 0) * NSEG + g]) >> 23) & 0xFFu;
+            sa[hb][g] = live ? (int)e : 127;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int hh = hb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            wr[hb][r] = hh < H ? s_w[hh] : 0.0f;
+            br[hb][r] = has_bias && hh < H ? s_b[hh] : 0.0f;
+        }
+    }
+}
+
 template <int R, int HB, bool GATHER, int NB, bool NT>
 __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *pool_scales, int64_t qscale_off,
                                                    int tiles_per_wave)
@@ -439,6 +531,12 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     __shared__ int32_t s_row[GATHER ? 4 * kGatherTilesF8 * kTile : 1];
     __shared__ uint32_t s_hist[kHistBins];
     __shared__ float s_out[4 * MAXT * kTile];
+    // contiguous mode: the guessed sequence's page ids (wave w, lane i: its
+    // tile i) and the query's scales, weights and biases, staged by DMA
+    __shared__ int32_t s_pg[GATHER ? 1 : 4 * 64];
+    __shared__ float s_qs[GATHER ? 1 : 64 * NSEG];
+    __shared__ float s_w[GATHER ? 1 : 64];
+    __shared__ float s_b[GATHER ? 1 : 64];
 
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -447,18 +545,19 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     LI_PHASE_START;
     // The query: codes as A fragments (lane l: head l%32 of block hb, k-block
     // l/32 of each 64-code step), segment scales as E8M0 exponents, weights.
-    // Requested first, beside the block-table row and the sequence id, and
-    // waited for with them before any tile is issued: one round trip for all
-    // of the start-up loads, and no wait for the query later in the stream
-    // (waiting for these loads once tiles are in flight would also wait for
-    // every tile issued before the wait).
+    // Gather mode loads them per lane, first, beside the sequence id and the
+    // candidates, and waits for them with those before any tile is issued:
+    // one round trip for all of the start-up loads (waiting for per-lane
+    // loads once tiles are in flight would also wait for every tile issued
+    // before them).  Contiguous mode stages them through LDS by DMA instead
+    // (below), so that the first tiles go out as soon as the page ids are in.
     i32x8 qa[HB][KS];
     int sa[HB][NSEG];
     float wr[HB][16];
     f32x16 br[HB]; // accumulator start values: each head's decoder bias (0 without one)
-    {
-        const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
-        const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
+    const uint8_t *qc = (const uint8_t *)a.qt + (int64_t)q * a.H * R;
+    const float *qs = (const float *)((const uint8_t *)a.qt + qscale_off) + (int64_t)q * a.H * NSEG;
+    if constexpr (GATHER) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             const int h = hb * 32 + (lane & 31);
@@ -501,11 +600,16 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
 
     // Contiguous mode: lane i holds the page id of this wave's tile i (at
     // most 64 tiles per wave); query q usually sits in sequence q, so that
-    // block-table row is requested before the sequence id arrives.
+    // block-table row is requested first, by LDS DMA, before the sequence id
+    // arrives and ahead of the query staging.
     const int b_guess = q < a.batch ? q : 0;
-    int page_guess = 0;
+    int staged = 0;
     if constexpr (!GATHER) {
-        if (lane < nt_max) page_guess = a.bt[(int64_t)b_guess * a.max_pages + (tile_row0(lane) >> 6)];
+        const int pidx = (int)min64(tile_row0(lane < nt_max ? lane : 0) >> 6, a.max_pages - 1);
+        dma4(a.bt + (int64_t)b_guess * a.max_pages + pidx, (lds_u8 *)(s_pg + wv * 64));
+        staged = stage_query_fp8<R, HB, NB, SLOT>(qc, qs, a.w + (int64_t)q * a.H,
+                                                  a.bias ? a.bias + (int64_t)q * a.H : nullptr, a.H,
+                                                  (lds_u8 *)ring_raw, (lds_u8 *)s_qs, (lds_u8 *)s_w, (lds_u8 *)s_b);
     }
     const int b = clamp_index(((const_i32_t *)a.qseq)[q], a.batch);
     int n = GATHER ? min(((const_i32_t *)a.cand_count)[q], (int)a.cand_ld)
@@ -516,8 +620,9 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
     auto clamp_page = [&](int page) { return page < 0 ? 0 : (page < a.num_pages ? page : a.num_pages - 1); };
     int tile_page = 0;
     if constexpr (!GATHER) {
+        wait_vmcnt_upto(staged); // the page ids have landed (vector loads complete in issue order)
         if (b == b_guess)
-            tile_page = page_guess;
+            tile_page = ((const __attribute__((address_space(3))) int32_t *)s_pg)[wv * 64 + lane];
         else if (lane < nt_max)
             tile_page = a.bt[(int64_t)b * a.max_pages + (tile_row0(lane) >> 6)];
         tile_page = clamp_page(tile_page);
@@ -595,11 +700,24 @@ __global__ __launch_bounds__(256) void k_score_fp8(ScoreArgs a, const float *poo
         }
     };
     const int npro = min(NB - 1, nt_max);
-    // every start-up load (query, weights, page ids, gathered rows) has
-    // landed: s_waitcnt vmcnt(0), issued as the builtin so that the compiler
-    // counts it and adds no wait of its own for these loads later
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (GATHER) {
+        // every start-up load (query, weights, gathered rows) has landed:
+        // s_waitcnt vmcnt(0), issued as the builtin so that the compiler
+        // counts it and adds no wait of its own for these loads later
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     for (int i = 0; i < npro; ++i) issue(i, i);
+    if constexpr (!GATHER) {
+        // the query staging was issued before these tiles, so it has landed
+        // once at most they are outstanding; every wave's part, then the
+        // registers, then no wave reuses a staging slot before all have read
+        wait_after<NIT, NB - 1>(npro);
+        wg_barrier();
+        read_query_fp8<R, HB, NB, SLOT>((const lds_u8 *)ring_raw, (const lds_f32 *)s_qs, (const lds_f32 *)s_w,
+                                        (const lds_f32 *)s_b, a.bias != nullptr, a.H, qa, sa, wr, br);
+        wait_lds();
+        wg_barrier();
+    }
 
     if (a.hist && blockIdx.x == 0 && threadIdx.x == 0) {
         a.hist[(int64_t)q * kHistStride + kSlotN] = n;
