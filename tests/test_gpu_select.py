@@ -184,6 +184,26 @@ def test_long_rows_with_a_dirty_workspace(mode, fill):
         B.fused_filter(B.FUSED_FILTER_ON)
 
 
+def test_concurrent_launches_on_two_streams_stay_exact():
+    # two long-row calls enqueued on two streams at once, each with a grid
+    # that fills the GPU: the fused filter pass of one may find its
+    # workgroups not all resident while the other holds CUs (a bounded wait,
+    # then the final kernel's reselection from the scores); every result
+    # must still be an exact top-k with its nested top-k
+    cache, seq, pos, mv, qt, w, n_q = _setup(29, [65536, 65536, 65536, 65536], 3000)
+    qt2 = (qt.float() * -1.0).to(torch.bfloat16)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for si, (st, q_) in enumerate(zip(streams, (qt, qt2))):
+            with torch.cuda.stream(st):
+                outs.append((rep, si, B.score_topk(cache, seq, pos, mv, q_, w, 2048, k_inner=512, keep_scores=True)))
+    torch.cuda.synchronize()
+    for rep, si, out in outs:
+        _check_full(out, n_q, 2048, f"concurrent call {rep} on stream {si}", k_inner=512)
+
+
 def test_many_queries_stream_exact():
     # more than 64 queries over rows beyond 8192: the streaming selection
     cache, seq, pos, mv, qt, w, n_q = _setup(31, [12000, 9000, 20000], 60, Q_per_seq=24)
