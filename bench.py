@@ -851,21 +851,47 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
+def source_digest(source: str) -> str:
+    """sha256 of a kernel's translation unit as written here: the source file
+    and every header it includes with #include "..." from the same folder,
+    transitively, taken in name order, each as its name, a NUL byte and its
+    bytes.  A counter summary recorded against this digest stays valid only
+    while none of those files changes."""
+    import hashlib
+    import re
+    folder = os.path.dirname(source)
+    seen, todo = set(), [os.path.basename(source)]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(folder, name), "rb") as f:
+            text = f.read()
+        for inc in re.findall(rb'^\s*#\s*include\s+"([^"/]+)"', text, re.M):
+            if os.path.exists(os.path.join(folder, inc.decode())):
+                todo.append(inc.decode())
+    h = hashlib.sha256()
+    for name in sorted(seen):
+        with open(os.path.join(folder, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(path: str, source: str):
     """HBM bytes per launch of the decode scoring kernel, from a committed
     counter summary, or None when that summary was taken on other kernel
-    source (its recorded sha256 no longer matches) or is absent."""
-    import hashlib
+    source (its recorded digest of the kernel's translation unit no longer
+    matches) or is absent."""
     try:
-        with open(source, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = source_digest(source)
         fields = {}
         with open(path) as f:
             for line in f:
                 if line.startswith("- ") and ": " in line:
                     key, val = line[2:].split(": ", 1)
                     fields[key.strip()] = val.strip().strip("`")
-        if fields.get("source_sha256") != sha:
+        if fields.get("source_digest") != sha:
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

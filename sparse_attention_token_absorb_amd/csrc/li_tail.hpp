@@ -56,14 +56,33 @@ __device__ __forceinline__ void zero_filter_counters(int32_t *hq)
     for (int i = 0; i < 5; ++i) __hip_atomic_store(hq + slots[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Rows per thread per round of the tail's passes over the staged scores
+// (2048 of a workgroup's rows): a round's LDS reads go out together, which
+// matters here, where each SIMD runs one wave.
+constexpr int kTailU = 8;
+
+// Scores of rows c0 + u * 256 + tid (u < kTailU) of the workgroup's rows
+// (reads past the last row repeat it; live[u] says which rows are real).
+__device__ __forceinline__ void tail_round(const lds_f32 *s_out, int c0, int rows, float (&p)[kTailU],
+                                           bool (&live)[kTailU])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kTailU; ++u) {
+        const int j = c0 + u * 256 + tid;
+        live[u] = j < rows;
+        p[u] = s_out[min(j, rows - 1)];
+    }
+}
+
 // The filter pass over this workgroup's rows row0 .. row0 + rows - 1 of
-// query q (n rows in all), their scores in s_out; the workgroup's digit
-// counts and its row count are already being added into the query's
-// histogram hq and its row total (all 256 threads).
+// query q (n rows in all, rows >= 1), their scores in s_out; the
+// workgroup's digit counts and its row count are already being added into
+// the query's histogram hq and its row total (all 256 threads).
 __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t row0, int rows, int n,
                                             const lds_f32 *s_out, uint32_t *s_hist, int32_t *hq, FilterLds *fl)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const FilterArgs &f = a.flt;
     const int K = min(n, f.k);
     const int Ki = f.k_inner > 0 ? min(n, f.k_inner) : 0;
@@ -143,59 +162,105 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
     if (bin < 0 || (Ki > 0 && bin_i < 0)) return; // inconsistent counts
     const bool inner = Ki > 0;
     const bool sep = inner && bin_i != bin; // inner ties need a list of their own
-    int nup = 0, ntie = 0, nupi = 0, ntiei = 0;
-    for (int j = tid; j < rows; j += 256) {
-        const int dg = (int)(score_key(s_out[j]) >> kDigit0Shift);
-        nup += dg > bin;
-        ntie += dg == bin;
-        if (inner) {
-            nupi += dg > bin_i;
-            ntiei += sep && dg == bin_i;
+    // a row's runs: above the outer digit (0) or on it (1), above the inner
+    // digit (2) or on it when that differs from the outer one (3); dg = -1
+    // for reads past the last row, which lie in no run
+    auto runs = [&](int dg, bool (&in)[4]) {
+        in[0] = dg > bin;
+        in[1] = dg == bin;
+        in[2] = inner && dg > bin_i;
+        in[3] = sep && dg == bin_i;
+    };
+    const int lo = inner ? min(bin, bin_i) : bin; // rows below this digit lie in no run
+    // Pass 1: each wave counts its rows in every run (ballots), takes its
+    // offsets in the workgroup's runs with one LDS add per run, and the
+    // workgroup's totals go to the query's run counters in one global add
+    // each, whose results (the workgroup's bases) are waited for only after
+    // pass 2 has ranked the first round's rows.
+    uint32_t wcnt[4] = {0u, 0u, 0u, 0u};
+    for (int c0 = 0; c0 < rows; c0 += 256 * kTailU) {
+        float p[kTailU];
+        bool live[kTailU];
+        tail_round(s_out, c0, rows, p, live);
+#pragma unroll
+        for (int u = 0; u < kTailU; ++u) {
+            const int dg = live[u] ? (int)(score_key(p[u]) >> kDigit0Shift) : -1;
+            if (__ballot(dg >= lo) == 0) continue; // the usual round: no row of the wave in a run
+            bool in[4];
+            runs(dg, in);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wcnt[r] += (uint32_t)__popcll(__ballot(in[r]));
         }
     }
-    // this thread's offsets in the workgroup's four runs: an exclusive wave
-    // scan plus one LDS atomic per wave and run, then one global add per run
-    const int cnts[4] = {nup, ntie, nupi, ntiei};
-    int loc[4];
+    uint32_t woff[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t incl = wave_incl_scan((uint32_t)cnts[j]);
-        const int wt = __builtin_amdgcn_readlane((int)incl, 63);
-        int wb = 0;
-        if (wt && (tid & 63) == 0) wb = atomicAdd(&fl->cnt[j], wt);
-        wb = __builtin_amdgcn_readfirstlane(wb);
-        loc[j] = wb + (int)incl - cnts[j];
+    for (int r = 0; r < 4; ++r) {
+        int v = 0;
+        if (lane == 0 && wcnt[r]) v = atomicAdd(&fl->cnt[r], (int)wcnt[r]);
+        woff[r] = (uint32_t)__builtin_amdgcn_readfirstlane(v);
     }
-    __syncthreads();
+    __syncthreads(); // the workgroup's run totals are complete
+    int gbase = 0;
     if (tid < 4) {
         const int slot = tid == 0 ? kSlotUpO : tid == 1 ? kSlotTieO : tid == 2 ? kSlotUpI : kSlotTieI;
         const int v = fl->cnt[tid];
-        fl->base[tid] = v ? add_agent(hq + slot, v) : 0;
+        if (v) gbase = add_agent(hq + slot, v);
     }
-    __syncthreads();
-    int pu = fl->base[0] + loc[0], pt = fl->base[1] + loc[1], pui = fl->base[2] + loc[2], pti = fl->base[3] + loc[3];
+    // Pass 2: every row of a run gets its slot (the wave's offset, the rows
+    // of earlier rounds, then lane order) and is stored there: out / outi
+    // hold row ids, cand / cand2 (key, row id) pairs; slots past a list's
+    // end are dropped but still counted.
     int32_t *out = f.idx + (int64_t)q * f.k;
     int32_t *outi = inner ? f.idx_inner + (int64_t)q * f.k_inner : nullptr;
     uint2 *cand = f.cand + (int64_t)q * f.cap;
     uint2 *cand2 = f.cand2 + (int64_t)q * f.cap;
-    for (int j = tid; j < rows; j += 256) {
-        const uint32_t key = score_key(s_out[j]);
-        const int dg = (int)(key >> kDigit0Shift);
-        const int32_t i = (int32_t)(row0 + j);
-        if (dg > bin) {
-            if (pu < f.k) out[pu] = i;
-            ++pu;
-        } else if (dg == bin) {
-            if (pt < f.cap) cand[pt] = make_uint2(key, (uint32_t)i);
-            ++pt;
+    const uint64_t below = lanes_below();
+    for (int c0 = 0; c0 < rows; c0 += 256 * kTailU) {
+        float p[kTailU];
+        bool live[kTailU];
+        tail_round(s_out, c0, rows, p, live);
+        int slot[kTailU][2]; // the row's slot in its outer run (0 or 1) and in its inner run (2 or 3)
+        int dgs[kTailU];
+#pragma unroll
+        for (int u = 0; u < kTailU; ++u) {
+            const int dg = live[u] ? (int)(score_key(p[u]) >> kDigit0Shift) : -1;
+            dgs[u] = dg;
+            slot[u][0] = slot[u][1] = 0;
+            if (__ballot(dg >= lo) == 0) continue;
+            bool in[4];
+            runs(dg, in);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint64_t m = __ballot(in[r]);
+                if (in[r]) slot[u][r >> 1] = (int)(woff[r] + (uint32_t)__popcll(m & below));
+                woff[r] += (uint32_t)__popcll(m);
+            }
         }
-        if (inner) {
-            if (dg > bin_i) {
-                if (pui < f.k_inner) outi[pui] = i;
-                ++pui;
-            } else if (sep && dg == bin_i) {
-                if (pti < f.cap) cand2[pti] = make_uint2(key, (uint32_t)i);
-                ++pti;
+        if (c0 == 0) {
+            if (tid < 4) fl->base[tid] = gbase;
+            __syncthreads(); // the workgroup's bases
+        }
+        const int b0 = fl->base[0], b1 = fl->base[1], b2 = fl->base[2], b3 = fl->base[3];
+#pragma unroll
+        for (int u = 0; u < kTailU; ++u) {
+            const int dg = dgs[u];
+            if (dg < lo) continue;
+            const int32_t i = (int32_t)(row0 + c0 + u * 256 + tid);
+            if (dg > bin) {
+                const int s = b0 + slot[u][0];
+                if (s < f.k) out[s] = i;
+            } else if (dg == bin) {
+                const int s = b1 + slot[u][0];
+                if (s < f.cap) cand[s] = make_uint2(score_key(p[u]), (uint32_t)i);
+            }
+            if (inner) {
+                if (dg > bin_i) {
+                    const int s = b2 + slot[u][1];
+                    if (s < f.k_inner) outi[s] = i;
+                } else if (sep && dg == bin_i) {
+                    const int s = b3 + slot[u][1];
+                    if (s < f.cap) cand2[s] = make_uint2(score_key(p[u]), (uint32_t)i);
+                }
             }
         }
     }
@@ -207,29 +272,48 @@ __device__ __forceinline__ void filter_pass(const ScoreArgs &a, int q, int64_t r
 // coalesced pass; with a histogram, their first radix digits are counted in
 // LDS and merged into the query's histogram (non-empty bins only), and with
 // the fused filter pass the scores leave after it (nothing in this launch
-// reads them).  All 256 threads.
+// reads them).  A workgroup past the query's last row (rows <= 0) has
+// nothing to count or sort and takes no part in the filter pass, whose row
+// total is then the sum of the others' rows, n.  All 256 threads.
 __device__ __forceinline__ void score_tail(const ScoreArgs &a, int q, int64_t row0, int rows, int n,
                                            const lds_f32 *s_out, uint32_t *s_hist, FilterLds *fl)
 {
+    if (rows <= 0) return;
     const int tid = threadIdx.x;
-    float *out = a.out + (int64_t)q * a.out_ld;
+    float *out = a.out + (int64_t)q * a.out_ld + row0;
+    auto store_scores = [&] {
+        for (int c0 = 0; c0 < rows; c0 += 256 * kTailU) {
+            float p[kTailU];
+            bool live[kTailU];
+            tail_round(s_out, c0, rows, p, live);
+#pragma unroll
+            for (int u = 0; u < kTailU; ++u)
+                if (live[u]) out[c0 + u * 256 + tid] = p[u];
+        }
+    };
     if (!a.hist) {
-        for (int j = tid; j < rows; j += 256) out[row0 + j] = s_out[j];
+        store_scores();
         return;
     }
     int32_t *hq = a.hist + (int64_t)q * kHistStride;
     const bool fused = a.flt.on;
-    for (int j = tid; j < rows; j += 256) {
-        const float p = s_out[j];
-        if (!fused) out[row0 + j] = p;
-        atomicAdd(&s_hist[score_key(p) >> kDigit0Shift], 1u);
+    for (int c0 = 0; c0 < rows; c0 += 256 * kTailU) {
+        float p[kTailU];
+        bool live[kTailU];
+        tail_round(s_out, c0, rows, p, live);
+#pragma unroll
+        for (int u = 0; u < kTailU; ++u) {
+            if (!live[u]) continue;
+            if (!fused) out[c0 + u * 256 + tid] = p[u];
+            atomicAdd(&s_hist[score_key(p[u]) >> kDigit0Shift], 1u);
+        }
     }
     __syncthreads();
     hist_flush(s_hist, hq, 256, tid);
     if (!fused) return;
     __syncthreads(); // every thread has issued its adds (and read s_hist, which the filter pass reuses)
     filter_pass(a, q, row0, rows, n, s_out, s_hist, hq, fl);
-    for (int j = tid; j < rows; j += 256) out[row0 + j] = s_out[j];
+    store_scores();
 }
 
 } // namespace

@@ -184,6 +184,34 @@ def test_long_rows_with_a_dirty_workspace(mode, fill):
         B.fused_filter(B.FUSED_FILTER_ON)
 
 
+# The zeroed region's per-query record (internal layout, read only by the
+# test below): 4096 first-digit bins, then counters; the tenth counter is the
+# number of rows the fused filter pass has sorted.
+_REC_INTS = 4096 + 16
+_SLOT_DONE = 4096 + 9
+
+
+@pytest.mark.parametrize("k_inner", [0, 512])
+def test_mixed_lengths_finish_inside_the_scoring_launch(k_inner):
+    # queries of different lengths in one batch: the workgroups past a short
+    # query's last row hold no rows and take no part in its filter pass, so
+    # each query's rows are all sorted inside the scoring launch (its count
+    # of sorted rows reaches n) and the final kernel does not select again
+    # from the scores; before, their empty row counts kept the row total
+    # from ever meeting n, and every short query waited out its bound
+    lens = [65536, 40000, 23000, 17000]
+    cache, seq, pos, mv, qt, w, n_q = _setup(27 + k_inner, lens, 500)
+    nb = B.workspace_bytes(B.LI_OP_SCORE_TOPK_EXT_SCORES, len(n_q), mv, H, R, 2048, 0)
+    ws = B.workspace(nb, _dev())
+    for rep in range(2):
+        out = B.score_topk(cache, seq, pos, mv, qt, w, 2048, k_inner=k_inner, keep_scores=True, ws=ws)
+        _check_full(out, n_q, 2048, f"mixed lengths, call {rep}", k_inner=k_inner)
+        torch.cuda.synchronize()
+        rec = ws[: len(n_q) * _REC_INTS * 4].view(torch.int32).view(len(n_q), _REC_INTS).cpu().numpy()
+        done = rec[:, _SLOT_DONE].tolist()
+        assert done == [int(n) for n in n_q], f"call {rep}: rows sorted by the filter pass {done}, rows {n_q}"
+
+
 def test_concurrent_launches_on_two_streams_stay_exact():
     # two long-row calls enqueued on two streams at once, each with a grid
     # that fills the GPU: the fused filter pass of one may find its
