@@ -189,6 +189,32 @@ def test_fp8_ragged_paged_full_and_hs():
     verify_fp8_hs(h, g, cache, qs, codes, "fp8-rag")
 
 
+def test_fp8_mixed_lengths_finish_inside_the_scoring_launch():
+    """Four sequences of different lengths on the FP8 cache: the workgroups
+    past a short query's last row take no part in its fused filter pass, so
+    every query's rows are sorted inside the scoring launch (the count of
+    sorted rows in the workspace's zeroed region, whose per-query record is
+    4096 first-digit bins and then 16 counters, the tenth of them that
+    count, reaches n) and the scores and top-k match the oracle."""
+    h = _gpu()
+    say("fp8 mixed lengths: fused filter pass completes for every query")
+    g = synth.make_decode("f8mix", 63, B=4, lens=[65536, 40000, 23000, 17000], r=256, H=64, d=128, k=2048,
+                          M=8192)
+    cache = fp8_cache(h, g)
+    qs = h.Queries(g)
+    fq = B.absorb_query(h.to_dev(g.q[0], torch.bfloat16), h.to_dev(g.W[0], torch.bfloat16), fp8=True)
+    nb = B.workspace_bytes(B.LI_OP_SCORE_TOPK_EXT_SCORES, g.Q, qs.max_valid, 64, 256, g.k, 0)
+    ws = B.workspace(nb, h.device())
+    out = B.score_topk(cache, qs.seq, qs.pos, qs.max_valid, fq, h.head_weights(g, 0), g.k, keep_scores=True, ws=ws)
+    torch.cuda.synchronize()
+    rec = ws[: g.Q * 4112 * 4].view(torch.int32).view(g.Q, 4112).cpu().numpy()
+    n_q = [oracle.valid_rows(g.qpos[i], g.lens[int(g.qseq[i])]) for i in range(g.Q)]
+    assert rec[:, 4096 + 9].tolist() == [int(n) for n in n_q], f"rows sorted {rec[:, 4096 + 9].tolist()}, rows {n_q}"
+    verify_fp8_full(h, g, 0, out, tag="fp8-mixed")
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_fp8_long_context_b4_n131072_full_and_hs():
     """The long-context workload (4 sequences of 131072 rows) on the FP8
     cache, in the launch configuration the benchmark times: every layer's
